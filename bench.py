@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Benchmark of the Conv1D(width 4) -> RG-LRU forward on one MI355X.
+
+Workload: the RecurrentGemma-2B-shaped recurrent layer, B=8, T=2048, D=2560, 10 heads of 256,
+bf16 x/y, fp32 state, seeded synthetic inputs (no dataset is involved). One step = one full
+rglru_forward (gate projections on MFMA, then the fused conv + gate + scan) over one batch, with
+the inputs already resident in HBM. Three independent input/output sets are rotated so that a
+step never re-reads the previous step's data out of the 256 MB last-level cache.
+
+Prints ONE JSON line: throughput (tokens*channels/s) and ms/step of the whole forward, a roofline
+record for the dominant kernel (its algorithmic HBM bytes per launch over its average duration,
+timed with HIP events on the stream the library launches on), and the fp64 CPU oracle timed on
+the host cores as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "RG-LRU fwd tokens·channels/s + % HBM peak, B=8 T=2048 D=2560 bf16"
+KERNEL_SOURCES = ["rglru_device.h", "rglru_mfma.h", "rglru_gates.hip", "rglru_scan.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gated_linear_recurrence_conv1d_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on the
+    current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, inp):
+    """The fp64 oracle, as it stands, on the host cores: the full workload (B=8, T=2048, D=2560,
+    all heads) takes a few seconds of wall time on a multi-core host."""
+    import oracle
+
+    t0 = time.perf_counter()
+    oracle.forward(inp["x"], inp["conv_w"], inp["W_a"], inp["b_a"], inp["W_x"], inp["b_x"],
+                   inp["Lam"], inp["h0"])
+    dt = time.perf_counter() - t0
+    return {"value": w.elements / dt, "unit": "tokens·channels/s", "cores": oracle.threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"full workload B={w.B} T={w.T} D={w.D} H={w.H} (one forward), fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="rg2b")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards over batch and heads without communication; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_linear_recurrence_conv1d_amd as rg
+    from workloads import WORKLOADS, make_inputs, to_device
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(w, seed=0)
+    g = to_device(inp, dev)
+    B, T, D, H = w.B, w.T, w.D, w.H
+    io = g["x"].dtype
+    R = 3
+    xs = [g["x"]] + [torch.randn_like(g["x"], dtype=torch.float32).to(io) for _ in range(R - 1)]
+    ys = [torch.empty_like(g["x"]) for _ in range(R)]
+    hTs = [torch.empty((B, D), dtype=torch.float32, device=dev) for _ in range(R)]
+    ws_bytes = rg.rglru_forward_workspace_size(B, T, D, H, io)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    plan, chunk = rg.rglru_forward_plan_info(B, T, D, H, io)
+
+    def fwd(i):
+        k = i % R
+        rg.rglru_forward(xs[k], g["conv_w"], g["W_a"], g["b_a"], g["W_x"], g["b_x"], g["Lam"],
+                         g["h0"], ys[k], hTs[k], ws)
+
+    for i in range(args.warmup):
+        fwd(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        fwd(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    # Per-stage timing with events around each stage, same kernels as rglru_forward.
+    pre = rg.pre_buffer(g["x"])
+    sws = torch.empty(max(1, rg.rglru_scan_workspace_size(B, T, D, H, io)), dtype=torch.uint8,
+                      device=dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def staged(i, e=None):
+        k = i % R
+        if e is not None:
+            e[0].record()
+        rg.rglru_gate_preacts(xs[k], g["conv_w"], g["W_a"], g["b_a"], g["W_x"], g["b_x"], pre)
+        if e is not None:
+            e[1].record()
+        rg.rglru_scan_preacts(xs[k], pre, g["conv_w"], g["Lam"], g["h0"], ys[k], hTs[k], H, sws,
+                              plan, chunk)
+        if e is not None:
+            e[2].record()
+
+    for i in range(args.warmup):
+        staged(i)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        staged(i, evs[i])
+    torch.cuda.synchronize()
+    gate_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    scan_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+
+    n = B * T * D
+    eb = 2 if io == torch.bfloat16 else 4
+    pb = 4 if io == torch.bfloat16 else 8
+    wbytes = 2 * H * (D // H) ** 2 * eb
+    # algorithmic bytes per launch ("Measurement")
+    scan_bytes = n * (eb + pb + eb) + 4 * D + eb * 4 * D + (8 if g["h0"] is not None else 4) * B * D
+    gate_bytes = n * (eb + pb) + wbytes + 4 * eb * D + 8 * D
+    kernels = {
+        "scan": {"ms": scan_ms, "bytes": scan_bytes, "plan": plan, "chunk_len": chunk},
+        "gates": {"ms": gate_ms, "bytes": gate_bytes,
+                  "tflops": 2.0 * n * 2 * (D // H) / (gate_ms * 1e-3) / 1e12},
+    }
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    kd = kernels[dom]
+    achieved = kd["bytes"] / (kd["ms"] * 1e-3) / 1e9
+    traffic = measured_traffic(dom, w.name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": dom, "kernel_ms": round(kd["ms"], 4),
+                "algorithmic_bytes": kd["bytes"]}
+
+    line = {
+        "metric": METRIC,
+        "value": n / (ms * 1e-3),
+        "unit": "tokens·channels/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if io == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded; N(0,1) inputs, 1/fan-in weights)",
+        "config": {"workload": w.name, "B": B, "T": T, "D": D, "H": H, "plan": plan,
+                   "chunk_len": chunk, "state": "f32", "io": str(io).replace("torch.", ""),
+                   "rotating_buffers": R},
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                        for kk, vv in v.items()} for k, v in kernels.items()},
+        "wall_s_timed": round(wall, 4),
+        "alg_gbs_end_to_end": round((n * 2 * eb + wbytes) / (ms * 1e-3) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

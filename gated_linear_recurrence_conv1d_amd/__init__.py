@@ -1,0 +1,220 @@
+"""Python binding of librglru.so (include/rglru.h): argument marshalling only.
+
+Each function takes torch tensors, checks dtype / device / contiguity, passes raw device pointers
+and the current HIP stream to the C entry point of the same name, and raises RglruError on a
+non-zero status. Every step of the computation runs in the library's HIP kernels; there is no
+fallback of any kind: if librglru.so is missing or fails to load, importing this package fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librglru.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run gated_linear_recurrence_conv1d_amd/build.py "
+                      "(or __graft_entry__.build())")
+_lib = ctypes.CDLL(LIB_PATH)
+
+RGLRU_OK = 0
+RGLRU_ERR_INVALID_ARG = 1
+RGLRU_ERR_UNSUPPORTED = 2
+RGLRU_ERR_WORKSPACE = 3
+RGLRU_ERR_HIP = 4
+RGLRU_F32 = 0
+RGLRU_BF16 = 1
+RGLRU_PLAN_AUTO = 0
+RGLRU_PLAN_DIRECT = 1
+RGLRU_PLAN_CHUNKED = 2
+_PLANS = {"auto": RGLRU_PLAN_AUTO, "direct": RGLRU_PLAN_DIRECT, "chunked": RGLRU_PLAN_CHUNKED}
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+_lib.rglru_status_string.argtypes = [_i]
+_lib.rglru_status_string.restype = ctypes.c_char_p
+_lib.rglru_forward_workspace_size.argtypes = [_i] * 5
+_lib.rglru_forward_workspace_size.restype = _sz
+_lib.rglru_scan_workspace_size.argtypes = [_i] * 5
+_lib.rglru_scan_workspace_size.restype = _sz
+_lib.rglru_forward_plan_info.argtypes = [_i] * 5 + [ctypes.POINTER(_i), ctypes.POINTER(_i)]
+_lib.rglru_forward_plan_info.restype = _i
+_lib.rglru_forward.argtypes = [_vp] * 10 + [_i] * 5 + [_vp, _sz, _vp]
+_lib.rglru_forward.restype = _i
+_lib.rglru_forward_planned.argtypes = [_vp] * 10 + [_i] * 5 + [_vp, _sz, _vp, _i, _i]
+_lib.rglru_forward_planned.restype = _i
+_lib.rglru_gate_preacts.argtypes = [_vp] * 7 + [_i] * 5 + [_vp]
+_lib.rglru_gate_preacts.restype = _i
+_lib.rglru_scan_preacts.argtypes = [_vp] * 7 + [_i] * 5 + [_vp, _sz, _vp, _i, _i]
+_lib.rglru_scan_preacts.restype = _i
+_lib.rglru_decode_step.argtypes = [_vp] * 10 + [_i] * 4 + [_vp]
+_lib.rglru_decode_step.restype = _i
+
+
+class RglruError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {rglru_status_string(status)} (status {status})")
+        self.status = status
+
+
+def rglru_status_string(status: int) -> str:
+    return _lib.rglru_status_string(int(status)).decode()
+
+
+def _dt(dtype) -> int:
+    if dtype in (torch.bfloat16, "bf16", RGLRU_BF16):
+        return RGLRU_BF16
+    if dtype in (torch.float32, "f32", RGLRU_F32):
+        return RGLRU_F32
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+def _ptr(t, io_dtype=None, name=""):
+    """Raw device pointer of a contiguous CUDA (HIP) tensor, or None."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if io_dtype is not None and t.dtype != io_dtype:
+        raise ValueError(f"{name}: expected {io_dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status, where):
+    if status != RGLRU_OK:
+        raise RglruError(status, where)
+
+
+def rglru_forward_workspace_size(B, T, D, H, dtype) -> int:
+    return int(_lib.rglru_forward_workspace_size(B, T, D, H, _dt(dtype)))
+
+
+def rglru_scan_workspace_size(B, T, D, H, dtype) -> int:
+    return int(_lib.rglru_scan_workspace_size(B, T, D, H, _dt(dtype)))
+
+
+def rglru_forward_plan_info(B, T, D, H, dtype):
+    plan, chunk = _i(), _i()
+    _check(_lib.rglru_forward_plan_info(B, T, D, H, _dt(dtype), ctypes.byref(plan),
+                                        ctypes.byref(chunk)), "rglru_forward_plan_info")
+    return {RGLRU_PLAN_DIRECT: "direct", RGLRU_PLAN_CHUNKED: "chunked"}[plan.value], chunk.value
+
+
+def _fwd_args(x, conv_w, W_a, b_a, W_x, b_x, Lam, h0, y, h_T):
+    io = x.dtype
+    B, T, D = x.shape
+    H = W_a.shape[0]
+    f32 = torch.float32
+    ptrs = [_ptr(x, io, "x"), _ptr(conv_w, io, "conv_w"), _ptr(W_a, io, "W_a"),
+            _ptr(b_a, f32, "b_a"), _ptr(W_x, io, "W_x"), _ptr(b_x, f32, "b_x"),
+            _ptr(Lam, f32, "Lambda"), _ptr(h0, f32, "h0"), _ptr(y, io, "y"),
+            _ptr(h_T, f32, "h_T")]
+    return ptrs, (B, T, D, H, _dt(io))
+
+
+def rglru_forward(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, h_T, workspace, stream=None):
+    ptrs, dims = _fwd_args(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, h_T)
+    _check(_lib.rglru_forward(*ptrs, *dims, _ptr(workspace, None, "workspace"),
+                              workspace.numel() * workspace.element_size(), _stream(stream)),
+           "rglru_forward")
+
+
+def rglru_forward_planned(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, h_T, workspace,
+                          plan="auto", chunk_len=0, stream=None):
+    ptrs, dims = _fwd_args(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, h_T)
+    _check(_lib.rglru_forward_planned(*ptrs, *dims, _ptr(workspace, None, "workspace"),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(stream), _PLANS[plan], int(chunk_len)),
+           "rglru_forward_planned")
+
+
+def rglru_gate_preacts(x, conv_w, W_a, b_a, W_x, b_x, pre, stream=None):
+    """pre: int32 [B,T,D] (fp16 pairs) for bf16 x, float32 [B,T,D,2] for fp32 x."""
+    io = x.dtype
+    B, T, D = x.shape
+    H = W_a.shape[0]
+    f32 = torch.float32
+    _check(_lib.rglru_gate_preacts(_ptr(x, io, "x"), _ptr(conv_w, io, "conv_w"),
+                                   _ptr(W_a, io, "W_a"), _ptr(b_a, f32, "b_a"),
+                                   _ptr(W_x, io, "W_x"), _ptr(b_x, f32, "b_x"),
+                                   _ptr(pre, None, "pre"), B, T, D, H, _dt(io), _stream(stream)),
+           "rglru_gate_preacts")
+
+
+def rglru_scan_preacts(x, pre, conv_w, Lambda, h0, y, h_T, H, workspace=None, plan="auto",
+                       chunk_len=0, stream=None):
+    io = x.dtype
+    B, T, D = x.shape
+    f32 = torch.float32
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.rglru_scan_preacts(_ptr(x, io, "x"), _ptr(pre, None, "pre"),
+                                   _ptr(conv_w, io, "conv_w"), _ptr(Lambda, f32, "Lambda"),
+                                   _ptr(h0, f32, "h0"), _ptr(y, io, "y"), _ptr(h_T, f32, "h_T"),
+                                   B, T, D, H, _dt(io), _ptr(workspace, None, "workspace"), wsb,
+                                   _stream(stream), _PLANS[plan], int(chunk_len)),
+           "rglru_scan_preacts")
+
+
+def rglru_decode_step(x_t, conv_state, h, y_t, conv_w, W_a, b_a, W_x, b_x, Lambda, stream=None):
+    io = x_t.dtype
+    N, D = x_t.shape
+    H = W_a.shape[0]
+    f32 = torch.float32
+    _check(_lib.rglru_decode_step(_ptr(x_t, io, "x_t"), _ptr(conv_state, io, "conv_state"),
+                                  _ptr(h, f32, "h"), _ptr(y_t, io, "y_t"),
+                                  _ptr(conv_w, io, "conv_w"), _ptr(W_a, io, "W_a"),
+                                  _ptr(b_a, f32, "b_a"), _ptr(W_x, io, "W_x"),
+                                  _ptr(b_x, f32, "b_x"), _ptr(Lambda, f32, "Lambda"), N, D, H,
+                                  _dt(io), _stream(stream)),
+           "rglru_decode_step")
+
+
+# ---- convenience wrappers (allocate outputs with torch, then call the entry points above) ----
+def pre_buffer(x):
+    """An empty pre-activation buffer in the layout rglru_gate_preacts writes."""
+    B, T, D = x.shape
+    if x.dtype == torch.bfloat16:
+        return torch.empty((B, T, D), dtype=torch.int32, device=x.device)
+    return torch.empty((B, T, D, 2), dtype=torch.float32, device=x.device)
+
+
+def forward(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0=None, plan="auto", chunk_len=0,
+            workspace=None, stream=None):
+    """Returns (y, h_T)."""
+    B, T, D = x.shape
+    H = W_a.shape[0]
+    y = torch.empty_like(x)
+    h_T = torch.empty((B, D), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        n = rglru_forward_workspace_size(B, T, D, H, x.dtype)
+        if plan == "chunked" and chunk_len:
+            # small explicit chunks may need more summary space than the default provisions
+            n += 12 * B * D * ((T + chunk_len - 1) // chunk_len) + 1024
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    rglru_forward_planned(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, h_T, workspace, plan,
+                          chunk_len, stream)
+    return y, h_T
+
+
+def decode_step(x_t, conv_state, h, conv_w, W_a, b_a, W_x, b_x, Lambda, stream=None):
+    """In place on conv_state and h; returns y_t."""
+    y_t = torch.empty_like(x_t)
+    rglru_decode_step(x_t, conv_state, h, y_t, conv_w, W_a, b_a, W_x, b_x, Lambda, stream)
+    return y_t

@@ -1,0 +1,268 @@
+// rglru_api.cpp -- the C ABI (include/rglru.h): argument checks, plan choice, workspace layout and
+// kernel launches. No allocation, no global state; every call is asynchronous on its stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "rglru.h"
+#include "rglru_launch.h"
+
+namespace {
+
+using rglru::kBF16;
+using rglru::kF32;
+
+constexpr size_t kAlign = 256;         // workspace carve alignment
+constexpr int kMinChunk = 16;          // smallest chunk the size query provisions for
+constexpr long long kTargetLanes = 2LL * 64 * 1024;  // ~2 waves per SIMD on 256 CUs x 4 SIMDs
+constexpr long long kDirectLanes = 64LL * 1024;      // >= 1 wave per SIMD: scan every channel whole
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+size_t elem_bytes(rglru_dtype dt) { return dt == RGLRU_BF16 ? 2 : 4; }
+
+rglru_status check_shape(int B, int T, int D, int H, rglru_dtype dt) {
+  if (B < 1 || T < 1 || D < 1 || H < 1) return RGLRU_ERR_INVALID_ARG;
+  if (D % H) return RGLRU_ERR_INVALID_ARG;
+  if (dt != RGLRU_F32 && dt != RGLRU_BF16) return RGLRU_ERR_UNSUPPORTED;
+  if (D / H > 256) return RGLRU_ERR_UNSUPPORTED;
+  // element offsets are formed in size_t; grid dims must fit the hardware limits
+  if (static_cast<long long>(B) > 65535 || H > 65535) return RGLRU_ERR_UNSUPPORTED;
+  return RGLRU_OK;
+}
+
+// Chunk length of the automatic plan; returns T when the direct plan is chosen.
+int auto_chunk(int B, int T, int D) {
+  const long long lanes = static_cast<long long>(B) * D;
+  if (lanes >= kDirectLanes) return T;
+  const long long want = (kTargetLanes + lanes - 1) / lanes;
+  long long L = (T + want - 1) / want;
+  L = std::max<long long>(L, kMinChunk);
+  return L >= T ? T : static_cast<int>(L);
+}
+
+size_t pre_bytes(int B, int T, int D, rglru_dtype dt) {
+  return static_cast<size_t>(B) * T * D * rglru::pre_pair_bytes(dt == RGLRU_BF16 ? kBF16 : kF32);
+}
+
+// Scan-stage workspace: chunk summaries [B][nC][D] float2, then carries [B][nC][D] float.
+struct ScanCarve {
+  size_t sums, carry, total;
+};
+
+ScanCarve scan_carve(int B, int D, int nC) {
+  ScanCarve c;
+  c.sums = 0;
+  c.carry = align_up(static_cast<size_t>(B) * nC * D * sizeof(float2));
+  c.total = c.carry + align_up(static_cast<size_t>(B) * nC * D * sizeof(float));
+  return c;
+}
+
+// Resolves the plan to (direct?, chunk length). Returns false for an invalid plan request.
+bool resolve_plan(int B, int T, int D, rglru_plan plan, int chunk_len, bool &direct, int &L) {
+  if (plan == RGLRU_PLAN_AUTO) {
+    L = auto_chunk(B, T, D);
+    direct = L >= T;
+  } else if (plan == RGLRU_PLAN_DIRECT) {
+    L = T;
+    direct = true;
+  } else if (plan == RGLRU_PLAN_CHUNKED) {
+    if (chunk_len < 0) return false;
+    L = chunk_len == 0 ? auto_chunk(B, T, D) : std::min(chunk_len, T);
+    direct = false;
+  } else {
+    return false;
+  }
+  return true;
+}
+
+rglru_status hip_status(hipError_t e) { return e == hipSuccess ? RGLRU_OK : RGLRU_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *rglru_status_string(rglru_status s) {
+  switch (s) {
+    case RGLRU_OK: return "ok";
+    case RGLRU_ERR_INVALID_ARG: return "invalid argument";
+    case RGLRU_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+    case RGLRU_ERR_WORKSPACE: return "workspace missing or too small";
+    case RGLRU_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+size_t rglru_scan_workspace_size(int B, int T, int D, int H, rglru_dtype dt) {
+  if (check_shape(B, T, D, H, dt) != RGLRU_OK) return 0;
+  return scan_carve(B, D, (T + kMinChunk - 1) / kMinChunk).total;
+}
+
+size_t rglru_forward_workspace_size(int B, int T, int D, int H, rglru_dtype dt) {
+  if (check_shape(B, T, D, H, dt) != RGLRU_OK) return 0;
+  return align_up(pre_bytes(B, T, D, dt)) + rglru_scan_workspace_size(B, T, D, H, dt);
+}
+
+rglru_status rglru_forward_plan_info(int B, int T, int D, int H, rglru_dtype dt, int *plan,
+                                     int *chunk_len) {
+  rglru_status st = check_shape(B, T, D, H, dt);
+  if (st != RGLRU_OK) return st;
+  if (!plan || !chunk_len) return RGLRU_ERR_INVALID_ARG;
+  bool direct;
+  int L;
+  resolve_plan(B, T, D, RGLRU_PLAN_AUTO, 0, direct, L);
+  *plan = direct ? RGLRU_PLAN_DIRECT : RGLRU_PLAN_CHUNKED;
+  *chunk_len = L;
+  return RGLRU_OK;
+}
+
+rglru_status rglru_scan_preacts(const void *x, const void *pre, const void *conv_w,
+                                const float *Lambda, const float *h0, void *y, float *h_T, int B,
+                                int T, int D, int H, rglru_dtype dt, void *workspace,
+                                size_t workspace_bytes, void *stream, rglru_plan plan,
+                                int chunk_len) {
+  rglru_status st = check_shape(B, T, D, H, dt);
+  if (st != RGLRU_OK) return st;
+  if (!x || !pre || !conv_w || !Lambda || !y) return RGLRU_ERR_INVALID_ARG;
+  const void *vec16[] = {x, pre, conv_w, y};
+  for (const void *p : vec16)
+    if (!aligned(p, 16)) return RGLRU_ERR_INVALID_ARG;
+  const void *vec4[] = {Lambda, h0, h_T};
+  for (const void *p : vec4)
+    if (p && !aligned(p, 4)) return RGLRU_ERR_INVALID_ARG;
+  bool direct;
+  int L;
+  if (!resolve_plan(B, T, D, plan, chunk_len, direct, L)) return RGLRU_ERR_INVALID_ARG;
+  const size_t io_bytes = static_cast<size_t>(B) * T * D * elem_bytes(dt);
+  const size_t pb = pre_bytes(B, T, D, dt);
+  if (overlaps(x, io_bytes, y, io_bytes) || overlaps(pre, pb, y, io_bytes))
+    return RGLRU_ERR_INVALID_ARG;
+  const int nC = direct ? 0 : (T + L - 1) / L;
+  if (nC > 65535) return RGLRU_ERR_UNSUPPORTED;  // one grid row per chunk
+  const ScanCarve c = scan_carve(B, D, nC);
+  if (!direct) {
+    if (!workspace || workspace_bytes < c.total) return RGLRU_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return RGLRU_ERR_INVALID_ARG;
+    if (overlaps(workspace, c.total, y, io_bytes) || overlaps(workspace, c.total, pre, pb) ||
+        overlaps(workspace, c.total, x, io_bytes))
+      return RGLRU_ERR_INVALID_ARG;
+  }
+  const int io = dt == RGLRU_BF16 ? kBF16 : kF32;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // start from a clean error state
+  if (direct)
+    return hip_status(
+        rglru::launch_scan_direct(x, pre, conv_w, Lambda, h0, y, h_T, B, T, D, io, s));
+  char *ws = static_cast<char *>(workspace);
+  return hip_status(rglru::launch_scan_chunked(x, pre, conv_w, Lambda, h0, y, h_T, B, T, D, L,
+                                               reinterpret_cast<float2 *>(ws + c.sums),
+                                               reinterpret_cast<float *>(ws + c.carry), io, s));
+}
+
+rglru_status rglru_forward_planned(const void *x, const void *conv_w, const void *W_a,
+                                   const float *b_a, const void *W_x, const float *b_x,
+                                   const float *Lambda, const float *h0, void *y, float *h_T,
+                                   int B, int T, int D, int H, rglru_dtype dt, void *workspace,
+                                   size_t workspace_bytes, void *stream, rglru_plan plan,
+                                   int chunk_len) {
+  rglru_status st = check_shape(B, T, D, H, dt);
+  if (st != RGLRU_OK) return st;
+  if (!x || !conv_w || !W_a || !b_a || !W_x || !b_x || !Lambda || !y)
+    return RGLRU_ERR_INVALID_ARG;
+  const void *vec16[] = {x, conv_w, W_a, W_x, y};
+  for (const void *p : vec16)
+    if (!aligned(p, 16)) return RGLRU_ERR_INVALID_ARG;
+  const void *vec4[] = {b_a, b_x, Lambda, h0, h_T};
+  for (const void *p : vec4)
+    if (p && !aligned(p, 4)) return RGLRU_ERR_INVALID_ARG;
+  bool direct;
+  int L;
+  if (!resolve_plan(B, T, D, plan, chunk_len, direct, L)) return RGLRU_ERR_INVALID_ARG;
+  const size_t io_bytes = static_cast<size_t>(B) * T * D * elem_bytes(dt);
+  if (overlaps(x, io_bytes, y, io_bytes)) return RGLRU_ERR_INVALID_ARG;
+  const size_t pre_area = align_up(pre_bytes(B, T, D, dt));
+  const size_t need = pre_area + (direct ? 0 : scan_carve(B, D, (T + L - 1) / L).total);
+  if (!workspace || workspace_bytes < need) return RGLRU_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return RGLRU_ERR_INVALID_ARG;
+  if (overlaps(workspace, need, y, io_bytes) || overlaps(workspace, need, x, io_bytes))
+    return RGLRU_ERR_INVALID_ARG;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int io = dt == RGLRU_BF16 ? kBF16 : kF32;
+  char *ws = static_cast<char *>(workspace);
+  (void)hipGetLastError();  // start from a clean error state
+  hipError_t e = rglru::launch_gates(x, conv_w, W_a, b_a, W_x, b_x, ws, B, T, D, H, io, s);
+  if (e != hipSuccess) return RGLRU_ERR_HIP;
+  return rglru_scan_preacts(x, ws, conv_w, Lambda, h0, y, h_T, B, T, D, H, dt, ws + pre_area,
+                            workspace_bytes - pre_area, stream, direct ? RGLRU_PLAN_DIRECT
+                                                                       : RGLRU_PLAN_CHUNKED,
+                            L);
+}
+
+rglru_status rglru_forward(const void *x, const void *conv_w, const void *W_a, const float *b_a,
+                           const void *W_x, const float *b_x, const float *Lambda,
+                           const float *h0, void *y, float *h_T, int B, int T, int D, int H,
+                           rglru_dtype dt, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+  return rglru_forward_planned(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, h_T, B, T, D, H, dt,
+                               workspace, workspace_bytes, stream, RGLRU_PLAN_AUTO, 0);
+}
+
+rglru_status rglru_gate_preacts(const void *x, const void *conv_w, const void *W_a,
+                                const float *b_a, const void *W_x, const float *b_x, void *pre,
+                                int B, int T, int D, int H, rglru_dtype dt, void *stream) {
+  rglru_status st = check_shape(B, T, D, H, dt);
+  if (st != RGLRU_OK) return st;
+  if (!x || !conv_w || !W_a || !b_a || !W_x || !b_x || !pre) return RGLRU_ERR_INVALID_ARG;
+  const void *vec16[] = {x, conv_w, W_a, W_x, pre};
+  for (const void *p : vec16)
+    if (!aligned(p, 16)) return RGLRU_ERR_INVALID_ARG;
+  const int io = dt == RGLRU_BF16 ? kBF16 : kF32;
+  const size_t io_bytes = static_cast<size_t>(B) * T * D * elem_bytes(dt);
+  const size_t pre_bytes = static_cast<size_t>(B) * T * D * rglru::pre_pair_bytes(io);
+  if (overlaps(x, io_bytes, pre, pre_bytes)) return RGLRU_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return hip_status(rglru::launch_gates(x, conv_w, W_a, b_a, W_x, b_x, pre, B, T, D, H, io,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+rglru_status rglru_decode_step(const void *x_t, void *conv_state, float *h, void *y_t,
+                               const void *conv_w, const void *W_a, const float *b_a,
+                               const void *W_x, const float *b_x, const float *Lambda, int N,
+                               int D, int H, rglru_dtype dt, void *stream) {
+  rglru_status st = check_shape(1, 1, D, H, dt);
+  if (st != RGLRU_OK) return st;
+  if (N < 1) return RGLRU_ERR_INVALID_ARG;
+  if (N > 65535 * 64) return RGLRU_ERR_UNSUPPORTED;
+  if (!x_t || !conv_state || !h || !y_t || !conv_w || !W_a || !b_a || !W_x || !b_x || !Lambda)
+    return RGLRU_ERR_INVALID_ARG;
+  const void *vec16[] = {x_t, conv_state, y_t, conv_w, W_a, W_x};
+  for (const void *p : vec16)
+    if (!aligned(p, 16)) return RGLRU_ERR_INVALID_ARG;
+  const void *vec4[] = {h, b_a, b_x, Lambda};
+  for (const void *p : vec4)
+    if (!aligned(p, 4)) return RGLRU_ERR_INVALID_ARG;
+  const size_t row = static_cast<size_t>(N) * D;
+  const size_t eb = elem_bytes(dt);
+  if (overlaps(y_t, row * eb, x_t, row * eb) || overlaps(y_t, row * eb, conv_state, 3 * row * eb) ||
+      overlaps(y_t, row * eb, h, row * sizeof(float)) ||
+      overlaps(conv_state, 3 * row * eb, h, row * sizeof(float)) ||
+      overlaps(conv_state, 3 * row * eb, x_t, row * eb) ||
+      overlaps(h, row * sizeof(float), x_t, row * eb))
+    return RGLRU_ERR_INVALID_ARG;
+  const int io = dt == RGLRU_BF16 ? kBF16 : kF32;
+  (void)hipGetLastError();
+  return hip_status(rglru::launch_decode(x_t, conv_state, h, y_t, conv_w, W_a, b_a, W_x, b_x,
+                                         Lambda, N, D, H, io, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

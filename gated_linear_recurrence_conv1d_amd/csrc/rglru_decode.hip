@@ -1,0 +1,191 @@
+// rglru_decode.hip -- one batched, in-place decode step of the Conv1D -> RG-LRU block.
+//
+// The state has a fixed size whatever the sequence length (alby13 blog, "Core Components of
+// Griffin -- 1. RG-LRU"; fast inference from it in "Griffin's Strengths"): per row, h[D] in fp32
+// and the conv's last three inputs conv_state[3][D], oldest first. One step:
+//   xc = w0 cs0 + w1 cs1 + w2 cs2 + w3 x_t;  gates from xc;  h <- a h + sqrt(1-a^2) i xc;
+//   y_t = h;  conv_state <- (cs1, cs2, x_t).
+// Every element of conv_state, h and y_t belongs to exactly one workgroup, which reads it before
+// it writes it, so the in-place update needs no synchronisation beyond the workgroup's own.
+//
+//  * decode_mfma<DH>: bf16 I/O, DH in {32, 64, 128, 256}. A 64-row tile of one head: conv in fp32
+//    into LDS (fp32 copy for the gate math, bf16 copy as the MFMA A operand), the same MFMA gate
+//    tile as the forward, then the nonlinearity and state update straight from the accumulators.
+//  * decode_valu<T>: any Dh <= 256, fp32 or bf16, one workgroup per (row, head).
+#include "rglru_launch.h"
+#include "rglru_mfma.h"
+
+namespace rglru {
+
+template <int DH>
+__global__ __launch_bounds__(kThreads) void decode_mfma(
+    const bf16_t *__restrict__ x_t, bf16_t *__restrict__ cs, float *__restrict__ h,
+    bf16_t *__restrict__ y_t, const bf16_t *__restrict__ conv_w, const bf16_t *__restrict__ W_a,
+    const float *__restrict__ b_a, const bf16_t *__restrict__ W_x,
+    const float *__restrict__ b_x, const float *__restrict__ Lambda, int N, int D) {
+  typedef GateTile<DH> C;
+  __shared__ __attribute__((aligned(16))) bf16_t lds_a[kTileRows * C::kLda];
+  __shared__ float lds_xc[kTileRows * DH];
+
+  const int n0 = blockIdx.x * kTileRows;
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  {
+    constexpr int P = DH / 2;
+    constexpr int RPG = kTileRows * P / kThreads;
+    const int p = tid % P;
+    const int r0 = (tid / P) * RPG;
+    const int d0 = g * DH + 2 * p;
+    float w0[4], w1[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t wv = *reinterpret_cast<const uint32_t *>(conv_w + static_cast<size_t>(j) * D + d0);
+      w0[j] = bf16lo(wv);
+      w1[j] = bf16hi(wv);
+    }
+    for (int r = r0; r < r0 + RPG; ++r) {
+      const int n = n0 + r;
+      float y0 = 0.0f, y1 = 0.0f;
+      if (n < N) {
+        uint32_t *c = reinterpret_cast<uint32_t *>(cs + static_cast<size_t>(n) * 3 * D + d0);
+        const uint32_t c0 = c[0];
+        const uint32_t c1 = c[D / 2];
+        const uint32_t c2 = c[D];
+        const uint32_t xv = *reinterpret_cast<const uint32_t *>(x_t + static_cast<size_t>(n) * D + d0);
+        y0 = fmaf(w0[3], bf16lo(xv), fmaf(w0[2], bf16lo(c2), fmaf(w0[1], bf16lo(c1), w0[0] * bf16lo(c0))));
+        y1 = fmaf(w1[3], bf16hi(xv), fmaf(w1[2], bf16hi(c2), fmaf(w1[1], bf16hi(c1), w1[0] * bf16hi(c0))));
+        c[0] = c1;
+        c[D / 2] = c2;
+        c[D] = xv;
+      }
+      *reinterpret_cast<uint32_t *>(lds_a + r * C::kLda + 2 * p) = pack_bf16x2(y0, y1);
+      lds_xc[r * DH + 2 * p] = y0;
+      lds_xc[r * DH + 2 * p + 1] = y1;
+    }
+  }
+  __syncthreads();
+
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  int gq0, rq0;
+  bool active;
+  C::assign(w, gq0, rq0, active);
+  if (!active) return;
+  f32x16_t acc[C::kGPW][C::kRPW][2];
+  const size_t woff = static_cast<size_t>(g) * DH * DH;
+  gate_tile_mfma<DH>(lds_a, W_a + woff, W_x + woff, gq0, rq0, lane, acc);
+
+#pragma unroll
+  for (int gi = 0; gi < C::kGPW; ++gi) {
+    const int cl = (gq0 + gi) * 32 + (lane & 31);
+    const int d = g * DH + cl;
+    const float ba = b_a[d], bx = b_x[d];
+    const float kd = decay_coeff(Lambda[d]);
+#pragma unroll
+    for (int ri = 0; ri < C::kRPW; ++ri)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int row = C::acc_row(rq0 + ri, j, lane);
+        const int n = n0 + row;
+        if (n < N) {
+          float a, u;
+          gate(acc[gi][ri][0][j] + ba, acc[gi][ri][1][j] + bx, lds_xc[row * DH + cl], kd, a, u);
+          const size_t off = static_cast<size_t>(n) * D + d;
+          const float hn = fmaf(a, h[off], u);
+          h[off] = hn;
+          y_t[off] = f32_to_bf16(hn);
+        }
+      }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void decode_valu(
+    const T *__restrict__ x_t, T *__restrict__ cs, float *__restrict__ h, T *__restrict__ y_t,
+    const T *__restrict__ conv_w, const T *__restrict__ W_a, const float *__restrict__ b_a,
+    const T *__restrict__ W_x, const float *__restrict__ b_x, const float *__restrict__ Lambda,
+    int D, int Dh) {
+  __shared__ float xc[256];
+  const int n = blockIdx.x;
+  const int g = blockIdx.y;
+  const int o = threadIdx.x;
+  const int d = g * Dh + o;
+  T *c = cs + static_cast<size_t>(n) * 3 * D;
+  float xv = 0.0f, c1 = 0.0f, c2 = 0.0f;
+  if (o < Dh) {
+    const float c0 = Elem<T>::load(c, d);
+    c1 = Elem<T>::load(c, static_cast<size_t>(D) + d);
+    c2 = Elem<T>::load(c, static_cast<size_t>(2) * D + d);
+    xv = Elem<T>::load(x_t, static_cast<size_t>(n) * D + d);
+    float acc = Elem<T>::load(conv_w, d) * c0;
+    acc = fmaf(Elem<T>::load(conv_w, static_cast<size_t>(D) + d), c1, acc);
+    acc = fmaf(Elem<T>::load(conv_w, static_cast<size_t>(2) * D + d), c2, acc);
+    acc = fmaf(Elem<T>::load(conv_w, static_cast<size_t>(3) * D + d), xv, acc);
+    xc[o] = acc;
+  }
+  __syncthreads();
+  if (o >= Dh) return;
+  // shift the conv state (values were read above; stores are exact copies of dtype values)
+  Elem<T>::store(c, d, c1);
+  Elem<T>::store(c, static_cast<size_t>(D) + d, c2);
+  Elem<T>::store(c, static_cast<size_t>(2) * D + d, xv);
+  const size_t wr = (static_cast<size_t>(g) * Dh + o) * Dh;
+  float sa = 0.0f, sx = 0.0f;
+  for (int i = 0; i < Dh; ++i) {
+    sa = fmaf(Elem<T>::load(W_a, wr + i), xc[i], sa);
+    sx = fmaf(Elem<T>::load(W_x, wr + i), xc[i], sx);
+  }
+  float a, u;
+  gate(sa + b_a[d], sx + b_x[d], xc[o], decay_coeff(Lambda[d]), a, u);
+  const size_t off = static_cast<size_t>(n) * D + d;
+  const float hn = fmaf(a, h[off], u);
+  h[off] = hn;
+  Elem<T>::store(y_t, off, hn);
+}
+
+hipError_t launch_decode(const void *x_t, void *conv_state, float *h, void *y_t,
+                         const void *conv_w, const void *W_a, const float *b_a, const void *W_x,
+                         const float *b_x, const float *Lambda, int N, int D, int H, int io,
+                         hipStream_t s) {
+  const int Dh = D / H;
+  if (io == kBF16 && (Dh == 32 || Dh == 64 || Dh == 128 || Dh == 256)) {
+    dim3 grid((N + kTileRows - 1) / kTileRows, H);
+    const bf16_t *xx = static_cast<const bf16_t *>(x_t);
+    bf16_t *cc = static_cast<bf16_t *>(conv_state);
+    bf16_t *yy = static_cast<bf16_t *>(y_t);
+    const bf16_t *cw = static_cast<const bf16_t *>(conv_w);
+    const bf16_t *wa = static_cast<const bf16_t *>(W_a);
+    const bf16_t *wx = static_cast<const bf16_t *>(W_x);
+#define RGLRU_DECODE_CASE(DHV)                                                                  \
+  case DHV:                                                                                     \
+    decode_mfma<DHV><<<grid, kThreads, 0, s>>>(xx, cc, h, yy, cw, wa, b_a, wx, b_x, Lambda, N, \
+                                               D);                                              \
+    break;
+    switch (Dh) {
+      RGLRU_DECODE_CASE(32)
+      RGLRU_DECODE_CASE(64)
+      RGLRU_DECODE_CASE(128)
+      RGLRU_DECODE_CASE(256)
+      default: return hipErrorInvalidValue;
+    }
+#undef RGLRU_DECODE_CASE
+    return hipGetLastError();
+  }
+  dim3 grid(N, H);
+  if (io == kBF16) {
+    decode_valu<bf16_t><<<grid, 256, 0, s>>>(
+        static_cast<const bf16_t *>(x_t), static_cast<bf16_t *>(conv_state), h,
+        static_cast<bf16_t *>(y_t), static_cast<const bf16_t *>(conv_w),
+        static_cast<const bf16_t *>(W_a), b_a, static_cast<const bf16_t *>(W_x), b_x, Lambda, D,
+        Dh);
+  } else {
+    decode_valu<float><<<grid, 256, 0, s>>>(
+        static_cast<const float *>(x_t), static_cast<float *>(conv_state), h,
+        static_cast<float *>(y_t), static_cast<const float *>(conv_w),
+        static_cast<const float *>(W_a), b_a, static_cast<const float *>(W_x), b_x, Lambda, D,
+        Dh);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rglru

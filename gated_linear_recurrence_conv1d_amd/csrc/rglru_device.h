@@ -1,0 +1,138 @@
+// rglru_device.h -- device-side element types and the RG-LRU gate math for gfx950.
+//
+// The gate math follows the RG-LRU (Griffin paper page on docshare.wps.com, section "Model
+// Architecture"; the recurrence gate that can drop the input and keep the history is the one of
+// Soham De's Griffin thread, tweet on adding a Recurrent Gate to LRU):
+//   r = sigmoid(pa), i = sigmoid(px), log a = -8 r softplus(-Lambda),
+//   a = exp(log a), m = sqrt(1 - a^2), u = m * i * xc, h <- a h + u.
+// In fp32, 1 - a*a cancels catastrophically when a is near 1 (a^8 = 0.9999 and r = 0.01 give
+// 1 - a^2 ~ 2e-6, where the literal form loses about 1e-2 of relative accuracy). So both a and
+// 1 - a^2 come from one e = expm1(log a): a = 1 + e and 1 - a^2 = -e (2 + e), which is exact
+// algebra and keeps full relative accuracy. expm1 on |z| <= 1/4 is its Taylor polynomial
+// z + z^2/2! + ... + z^7/7! (truncation below 1.6e-9 relative there); below -1/4 it is
+// exp(z) - 1, whose cancellation costs at most a few ulps because |e| > 0.22.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rglru {
+
+constexpr int kConvW = 4;      // temporal conv width
+constexpr float kGateC = 8.0f;  // the fixed scale c of the recurrence gate
+
+typedef uint16_t bf16_t;  // raw bf16 bits
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// fp32 -> bf16 with round-to-nearest-even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// (pa, px) pre-activation pair for the bf16 path: two fp16 values (round-to-nearest-even),
+// pa in the low half. fp16 keeps 11 significant bits; values beyond its range become +-inf,
+// which the sigmoids map to exactly 0 or 1, as the exact values would be after rounding.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  _Float16 a = static_cast<_Float16>(lo);
+  _Float16 b = static_cast<_Float16>(hi);
+  uint16_t ua, ub;
+  __builtin_memcpy(&ua, &a, 2);
+  __builtin_memcpy(&ub, &b, 2);
+  return static_cast<uint32_t>(ua) | (static_cast<uint32_t>(ub) << 16);
+}
+__device__ __forceinline__ float f16lo(uint32_t v) {
+  uint16_t u = static_cast<uint16_t>(v & 0xffffu);
+  _Float16 h;
+  __builtin_memcpy(&h, &u, 2);
+  return static_cast<float>(h);
+}
+__device__ __forceinline__ float f16hi(uint32_t v) {
+  uint16_t u = static_cast<uint16_t>(v >> 16);
+  _Float16 h;
+  __builtin_memcpy(&h, &u, 2);
+  return static_cast<float>(h);
+}
+
+// Element I/O traits: float or bf16 storage, fp32 arithmetic.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float *p, size_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float *p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<bf16_t> {
+  __device__ __forceinline__ static float load(const bf16_t *p, size_t i) {
+    return bf16_to_f32(p[i]);
+  }
+  __device__ __forceinline__ static void store(bf16_t *p, size_t i, float v) {
+    p[i] = f32_to_bf16(v);
+  }
+};
+
+// Pre-activation pair storage: float2 for fp32 I/O, fp16x2 in a uint32 for bf16 I/O.
+template <typename T> struct PrePair;
+template <> struct PrePair<float> {
+  typedef float2 type;
+  __device__ __forceinline__ static type pack(float pa, float px) { return make_float2(pa, px); }
+  __device__ __forceinline__ static float pa(type v) { return v.x; }
+  __device__ __forceinline__ static float px(type v) { return v.y; }
+};
+template <> struct PrePair<bf16_t> {
+  typedef uint32_t type;
+  __device__ __forceinline__ static type pack(float pa, float px) { return pack_f16x2(pa, px); }
+  __device__ __forceinline__ static float pa(type v) { return f16lo(v); }
+  __device__ __forceinline__ static float px(type v) { return f16hi(v); }
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Per-channel constant kd = -c * softplus(-Lambda), so that log a = kd * r. softplus is taken
+// as max(z,0) + log1p(exp(-|z|)); computed once per lane with the accurate library functions.
+__device__ __forceinline__ float decay_coeff(float lambda) {
+  float z = -lambda;
+  float sp = fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
+  return -kGateC * sp;
+}
+
+// 1 / (1 + exp(-v)) with the hardware exp2 and reciprocal. v = -inf.. : exp2 overflows to inf and
+// the reciprocal returns exactly 0; large positive v gives exp2 = 0 and exactly 1.
+__device__ __forceinline__ float fast_sigmoid(float v) {
+  float e = __builtin_amdgcn_exp2f(-v * kLog2e);
+  return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// expm1(z) for z <= 0 (log a is never positive).
+__device__ __forceinline__ float expm1_nonpos(float z) {
+  float p = fmaf(z, 1.0f / 5040.0f, 1.0f / 720.0f);
+  p = fmaf(z, p, 1.0f / 120.0f);
+  p = fmaf(z, p, 1.0f / 24.0f);
+  p = fmaf(z, p, 1.0f / 6.0f);
+  p = fmaf(z, p, 0.5f);
+  p = fmaf(z, p, 1.0f);
+  float e = z * p;
+  if (z < -0.25f) e = __builtin_amdgcn_exp2f(z * kLog2e) - 1.0f;
+  return e;
+}
+
+// One RG-LRU gate evaluation: returns the decay a and the gated, normalised input u.
+__device__ __forceinline__ void gate(float pa, float px, float xc, float kd, float &a, float &u) {
+  float r = fast_sigmoid(pa);
+  float ig = fast_sigmoid(px);
+  float e = expm1_nonpos(kd * r);
+  a = 1.0f + e;
+  float w = -e * (2.0f + e);  // 1 - a^2, >= 0
+  float m = __builtin_amdgcn_sqrtf(w);
+  u = m * (ig * xc);
+}
+
+}  // namespace rglru

@@ -1,0 +1,178 @@
+// rglru_gates.hip -- gate projections of the RG-LRU with the temporal Conv1D fused in front.
+//
+// pre[b][t][d] = (b_a[d] + (W_a[g] xc_t)[o], b_x[d] + (W_x[g] xc_t)[o]) with
+// xc_t = causal depthwise conv of width 4 (Soham De's Griffin thread, tweet on keeping the
+// recurrent block simple; the gates are state-free, alby13 blog, "Core Components of Griffin --
+// 1. RG-LRU", which is what lets them run as one batched contraction ahead of the scan).
+//
+// Two kernels:
+//  * gates_mfma<DH>: bf16 I/O, DH in {32, 64, 128, 256}. Conv in fp32 into an LDS tile (rounded
+//    to bf16 for the MFMA A operand), then the 64 x 2DH tile on v_mfma_f32_32x32x16_bf16 with
+//    fp32 accumulation; fp16 (pa, px) pairs out.
+//  * gates_valu<T>: any Dh <= 256, fp32 or bf16 I/O, plain fp32 FMAs (used for fp32 I/O, where
+//    the 1e-4 accuracy target leaves no room for bf16 operands, and for odd head sizes).
+#include "rglru_launch.h"
+#include "rglru_mfma.h"
+
+namespace rglru {
+
+template <int DH>
+__global__ __launch_bounds__(kThreads) void gates_mfma(
+    const bf16_t *__restrict__ x, const bf16_t *__restrict__ conv_w,
+    const bf16_t *__restrict__ W_a, const float *__restrict__ b_a,
+    const bf16_t *__restrict__ W_x, const float *__restrict__ b_x, uint32_t *__restrict__ pre,
+    int T, int D) {
+  typedef GateTile<DH> C;
+  __shared__ __attribute__((aligned(16))) bf16_t lds_a[kTileRows * C::kLda];
+
+  const int t0 = blockIdx.x * kTileRows;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+
+  // ---- conv prologue: thread = (channel pair p, row group rg); sliding window over its rows.
+  {
+    constexpr int P = DH / 2;
+    constexpr int RPG = kTileRows * P / kThreads;  // rows per thread
+    const int p = tid % P;
+    const int r0 = (tid / P) * RPG;
+    const int d0 = g * DH + 2 * p;
+    const uint32_t *xb = reinterpret_cast<const uint32_t *>(x + static_cast<size_t>(b) * T * D);
+    float w0[4], w1[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t wv = *reinterpret_cast<const uint32_t *>(conv_w + static_cast<size_t>(j) * D + d0);
+      w0[j] = bf16lo(wv);
+      w1[j] = bf16hi(wv);
+    }
+    float a0[3], a1[3];  // x[t-3], x[t-2], x[t-1] for the two channels
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      int t = t0 + r0 - 3 + k;
+      uint32_t v = (t >= 0 && t < T) ? xb[(static_cast<size_t>(t) * D + d0) >> 1] : 0u;
+      a0[k] = bf16lo(v);
+      a1[k] = bf16hi(v);
+    }
+#pragma unroll 4
+    for (int r = 0; r < RPG; ++r) {
+      int t = t0 + r0 + r;
+      uint32_t v = (t < T) ? xb[(static_cast<size_t>(t) * D + d0) >> 1] : 0u;
+      float c0 = bf16lo(v), c1 = bf16hi(v);
+      float y0 = fmaf(w0[3], c0, fmaf(w0[2], a0[2], fmaf(w0[1], a0[1], w0[0] * a0[0])));
+      float y1 = fmaf(w1[3], c1, fmaf(w1[2], a1[2], fmaf(w1[1], a1[1], w1[0] * a1[0])));
+      *reinterpret_cast<uint32_t *>(lds_a + (r0 + r) * C::kLda + 2 * p) = pack_bf16x2(y0, y1);
+      a0[0] = a0[1]; a0[1] = a0[2]; a0[2] = c0;
+      a1[0] = a1[1]; a1[1] = a1[2]; a1[2] = c1;
+    }
+  }
+  __syncthreads();
+
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  int gq0, rq0;
+  bool active;
+  C::assign(w, gq0, rq0, active);
+  if (!active) return;
+
+  f32x16_t acc[C::kGPW][C::kRPW][2];
+  const size_t woff = static_cast<size_t>(g) * DH * DH;
+  gate_tile_mfma<DH>(lds_a, W_a + woff, W_x + woff, gq0, rq0, lane, acc);
+
+  // ---- epilogue: bias, fp16 pair, store.
+#pragma unroll
+  for (int gi = 0; gi < C::kGPW; ++gi) {
+    const int d = g * DH + (gq0 + gi) * 32 + (lane & 31);
+    const float ba = b_a[d], bx = b_x[d];
+#pragma unroll
+    for (int ri = 0; ri < C::kRPW; ++ri)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int t = t0 + C::acc_row(rq0 + ri, j, lane);
+        if (t < T)
+          pre[(static_cast<size_t>(b) * T + t) * D + d] =
+              pack_f16x2(acc[gi][ri][0][j] + ba, acc[gi][ri][1][j] + bx);
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------------------------
+constexpr int kValuRows = 16;
+
+template <typename T>
+__global__ __launch_bounds__(256) void gates_valu(
+    const T *__restrict__ x, const T *__restrict__ conv_w, const T *__restrict__ W_a,
+    const float *__restrict__ b_a, const T *__restrict__ W_x, const float *__restrict__ b_x,
+    typename PrePair<T>::type *__restrict__ pre, int Tn, int D, int Dh) {
+  __shared__ float xc[kValuRows * 256];
+  const int t0 = blockIdx.x * kValuRows;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const T *xb = x + static_cast<size_t>(b) * Tn * D;
+  for (int e = threadIdx.x; e < kValuRows * Dh; e += blockDim.x) {
+    const int r = e / Dh, i = e % Dh;
+    const int d = g * Dh + i;
+    const int t = t0 + r;
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kConvW; ++j) {
+      const int s = t - (kConvW - 1) + j;
+      if (s >= 0 && s < Tn)
+        acc = fmaf(Elem<T>::load(conv_w, static_cast<size_t>(j) * D + d),
+                   Elem<T>::load(xb, static_cast<size_t>(s) * D + d), acc);
+    }
+    xc[r * Dh + i] = acc;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < kValuRows * Dh; e += blockDim.x) {
+    const int r = e / Dh, o = e % Dh;
+    const int t = t0 + r;
+    if (t >= Tn) continue;
+    const int d = g * Dh + o;
+    const size_t wr = (static_cast<size_t>(g) * Dh + o) * Dh;
+    float sa = 0.0f, sx = 0.0f;
+    for (int i = 0; i < Dh; ++i) {
+      const float v = xc[r * Dh + i];
+      sa = fmaf(Elem<T>::load(W_a, wr + i), v, sa);
+      sx = fmaf(Elem<T>::load(W_x, wr + i), v, sx);
+    }
+    pre[(static_cast<size_t>(b) * Tn + t) * D + d] = PrePair<T>::pack(sa + b_a[d], sx + b_x[d]);
+  }
+}
+
+// ----------------------------------------------------------------------------------------------
+hipError_t launch_gates(const void *x, const void *conv_w, const void *W_a, const float *b_a,
+                        const void *W_x, const float *b_x, void *pre, int B, int T, int D, int H,
+                        int io, hipStream_t s) {
+  const int Dh = D / H;
+  if (io == kBF16 && (Dh == 32 || Dh == 64 || Dh == 128 || Dh == 256)) {
+    dim3 grid((T + kTileRows - 1) / kTileRows, H, B);
+    const bf16_t *xx = static_cast<const bf16_t *>(x);
+    const bf16_t *cw = static_cast<const bf16_t *>(conv_w);
+    const bf16_t *wa = static_cast<const bf16_t *>(W_a);
+    const bf16_t *wx = static_cast<const bf16_t *>(W_x);
+    uint32_t *pp = static_cast<uint32_t *>(pre);
+    switch (Dh) {
+      case 32: gates_mfma<32><<<grid, kThreads, 0, s>>>(xx, cw, wa, b_a, wx, b_x, pp, T, D); break;
+      case 64: gates_mfma<64><<<grid, kThreads, 0, s>>>(xx, cw, wa, b_a, wx, b_x, pp, T, D); break;
+      case 128: gates_mfma<128><<<grid, kThreads, 0, s>>>(xx, cw, wa, b_a, wx, b_x, pp, T, D); break;
+      case 256: gates_mfma<256><<<grid, kThreads, 0, s>>>(xx, cw, wa, b_a, wx, b_x, pp, T, D); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  dim3 grid((T + kValuRows - 1) / kValuRows, H, B);
+  if (io == kBF16) {
+    gates_valu<bf16_t><<<grid, 256, 0, s>>>(
+        static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(conv_w),
+        static_cast<const bf16_t *>(W_a), b_a, static_cast<const bf16_t *>(W_x), b_x,
+        static_cast<uint32_t *>(pre), T, D, Dh);
+  } else {
+    gates_valu<float><<<grid, 256, 0, s>>>(
+        static_cast<const float *>(x), static_cast<const float *>(conv_w),
+        static_cast<const float *>(W_a), b_a, static_cast<const float *>(W_x), b_x,
+        static_cast<float2 *>(pre), T, D, Dh);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rglru

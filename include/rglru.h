@@ -1,0 +1,140 @@
+/*
+ * rglru.h -- C ABI of the MI355X (gfx950) library for Griffin's recurrent-block hot path:
+ * a causal depthwise temporal Conv1D of width 4 feeding the RG-LRU gated linear recurrence.
+ *
+ * What is computed (per batch b, channel d, time t; head g = d / Dh, o = d % Dh):
+ *   xc[t][d] = sum_{j=0..3} conv_w[j][d] * x[t-3+j][d]        x before t = 0 reads zero
+ *   pa = b_a[d] + sum_i W_a[g][o][i] * xc[t][g*Dh+i]          block-diagonal gates, out = W in
+ *   px = b_x[d] + sum_i W_x[g][o][i] * xc[t][g*Dh+i]
+ *   r = sigmoid(pa), i = sigmoid(px), log a = -8 * r * softplus(-Lambda[d])
+ *   h[t] = a * h[t-1] + sqrt(1 - a^2) * (i * xc[t]);   y[t] = h[t]
+ * Sources: the temporal Conv1D in the recurrent block and the recurrence gate that can drop the
+ * input at time t and keep the history (Soham De's Griffin thread, muskviewer.com, the tweets on
+ * keeping the recurrent block simple and on adding a Recurrent Gate to LRU); gates that do not
+ * read the recurrent state and a fixed-size state (alby13 blog "Beyond Transformer Architecture:
+ * Griffin and Google RecurrentGemma", section "Core Components of Griffin -- 1. RG-LRU"); the
+ * diagonal recurrence (Soham De's thread, tweet on S4D/LRU); the RG-LRU layer itself (Griffin
+ * paper page on docshare.wps.com: abstract, Introduction, section "Model Architecture").
+ *
+ * Conventions for every entry point:
+ *  - Pointers named x, y, conv_w, W_a, W_x, conv_state, workspace, b_a, b_x, Lambda, h0, h_T, h
+ *    are DEVICE pointers (hipMalloc'd or torch CUDA tensors on the current device), contiguous,
+ *    row-major, 16-byte aligned. The caller owns all memory; the library never allocates or
+ *    frees and keeps no state between calls, so calls on different streams with different
+ *    workspaces may run concurrently.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream. Execution is
+ *    asynchronous on that stream; the status reflects argument checks and launch errors only.
+ *  - Argument checks happen before any launch; a failed check launches nothing.
+ *  - dtype selects the element type of x, y, conv_w, W_a, W_x and conv_state (fp32 or bf16).
+ *    b_a, b_x, Lambda, h0, h_T and h are always fp32.
+ *  - Supported sizes: B, T, D, H, N >= 1; D % H == 0; Dh = D / H <= 256. bf16 with Dh in
+ *    {32, 64, 128, 256} runs the gate projections on MFMA; other shapes run them on the vector
+ *    ALU.
+ */
+#ifndef RGLRU_H
+#define RGLRU_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RGLRU_OK = 0,
+  RGLRU_ERR_INVALID_ARG = 1, /* null required pointer, bad size, aliasing output */
+  RGLRU_ERR_UNSUPPORTED = 2, /* dtype or Dh outside the supported set */
+  RGLRU_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query returned */
+  RGLRU_ERR_HIP = 4          /* a HIP launch reported an error */
+} rglru_status;
+
+typedef enum { RGLRU_F32 = 0, RGLRU_BF16 = 1 } rglru_dtype;
+
+/* How the time scan is parallelised. DIRECT: one lane per (b, d) walks all T steps.
+ * CHUNKED: time is cut into chunks; pass 1 reduces each chunk to (sum of log a, local state),
+ * pass 2 prefixes those summaries across chunks with a wavefront scan, pass 3 re-scans each chunk
+ * from its carry-in. Both give the same result up to fp32 rounding (the scan is associative). */
+typedef enum { RGLRU_PLAN_AUTO = 0, RGLRU_PLAN_DIRECT = 1, RGLRU_PLAN_CHUNKED = 2 } rglru_plan;
+
+/* Text for a status code (static storage, never NULL). */
+const char *rglru_status_string(rglru_status s);
+
+/* Bytes of device workspace rglru_forward needs for this shape, for any plan. Returns 0 when
+ * the shape is invalid. */
+size_t rglru_forward_workspace_size(int B, int T, int D, int H, rglru_dtype dt);
+
+/* The plan and chunk length RGLRU_PLAN_AUTO picks for this shape (host-side query, no launch).
+ * Writes *plan (RGLRU_PLAN_DIRECT or RGLRU_PLAN_CHUNKED) and *chunk_len (T for DIRECT). */
+rglru_status rglru_forward_plan_info(int B, int T, int D, int H, rglru_dtype dt, int *plan,
+                                     int *chunk_len);
+
+/* Full-sequence forward.
+ *  x       [B][T][D] dtype          input sequence (channels contiguous)
+ *  conv_w  [4][D]    dtype          temporal conv taps; conv_w[3] multiplies the current token
+ *  W_a     [H][Dh][Dh] dtype        recurrence-gate weights per head, [out][in]
+ *  b_a     [D] f32                  recurrence-gate bias
+ *  W_x     [H][Dh][Dh] dtype        input-gate weights per head, [out][in]
+ *  b_x     [D] f32                  input-gate bias
+ *  Lambda  [D] f32                  decay parameter (a = sigmoid(Lambda)^(8 r))
+ *  h0      [B][D] f32 or NULL       initial state (NULL: zeros)
+ *  y       [B][T][D] dtype, out     states h[t] rounded to dtype (round-to-nearest-even);
+ *                                   must not overlap x or the workspace
+ *  h_T     [B][D] f32 or NULL, out  final fp32 state
+ *  workspace / workspace_bytes      device scratch of at least rglru_forward_workspace_size()
+ * Returns RGLRU_OK or an error code; see the conventions above. */
+rglru_status rglru_forward(const void *x, const void *conv_w, const void *W_a, const float *b_a,
+                           const void *W_x, const float *b_x, const float *Lambda,
+                           const float *h0, void *y, float *h_T, int B, int T, int D, int H,
+                           rglru_dtype dt, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* rglru_forward with an explicit plan. chunk_len is used by RGLRU_PLAN_CHUNKED (0 = automatic,
+ * otherwise 1 <= chunk_len); it is ignored by the other plans. */
+rglru_status rglru_forward_planned(const void *x, const void *conv_w, const void *W_a,
+                                   const float *b_a, const void *W_x, const float *b_x,
+                                   const float *Lambda, const float *h0, void *y, float *h_T,
+                                   int B, int T, int D, int H, rglru_dtype dt, void *workspace,
+                                   size_t workspace_bytes, void *stream, rglru_plan plan,
+                                   int chunk_len);
+
+/* The gate projections alone (conv + block-diagonal matmuls + biases), as the forward computes
+ * them before its scan. pre [B][T][D] holds one (pa, px) pair per element: two fp16 values
+ * (pa in the low half) for bf16, two fp32 values (pa first) for fp32. */
+rglru_status rglru_gate_preacts(const void *x, const void *conv_w, const void *W_a,
+                                const float *b_a, const void *W_x, const float *b_x, void *pre,
+                                int B, int T, int D, int H, rglru_dtype dt, void *stream);
+
+/* Bytes of device workspace rglru_scan_preacts needs for this shape, for any plan with chunk
+ * length >= 16 (0 when the shape is invalid). */
+size_t rglru_scan_workspace_size(int B, int T, int D, int H, rglru_dtype dt);
+
+/* The scan stage alone: conv recomputed from x, gate nonlinearity and RG-LRU scan, reading the
+ * pre-activation pairs in the layout rglru_gate_preacts writes. Arguments as for
+ * rglru_forward_planned; `pre` must not overlap y; workspace holds only the chunk summaries
+ * (RGLRU_PLAN_DIRECT needs none: workspace may then be NULL). rglru_forward is exactly
+ * rglru_gate_preacts followed by this call. */
+rglru_status rglru_scan_preacts(const void *x, const void *pre, const void *conv_w,
+                                const float *Lambda, const float *h0, void *y, float *h_T, int B,
+                                int T, int D, int H, rglru_dtype dt, void *workspace,
+                                size_t workspace_bytes, void *stream, rglru_plan plan,
+                                int chunk_len);
+
+/* One decode step for N independent sequences, in place.
+ *  x_t         [N][D] dtype                new token per row
+ *  conv_state  [N][3][D] dtype, in/out     last three inputs, oldest first; becomes
+ *                                          (cs[1], cs[2], x_t)
+ *  h           [N][D] f32, in/out          recurrent state
+ *  y_t         [N][D] dtype, out           new state rounded to dtype; must not overlap the
+ *                                          other buffers
+ *  conv_w, W_a, b_a, W_x, b_x, Lambda      as for rglru_forward
+ * Returns RGLRU_OK or an error code. */
+rglru_status rglru_decode_step(const void *x_t, void *conv_state, float *h, void *y_t,
+                               const void *conv_w, const void *W_a, const float *b_a,
+                               const void *W_x, const float *b_x, const float *Lambda, int N,
+                               int D, int H, rglru_dtype dt, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RGLRU_H */

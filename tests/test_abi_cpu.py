@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI (no GPU, no kernel launch): the library loads, exports every
+entry point include/rglru.h declares, sizes its workspace as documented, picks plans, and rejects
+bad arguments with the documented status before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_linear_recurrence_conv1d_amd as rg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rglru.h")
+lib = rg._lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rglru_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 9, names
+    for n in names:
+        assert hasattr(lib, n), f"librglru.so does not export {n}"
+
+
+def test_status_strings():
+    for code in range(5):
+        s = rg.rglru_status_string(code)
+        assert isinstance(s, str) and s
+    assert rg.rglru_status_string(0) == "ok"
+    assert "unknown" in rg.rglru_status_string(99)
+
+
+def test_workspace_sizes():
+    B, T, D, H = 8, 2048, 2560, 10
+    pre = B * T * D * 4
+    nC = (T + 15) // 16
+    scan = B * nC * D * 8 + B * nC * D * 4
+    assert rg.rglru_scan_workspace_size(B, T, D, H, "bf16") >= scan
+    assert rg.rglru_forward_workspace_size(B, T, D, H, "bf16") >= pre + scan
+    assert rg.rglru_forward_workspace_size(B, T, D, H, "f32") >= 2 * pre + scan
+    assert rg.rglru_forward_workspace_size(B, T, D, 7, "bf16") == 0   # D % H != 0
+    assert rg.rglru_forward_workspace_size(0, T, D, H, "bf16") == 0
+    assert rg.rglru_forward_workspace_size(1, 1, 1024, 2, "bf16") == 0  # Dh = 512 > 256
+
+
+def test_auto_plan_choices():
+    assert rg.rglru_forward_plan_info(16, 4096, 4096, 16, "bf16") == ("direct", 4096)
+    plan, L = rg.rglru_forward_plan_info(8, 2048, 2560, 10, "bf16")
+    assert plan == "chunked" and 16 <= L < 2048
+    assert (8 * 2560) * ((2048 + L - 1) // L) >= 2 * 65536
+    plan, L = rg.rglru_forward_plan_info(1, 65536, 2560, 10, "bf16")
+    assert plan == "chunked" and 16 <= L < 65536
+    plan, L = rg.rglru_forward_plan_info(1, 256, 256, 16, "f32")
+    assert plan == "chunked" and L == 16
+    assert rg.rglru_forward_plan_info(1, 10, 256, 16, "f32") == ("direct", 10)
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails its checks before any launch
+
+
+def fwd(**kw):
+    a = dict(x=FAKE, conv_w=FAKE + 0x1000, W_a=FAKE + 0x2000, b_a=FAKE + 0x3000,
+             W_x=FAKE + 0x4000, b_x=FAKE + 0x5000, Lam=FAKE + 0x6000, h0=None,
+             y=0x7000000000, h_T=None, B=2, T=64, D=512, H=2, dt=rg.RGLRU_BF16, ws=None,
+             wsb=0, stream=None, plan=rg.RGLRU_PLAN_AUTO, chunk=0)
+    a.update(kw)
+    return lib.rglru_forward_planned(a["x"], a["conv_w"], a["W_a"], a["b_a"], a["W_x"],
+                                     a["b_x"], a["Lam"], a["h0"], a["y"], a["h_T"], a["B"],
+                                     a["T"], a["D"], a["H"], a["dt"], a["ws"], a["wsb"],
+                                     a["stream"], a["plan"], a["chunk"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), rg.RGLRU_ERR_INVALID_ARG),
+    (dict(y=None), rg.RGLRU_ERR_INVALID_ARG),
+    (dict(W_x=None), rg.RGLRU_ERR_INVALID_ARG),
+    (dict(Lam=None), rg.RGLRU_ERR_INVALID_ARG),
+    (dict(B=0), rg.RGLRU_ERR_INVALID_ARG),
+    (dict(T=0), rg.RGLRU_ERR_INVALID_ARG),
+    (dict(H=3), rg.RGLRU_ERR_INVALID_ARG),
+    (dict(D=1024, H=2), rg.RGLRU_ERR_UNSUPPORTED),    # Dh = 512
+    (dict(dt=7), rg.RGLRU_ERR_UNSUPPORTED),
+    (dict(x=FAKE + 2), rg.RGLRU_ERR_INVALID_ARG),     # misaligned
+    (dict(y=FAKE), rg.RGLRU_ERR_INVALID_ARG),         # y aliases x
+    (dict(), rg.RGLRU_ERR_WORKSPACE),                 # no workspace
+    (dict(ws=0x9000000000, wsb=100), rg.RGLRU_ERR_WORKSPACE),
+    (dict(plan=9), rg.RGLRU_ERR_INVALID_ARG),
+    (dict(plan=rg.RGLRU_PLAN_CHUNKED, chunk=-1), rg.RGLRU_ERR_INVALID_ARG),
+])
+def test_forward_argument_checks(kw, status):
+    assert fwd(**kw) == status
+
+
+def test_forward_workspace_overlapping_output_rejected():
+    n = rg.rglru_forward_workspace_size(2, 64, 512, 2, "bf16")
+    y = 0x7000000000
+    assert fwd(ws=y + 256, wsb=n) == rg.RGLRU_ERR_INVALID_ARG
+
+
+def test_decode_argument_checks():
+    def dec(**kw):
+        a = dict(x_t=FAKE, cs=FAKE + 0x100000, h=FAKE + 0x200000, y_t=FAKE + 0x300000,
+                 conv_w=FAKE + 0x400000, W_a=FAKE + 0x500000, b_a=FAKE + 0x600000,
+                 W_x=FAKE + 0x700000, b_x=FAKE + 0x800000, Lam=FAKE + 0x900000, N=4, D=512,
+                 H=2, dt=rg.RGLRU_BF16)
+        a.update(kw)
+        return lib.rglru_decode_step(a["x_t"], a["cs"], a["h"], a["y_t"], a["conv_w"], a["W_a"],
+                                     a["b_a"], a["W_x"], a["b_x"], a["Lam"], a["N"], a["D"],
+                                     a["H"], a["dt"], None)
+    assert dec(N=0) == rg.RGLRU_ERR_INVALID_ARG
+    assert dec(h=None) == rg.RGLRU_ERR_INVALID_ARG
+    assert dec(y_t=FAKE) == rg.RGLRU_ERR_INVALID_ARG          # y_t aliases x_t
+    assert dec(y_t=FAKE + 0x100000 + 2048) == rg.RGLRU_ERR_INVALID_ARG  # inside conv_state
+    assert dec(D=1024) == rg.RGLRU_ERR_UNSUPPORTED
+    assert dec(cs=FAKE + 0x100004) == rg.RGLRU_ERR_INVALID_ARG  # misaligned
+    assert dec(dt=5) == rg.RGLRU_ERR_UNSUPPORTED
+
+
+def test_gate_and_scan_stage_checks():
+    assert lib.rglru_gate_preacts(FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000,
+                                  FAKE + 0x4000, FAKE + 0x5000, None, 2, 64, 512, 2,
+                                  rg.RGLRU_BF16, None) == rg.RGLRU_ERR_INVALID_ARG
+    assert lib.rglru_gate_preacts(FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000,
+                                  FAKE + 0x4000, FAKE + 0x5000, FAKE, 2, 64, 512, 2,
+                                  rg.RGLRU_BF16, None) == rg.RGLRU_ERR_INVALID_ARG  # pre aliases x
+    # chunked scan without workspace
+    assert lib.rglru_scan_preacts(FAKE, 0x8000000000, FAKE + 0x1000, FAKE + 0x2000, None,
+                                  0x7000000000, None, 2, 64, 512, 2, rg.RGLRU_BF16, None, 0,
+                                  None, rg.RGLRU_PLAN_CHUNKED, 16) == rg.RGLRU_ERR_WORKSPACE

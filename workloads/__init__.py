@@ -123,3 +123,21 @@ def make_inputs(w: Workload, seed: int = 0, *, B: Optional[int] = None, T: Optio
         b_x = np.zeros(D, np.float32)
     return dict(x=x, conv_w=conv_w, W_a=W_a, W_x=W_x, b_a=b_a, b_x=b_x, Lam=lam, h0=h0,
                 conv_state=cs, B=B, T=T, D=D, H=H, dtype=w.dtype)
+
+
+def to_device(inp: dict, device="cuda"):
+    """torch tensors on `device` for the GPU side: I/O-dtype tensors for x, conv_w, W_a, W_x and
+    conv_state (exact, since the values are already representable), float32 for the rest."""
+    import torch
+
+    io = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+    out = {}
+    for k in ("x", "conv_w", "W_a", "W_x", "conv_state"):
+        if inp.get(k) is not None:
+            out[k] = torch.from_numpy(inp[k]).to(device=device, dtype=io).contiguous()
+    for k in ("b_a", "b_x", "Lam", "h0"):
+        if inp.get(k) is not None:
+            out[k] = torch.from_numpy(inp[k]).to(device=device, dtype=torch.float32).contiguous()
+        else:
+            out[k] = None
+    return out
