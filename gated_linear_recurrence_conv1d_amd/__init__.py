@@ -30,7 +30,9 @@ RGLRU_BF16 = 1
 RGLRU_PLAN_AUTO = 0
 RGLRU_PLAN_DIRECT = 1
 RGLRU_PLAN_CHUNKED = 2
-_PLANS = {"auto": RGLRU_PLAN_AUTO, "direct": RGLRU_PLAN_DIRECT, "chunked": RGLRU_PLAN_CHUNKED}
+RGLRU_PLAN_FUSED = 3
+_PLANS = {"auto": RGLRU_PLAN_AUTO, "direct": RGLRU_PLAN_DIRECT, "chunked": RGLRU_PLAN_CHUNKED,
+          "fused": RGLRU_PLAN_FUSED}
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -114,7 +116,8 @@ def rglru_forward_plan_info(B, T, D, H, dtype):
     plan, chunk = _i(), _i()
     _check(_lib.rglru_forward_plan_info(B, T, D, H, _dt(dtype), ctypes.byref(plan),
                                         ctypes.byref(chunk)), "rglru_forward_plan_info")
-    return {RGLRU_PLAN_DIRECT: "direct", RGLRU_PLAN_CHUNKED: "chunked"}[plan.value], chunk.value
+    return {RGLRU_PLAN_DIRECT: "direct", RGLRU_PLAN_CHUNKED: "chunked",
+            RGLRU_PLAN_FUSED: "fused"}[plan.value], chunk.value
 
 
 def _fwd_args(x, conv_w, W_a, b_a, W_x, b_x, Lam, h0, y, h_T):

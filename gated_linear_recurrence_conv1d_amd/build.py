@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "librglru.so")
-SOURCES = ["rglru_api.cpp", "rglru_gates.hip", "rglru_scan.hip", "rglru_decode.hip"]
+SOURCES = ["rglru_api.cpp", "rglru_gates.hip", "rglru_scan.hip", "rglru_decode.hip",
+           "rglru_fused.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

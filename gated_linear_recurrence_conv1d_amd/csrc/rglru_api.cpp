@@ -67,7 +67,9 @@ ScanCarve scan_carve(int B, int D, int nC) {
   return c;
 }
 
-// Resolves the plan to (direct?, chunk length). Returns false for an invalid plan request.
+enum Kind { kDirect, kChunked, kFused };
+
+// Scan-only plan resolution to (direct?, chunk length). Returns false for an invalid request.
 bool resolve_plan(int B, int T, int D, rglru_plan plan, int chunk_len, bool &direct, int &L) {
   if (plan == RGLRU_PLAN_AUTO) {
     L = auto_chunk(B, T, D);
@@ -83,6 +85,28 @@ bool resolve_plan(int B, int T, int D, rglru_plan plan, int chunk_len, bool &dir
     return false;
   }
   return true;
+}
+
+// Forward plan resolution: FUSED when asked for or (AUTO) when the shape supports it.
+rglru_status resolve_forward(int B, int T, int D, int H, rglru_dtype dt, rglru_plan plan,
+                             int chunk_len, Kind &kind, int &L) {
+  const int io = dt == RGLRU_BF16 ? kBF16 : kF32;
+  const bool fusable = rglru::fused_supported(io, D / H);
+  if (plan == RGLRU_PLAN_FUSED || (plan == RGLRU_PLAN_AUTO && fusable)) {
+    if (!fusable) return RGLRU_ERR_UNSUPPORTED;
+    kind = kFused;
+    L = 64;
+    return RGLRU_OK;
+  }
+  bool direct;
+  if (!resolve_plan(B, T, D, plan, chunk_len, direct, L)) return RGLRU_ERR_INVALID_ARG;
+  kind = direct ? kDirect : kChunked;
+  return RGLRU_OK;
+}
+
+size_t fused_bytes(int B, int T, int D, int H) {
+  return rglru::fused_ctrl_bytes(H) +
+         2 * rglru::fused_slots(B, T, H, D / H) * sizeof(unsigned long long);
 }
 
 rglru_status hip_status(hipError_t e) { return e == hipSuccess ? RGLRU_OK : RGLRU_ERR_HIP; }
@@ -109,7 +133,8 @@ size_t rglru_scan_workspace_size(int B, int T, int D, int H, rglru_dtype dt) {
 
 size_t rglru_forward_workspace_size(int B, int T, int D, int H, rglru_dtype dt) {
   if (check_shape(B, T, D, H, dt) != RGLRU_OK) return 0;
-  return align_up(pre_bytes(B, T, D, dt)) + rglru_scan_workspace_size(B, T, D, H, dt);
+  const size_t split = align_up(pre_bytes(B, T, D, dt)) + rglru_scan_workspace_size(B, T, D, H, dt);
+  return std::max(split, align_up(fused_bytes(B, T, D, H)));
 }
 
 rglru_status rglru_forward_plan_info(int B, int T, int D, int H, rglru_dtype dt, int *plan,
@@ -117,10 +142,11 @@ rglru_status rglru_forward_plan_info(int B, int T, int D, int H, rglru_dtype dt,
   rglru_status st = check_shape(B, T, D, H, dt);
   if (st != RGLRU_OK) return st;
   if (!plan || !chunk_len) return RGLRU_ERR_INVALID_ARG;
-  bool direct;
+  Kind kind;
   int L;
-  resolve_plan(B, T, D, RGLRU_PLAN_AUTO, 0, direct, L);
-  *plan = direct ? RGLRU_PLAN_DIRECT : RGLRU_PLAN_CHUNKED;
+  st = resolve_forward(B, T, D, H, dt, RGLRU_PLAN_AUTO, 0, kind, L);
+  if (st != RGLRU_OK) return st;
+  *plan = kind == kFused ? RGLRU_PLAN_FUSED : kind == kDirect ? RGLRU_PLAN_DIRECT : RGLRU_PLAN_CHUNKED;
   *chunk_len = L;
   return RGLRU_OK;
 }
@@ -141,6 +167,7 @@ rglru_status rglru_scan_preacts(const void *x, const void *pre, const void *conv
     if (p && !aligned(p, 4)) return RGLRU_ERR_INVALID_ARG;
   bool direct;
   int L;
+  if (plan == RGLRU_PLAN_FUSED) return RGLRU_ERR_INVALID_ARG;
   if (!resolve_plan(B, T, D, plan, chunk_len, direct, L)) return RGLRU_ERR_INVALID_ARG;
   const size_t io_bytes = static_cast<size_t>(B) * T * D * elem_bytes(dt);
   const size_t pb = pre_bytes(B, T, D, dt);
@@ -184,11 +211,24 @@ rglru_status rglru_forward_planned(const void *x, const void *conv_w, const void
   const void *vec4[] = {b_a, b_x, Lambda, h0, h_T};
   for (const void *p : vec4)
     if (p && !aligned(p, 4)) return RGLRU_ERR_INVALID_ARG;
-  bool direct;
+  Kind kind;
   int L;
-  if (!resolve_plan(B, T, D, plan, chunk_len, direct, L)) return RGLRU_ERR_INVALID_ARG;
+  st = resolve_forward(B, T, D, H, dt, plan, chunk_len, kind, L);
+  if (st != RGLRU_OK) return st;
   const size_t io_bytes = static_cast<size_t>(B) * T * D * elem_bytes(dt);
   if (overlaps(x, io_bytes, y, io_bytes)) return RGLRU_ERR_INVALID_ARG;
+  if (kind == kFused) {
+    const size_t need = fused_bytes(B, T, D, H);
+    if (!workspace || workspace_bytes < need) return RGLRU_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return RGLRU_ERR_INVALID_ARG;
+    if (overlaps(workspace, need, y, io_bytes) || overlaps(workspace, need, x, io_bytes))
+      return RGLRU_ERR_INVALID_ARG;
+    if (static_cast<long long>((T + 63) / 64) * B * H > 0x7fffffffLL) return RGLRU_ERR_UNSUPPORTED;
+    (void)hipGetLastError();  // start from a clean error state
+    return hip_status(rglru::launch_fused(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, h_T, B,
+                                          T, D, H, workspace, static_cast<hipStream_t>(stream)));
+  }
+  const bool direct = kind == kDirect;
   const size_t pre_area = align_up(pre_bytes(B, T, D, dt));
   const size_t need = pre_area + (direct ? 0 : scan_carve(B, D, (T + L - 1) / L).total);
   if (!workspace || workspace_bytes < need) return RGLRU_ERR_WORKSPACE;

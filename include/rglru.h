@@ -50,11 +50,23 @@ typedef enum {
 
 typedef enum { RGLRU_F32 = 0, RGLRU_BF16 = 1 } rglru_dtype;
 
-/* How the time scan is parallelised. DIRECT: one lane per (b, d) walks all T steps.
- * CHUNKED: time is cut into chunks; pass 1 reduces each chunk to (sum of log a, local state),
- * pass 2 prefixes those summaries across chunks with a wavefront scan, pass 3 re-scans each chunk
- * from its carry-in. Both give the same result up to fp32 rounding (the scan is associative). */
-typedef enum { RGLRU_PLAN_AUTO = 0, RGLRU_PLAN_DIRECT = 1, RGLRU_PLAN_CHUNKED = 2 } rglru_plan;
+/* How the forward is executed. DIRECT and CHUNKED first write the gate pre-activations to the
+ * workspace (MFMA gate projection), then scan: DIRECT has one lane per (b, d) walk all T steps;
+ * CHUNKED cuts time into chunks, pass 1 reduces each chunk to (sum of log a, local state), pass 2
+ * prefixes those summaries across chunks with a wavefront scan, pass 3 re-scans each chunk from
+ * its carry-in. FUSED (bf16, Dh in {32, 64, 128, 256}) does everything in one pass over 64-step
+ * tiles -- conv, MFMA gates, nonlinearity, in-tile scan -- and links the tiles of a sequence by a
+ * decoupled look-back, so HBM sees x once and y once. All give the same result up to fp32
+ * rounding and the rounding of stored pre-activations (the scan is associative). DIRECT and
+ * CHUNKED are bitwise deterministic; FUSED combines whichever predecessor tiles have published
+ * when it looks back, so its carried state is reproducible to fp32 rounding only. AUTO picks
+ * FUSED when supported, else DIRECT or CHUNKED by the number of channels. */
+typedef enum {
+  RGLRU_PLAN_AUTO = 0,
+  RGLRU_PLAN_DIRECT = 1,
+  RGLRU_PLAN_CHUNKED = 2,
+  RGLRU_PLAN_FUSED = 3
+} rglru_plan;
 
 /* Text for a status code (static storage, never NULL). */
 const char *rglru_status_string(rglru_status s);
@@ -64,7 +76,8 @@ const char *rglru_status_string(rglru_status s);
 size_t rglru_forward_workspace_size(int B, int T, int D, int H, rglru_dtype dt);
 
 /* The plan and chunk length RGLRU_PLAN_AUTO picks for this shape (host-side query, no launch).
- * Writes *plan (RGLRU_PLAN_DIRECT or RGLRU_PLAN_CHUNKED) and *chunk_len (T for DIRECT). */
+ * Writes *plan (RGLRU_PLAN_DIRECT, _CHUNKED or _FUSED) and *chunk_len (T for DIRECT, the tile
+ * length 64 for FUSED). */
 rglru_status rglru_forward_plan_info(int B, int T, int D, int H, rglru_dtype dt, int *plan,
                                      int *chunk_len);
 
@@ -89,7 +102,8 @@ rglru_status rglru_forward(const void *x, const void *conv_w, const void *W_a, c
                            void *stream);
 
 /* rglru_forward with an explicit plan. chunk_len is used by RGLRU_PLAN_CHUNKED (0 = automatic,
- * otherwise 1 <= chunk_len); it is ignored by the other plans. */
+ * otherwise 1 <= chunk_len); it is ignored by the other plans. RGLRU_PLAN_FUSED on an
+ * unsupported dtype / head size returns RGLRU_ERR_UNSUPPORTED. */
 rglru_status rglru_forward_planned(const void *x, const void *conv_w, const void *W_a,
                                    const float *b_a, const void *W_x, const float *b_x,
                                    const float *Lambda, const float *h0, void *y, float *h_T,
@@ -110,9 +124,10 @@ size_t rglru_scan_workspace_size(int B, int T, int D, int H, rglru_dtype dt);
 
 /* The scan stage alone: conv recomputed from x, gate nonlinearity and RG-LRU scan, reading the
  * pre-activation pairs in the layout rglru_gate_preacts writes. Arguments as for
- * rglru_forward_planned; `pre` must not overlap y; workspace holds only the chunk summaries
- * (RGLRU_PLAN_DIRECT needs none: workspace may then be NULL). rglru_forward is exactly
- * rglru_gate_preacts followed by this call. */
+ * rglru_forward_planned (plan AUTO, DIRECT or CHUNKED; FUSED is rejected as invalid, it has no
+ * separate scan stage); `pre` must not overlap y; workspace holds only the chunk summaries
+ * (RGLRU_PLAN_DIRECT needs none: workspace may then be NULL). rglru_forward with the DIRECT or
+ * CHUNKED plan is exactly rglru_gate_preacts followed by this call. */
 rglru_status rglru_scan_preacts(const void *x, const void *pre, const void *conv_w,
                                 const float *Lambda, const float *h0, void *y, float *h_T, int B,
                                 int T, int D, int H, rglru_dtype dt, void *workspace,

@@ -37,6 +37,8 @@ def test_status_strings():
 
 def test_workspace_sizes():
     B, T, D, H = 8, 2048, 2560, 10
+    tiles = (T // 64) * B * H
+    assert rg.rglru_forward_workspace_size(B, T, D, H, "bf16") >= 256 + 2 * tiles * (D // H) * 8
     pre = B * T * D * 4
     nC = (T + 15) // 16
     scan = B * nC * D * 8 + B * nC * D * 4
@@ -49,15 +51,19 @@ def test_workspace_sizes():
 
 
 def test_auto_plan_choices():
-    assert rg.rglru_forward_plan_info(16, 4096, 4096, 16, "bf16") == ("direct", 4096)
-    plan, L = rg.rglru_forward_plan_info(8, 2048, 2560, 10, "bf16")
+    # bf16 with Dh in {32, 64, 128, 256}: the single-pass fused plan over 64-step tiles
+    assert rg.rglru_forward_plan_info(16, 4096, 4096, 16, "bf16") == ("fused", 64)
+    assert rg.rglru_forward_plan_info(8, 2048, 2560, 10, "bf16") == ("fused", 64)
+    assert rg.rglru_forward_plan_info(1, 65536, 2560, 10, "bf16") == ("fused", 64)
+    # otherwise the split plans, chosen by how many channels there are to spread over lanes
+    assert rg.rglru_forward_plan_info(16, 4096, 4800, 100, "bf16") == ("direct", 4096)  # Dh 48
+    plan, L = rg.rglru_forward_plan_info(8, 2048, 2400, 50, "bf16")
     assert plan == "chunked" and 16 <= L < 2048
-    assert (8 * 2560) * ((2048 + L - 1) // L) >= 2 * 65536
-    plan, L = rg.rglru_forward_plan_info(1, 65536, 2560, 10, "bf16")
-    assert plan == "chunked" and 16 <= L < 65536
+    assert (8 * 2400) * ((2048 + L - 1) // L) >= 2 * 65536
     plan, L = rg.rglru_forward_plan_info(1, 256, 256, 16, "f32")
     assert plan == "chunked" and L == 16
     assert rg.rglru_forward_plan_info(1, 10, 256, 16, "f32") == ("direct", 10)
+    assert rg.rglru_forward_plan_info(16, 4096, 4096, 16, "f32") == ("direct", 4096)
 
 
 FAKE = 0x10000  # never dereferenced: every call below fails its checks before any launch
@@ -91,6 +97,9 @@ def fwd(**kw):
     (dict(ws=0x9000000000, wsb=100), rg.RGLRU_ERR_WORKSPACE),
     (dict(plan=9), rg.RGLRU_ERR_INVALID_ARG),
     (dict(plan=rg.RGLRU_PLAN_CHUNKED, chunk=-1), rg.RGLRU_ERR_INVALID_ARG),
+    (dict(plan=rg.RGLRU_PLAN_FUSED, D=96, H=2), rg.RGLRU_ERR_UNSUPPORTED),   # Dh = 48
+    (dict(plan=rg.RGLRU_PLAN_FUSED, dt=rg.RGLRU_F32), rg.RGLRU_ERR_UNSUPPORTED),
+    (dict(plan=rg.RGLRU_PLAN_FUSED), rg.RGLRU_ERR_WORKSPACE),
 ])
 def test_forward_argument_checks(kw, status):
     assert fwd(**kw) == status
@@ -128,6 +137,10 @@ def test_gate_and_scan_stage_checks():
     assert lib.rglru_gate_preacts(FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000,
                                   FAKE + 0x4000, FAKE + 0x5000, FAKE, 2, 64, 512, 2,
                                   rg.RGLRU_BF16, None) == rg.RGLRU_ERR_INVALID_ARG  # pre aliases x
+    # the fused plan has no separate scan stage
+    assert lib.rglru_scan_preacts(FAKE, 0x8000000000, FAKE + 0x1000, FAKE + 0x2000, None,
+                                  0x7000000000, None, 2, 64, 512, 2, rg.RGLRU_BF16, None, 0,
+                                  None, rg.RGLRU_PLAN_FUSED, 0) == rg.RGLRU_ERR_INVALID_ARG
     # chunked scan without workspace
     assert lib.rglru_scan_preacts(FAKE, 0x8000000000, FAKE + 0x1000, FAKE + 0x2000, None,
                                   0x7000000000, None, 2, 64, 512, 2, rg.RGLRU_BF16, None, 0,
