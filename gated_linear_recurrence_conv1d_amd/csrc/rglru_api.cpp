@@ -91,7 +91,7 @@ bool resolve_plan(int B, int T, int D, rglru_plan plan, int chunk_len, bool &dir
 rglru_status resolve_forward(int B, int T, int D, int H, rglru_dtype dt, rglru_plan plan,
                              int chunk_len, Kind &kind, int &L) {
   const int io = dt == RGLRU_BF16 ? kBF16 : kF32;
-  const bool fusable = rglru::fused_supported(io, D / H);
+  const bool fusable = rglru::fused_supported(io, T, D, D / H);
   if (plan == RGLRU_PLAN_FUSED || (plan == RGLRU_PLAN_AUTO && fusable)) {
     if (!fusable) return RGLRU_ERR_UNSUPPORTED;
     kind = kFused;

@@ -29,15 +29,14 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
 __device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-// fp32 -> bf16 with round-to-nearest-even (NaN stays NaN).
+// fp32 -> bf16 with round-to-nearest-even (gfx950 converts in hardware, v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  const bf16x2_v v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // (pa, px) pre-activation pair for the bf16 path: two fp16 values (round-to-nearest-even),
@@ -111,15 +110,20 @@ __device__ __forceinline__ float fast_sigmoid(float v) {
   return __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// expm1(z) for z <= 0 (log a is never positive).
-__device__ __forceinline__ float expm1_nonpos(float z) {
+// Taylor polynomial of expm1 on [-1/4, 0] (see the header comment).
+__device__ __forceinline__ float expm1_poly(float z) {
   float p = fmaf(z, 1.0f / 5040.0f, 1.0f / 720.0f);
   p = fmaf(z, p, 1.0f / 120.0f);
   p = fmaf(z, p, 1.0f / 24.0f);
   p = fmaf(z, p, 1.0f / 6.0f);
   p = fmaf(z, p, 0.5f);
   p = fmaf(z, p, 1.0f);
-  float e = z * p;
+  return z * p;
+}
+
+// expm1(z) for z <= 0 (log a is never positive).
+__device__ __forceinline__ float expm1_nonpos(float z) {
+  float e = expm1_poly(z);
   if (z < -0.25f) e = __builtin_amdgcn_exp2f(z * kLog2e) - 1.0f;
   return e;
 }

@@ -35,11 +35,12 @@ hipError_t launch_decode(const void *x_t, void *conv_state, float *h, void *y_t,
                          const float *b_x, const float *Lambda, int N, int D, int H, int io,
                          hipStream_t s);
 
-// Single-pass fused forward (bf16 I/O, Dh in {32, 64, 128, 256}): conv + MFMA gates + gate
+// Single-pass fused forward (bf16 I/O, Dh in {32, 64, 128, 256}, T * D < 2^31 so that offsets
+// within one sequence fit in 32 bits): conv + MFMA gates + gate
 // nonlinearity + scan with a decoupled look-back across 64-step time tiles. ctrl_ws:
 // fused_ctrl_bytes(H) of control words followed by 2 * fused_slots() 64-bit look-back words;
 // both are reset by the launcher before the main kernel.
-bool fused_supported(int io, int Dh);
+bool fused_supported(int io, int T, int D, int Dh);
 size_t fused_ctrl_bytes(int H);
 size_t fused_slots(int B, int T, int H, int Dh);
 hipError_t launch_fused(const void *x, const void *conv_w, const void *W_a, const float *b_a,
