@@ -42,16 +42,13 @@ constexpr unsigned long long kEmpty = ~0ull;
 constexpr int kFusedRows = 64;
 constexpr unsigned kMaxSpin = 1u << 26;  // bounded wait: a lost predecessor yields NaN, not a hang
 
-// A workgroup owns one part of one head -- kCPW channels: all of them when Dh <= 128, else one
-// half -- for its whole life (persistent), one wave per 32 channels, and walks that part's tiles
-// in ticket order. Two such workgroups share a CU (LDS ~68 KB and <= 256 VGPRs per wave each),
-// so one's MFMA phase overlaps the other's gate math. Each wave fetches its channels' W_a / W_x
-// rows (the MFMA B operand, 128 VGPRs at Dh = 256) at the start of every tile; they arrive while
-// the conv prologue runs, their registers are free again for the gate math, and the rows stay hot
-// in L2. The A tile holds all Dh input channels (the gates mix every channel of the head), so
-// the conv of a tile is computed by each of its parts.
+// A workgroup owns one head for its whole life (persistent) and walks that head's tiles in
+// ticket order: one wave per 32 channels (8 waves for Dh = 256, two per SIMD, one workgroup per
+// CU with a 100 KB LDS tile pair). Each wave keeps its channels' W_a / W_x rows -- the MFMA B
+// operand, 128 VGPRs at Dh = 256 -- in registers for the whole kernel, so the tile loop touches
+// HBM only for x and y. The conv of a tile is computed once, for all Dh channels.
 template <int DH> struct Fused {
-  static constexpr int kCPW = DH < 128 ? DH : 128;  // channels per workgroup
+  static constexpr int kCPW = DH;                   // channels per workgroup
   static constexpr int kNW = kCPW / 32;             // waves
   static constexpr int kParts = DH / kCPW;          // workgroups per (sequence, head) tile
   static constexpr int kThreads = 64 * kNW;
@@ -226,7 +223,7 @@ __device__ __forceinline__ void fused_epilogue(
   asm volatile("" : "+s"(Dv));
   bf16_t *yt = y + (static_cast<size_t>(tc.b) * T + tc.t0) * D;  // this tile's row 0
   const unsigned lane_off = static_cast<unsigned>(d - g * DH) + 4u * half * Dv;
-  bf16_t *yh = yt + g * DH;
+  char *yh = reinterpret_cast<char *>(yt + g * DH);
   float carry[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) carry[k] = fmaf(qz[k], h_in, cz[k]);
@@ -237,7 +234,7 @@ __device__ __forceinline__ void fused_epilogue(
       for (int jj = 0; jj < 16; ++jj) {
         const int r = rt * 32 + 8 * (jj >> 2) + (jj & 3);  // row of half 0; half 1: 4 further
         const float hv = fmaf(acc[rt][0][jj], carry[rt * 4 + (jj >> 2)], acc[rt][1][jj]);
-        yh[r * Dv + lane_off] = f32_to_bf16(hv);
+        *reinterpret_cast<bf16_t *>(yh + (r * Dv + lane_off) * 2u) = f32_to_bf16(hv);
       }
   } else {
 #pragma unroll
@@ -247,7 +244,7 @@ __device__ __forceinline__ void fused_epilogue(
         const int r = rt * 32 + 8 * (jj >> 2) + (jj & 3);
         const float hv = fmaf(acc[rt][0][jj], carry[rt * 4 + (jj >> 2)], acc[rt][1][jj]);
         const int t = tc.t0 + r + 4 * half;
-        if (t < T) yh[r * Dv + lane_off] = f32_to_bf16(hv);
+        if (t < T) *reinterpret_cast<bf16_t *>(yh + (r * Dv + lane_off) * 2u) = f32_to_bf16(hv);
         if (t == T - 1 && h_T) h_T[static_cast<size_t>(tc.b) * D + d] = hv;
       }
   }
@@ -285,22 +282,30 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
   const int d = g * DH + cl;
   const float kd = decay_coeff(Lambda[d]);
   const float ba2 = -kLog2e * b_a[d], bx2 = -kLog2e * b_x[d];
-  const bf16_t *wa_row = W_a + (static_cast<size_t>(g) * DH + cl) * DH + half * 8;
-  const bf16_t *wx_row = W_x + (static_cast<size_t>(g) * DH + cl) * DH + half * 8;
+  // B operand of this wave: its 32 channels' W_a / W_x rows, resident for the kernel's life
+  bf16x8_t wa[F::kKS], wx[F::kKS];
+  {
+    const bf16_t *wa_row = W_a + (static_cast<size_t>(g) * DH + cl) * DH + half * 8;
+    const bf16_t *wx_row = W_x + (static_cast<size_t>(g) * DH + cl) * DH + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < F::kKS; ++ks) {
+      wa[ks] = load_bf16x8(wa_row + ks * 16);
+      wx[ks] = load_bf16x8(wx_row + ks * 16);
+    }
+  }
 
   // conv-prologue role of this thread: channel pair pc0/pc0+1, rows pr0 .. pr0+PRPG-1
   constexpr int PP = DH / 2;
   constexpr int PRPG = kFusedRows * PP / F::kThreads;
   constexpr int PSUB = PRPG > 16 ? 16 : PRPG;  // rows per load batch (bounds live registers)
   const int pc0 = 2 * (tid % PP);
-  const int pr0 = (tid / PP) * PRPG;
+  // a wave spans whole row groups only when a row group is >= 64 lanes wide (Dh >= 128); then
+  // the row index is wave-uniform and all row arithmetic stays scalar
+  const int pr0 = PP % 64 == 0 ? __builtin_amdgcn_readfirstlane((tid / PP) * PRPG)
+                               : (tid / PP) * PRPG;
   const int pd0 = g * DH + pc0;
   const int pcf = pc0 - part * F::kCPW;
   const bool pmine = __builtin_amdgcn_readfirstlane(pcf >= 0 && pcf < F::kCPW);  // per wave
-  uint32_t cw[4];  // the pair's conv taps (bf16x2)
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    cw[k] = *reinterpret_cast<const uint32_t *>(conv_w + static_cast<size_t>(k) * D + pd0);
 
   for (int it = 0;; ++it) {
     if (tid == 0) s_tile[it & 1] = static_cast<int>(atomicAdd(ticket, 1u));
@@ -312,30 +317,25 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
     tc.b = tc.j % B;
     tc.t0 = tc.tt * kFusedRows;
 
-    // B operand of this wave (its 32 channels' W_a / W_x rows), fetched per tile from L2 so its
-    // registers are free during the gate math; the loads overlap the conv prologue.
-    bf16x8_t wa[F::kKS], wx[F::kKS];
-#pragma unroll
-    for (int ks = 0; ks < F::kKS; ++ks) {
-      wa[ks] = load_bf16x8(wa_row + ks * 16);
-      wx[ks] = load_bf16x8(wx_row + ks * 16);
-    }
-
     // ---- conv prologue (fp32). Thread = (channel pair p, run of rows r0..). Every load is
     // unconditional so that all of them are in flight at once: row indices past the end are
     // clamped to T-1 (those rows only feed rows >= T, whose results are discarded), and the three
     // halo rows before t = 0 are zeroed by a wave-uniform branch in the first tile only.
     // Offsets within one sequence fit in 32 bits (T * D < 2^31 is checked by the launcher).
     {
-      const uint32_t *xb =
-          reinterpret_cast<const uint32_t *>(x + static_cast<size_t>(tc.b) * T * D);
+      uint32_t cw[4];  // the pair's conv taps (bf16x2); re-read per tile (cache hits) to save VGPRs
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        cw[k] = *reinterpret_cast<const uint32_t *>(conv_w + static_cast<size_t>(k) * D + pd0);
+      const char *xb = reinterpret_cast<const char *>(x + static_cast<size_t>(tc.b) * T * D);
 #pragma unroll
       for (int rb = 0; rb < PRPG; rb += PSUB) {
         uint32_t xv[PSUB + 3];
 #pragma unroll
         for (int k = 0; k < PSUB + 3; ++k) {
-          const int t = min(max(tc.t0 + pr0 + rb - 3 + k, 0), T - 1);
-          xv[k] = xb[static_cast<unsigned>(t * D + pd0) >> 1];
+          const int t = min(max(tc.t0 + pr0 + rb - 3 + k, 0), T - 1);  // scalar
+          xv[k] = *reinterpret_cast<const uint32_t *>(xb + static_cast<unsigned>(t * D) * 2u +
+                                                      static_cast<unsigned>(pd0) * 2u);
         }
         if (tc.t0 + pr0 + rb == 0) {  // wave-uniform
           xv[0] = 0u;
@@ -418,12 +418,12 @@ hipError_t launch_fused(const void *x, const void *conv_w, const void *W_a, cons
   const bf16_t *wa = static_cast<const bf16_t *>(W_a);
   const bf16_t *wx = static_cast<const bf16_t *>(W_x);
   bf16_t *yy = static_cast<bf16_t *>(y);
-  // Persistent grid: about two workgroups per CU, the same number for every (head, part) pair.
-  // Extra workgroups that only start once others exit find the tickets used up and leave.
+  // Persistent grid: about one workgroup per CU, the same number for every head. Extra
+  // workgroups that only start once others exit find the tickets used up and leave.
 #define RGLRU_FUSED_CASE(DHV)                                                                   \
   case DHV: {                                                                                   \
     const int P2 = H * Fused<DHV>::kParts;                                                      \
-    const int per = std::max(1, (2 * cus + P2 - 1) / P2);                                       \
+    const int per = std::max(1, (cus + P2 - 1) / P2);                                       \
     fused_forward<DHV><<<P2 * per, Fused<DHV>::kThreads, 0, s>>>(                               \
         xx, cw, wa, b_a, wx, b_x, Lambda, h0, yy, h_T, B, T, D, H, nTT, ctrl, agg, incl);       \
     break;                                                                                      \
