@@ -17,6 +17,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
     # no packed fp32 (v_pk_*_f32) in generated device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep single-lane atomics (work tickets) as plain atomics: the wave-aggregating rewrite
+    # consumes the returned value right after the atomic, which would stall on its round trip
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]
 

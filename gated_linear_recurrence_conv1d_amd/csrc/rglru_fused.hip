@@ -41,6 +41,12 @@ namespace rglru {
 constexpr unsigned long long kEmpty = ~0ull;
 constexpr int kFusedRows = 64;
 constexpr unsigned kMaxSpin = 1u << 26;  // bounded wait: a lost predecessor yields NaN, not a hang
+constexpr unsigned kWaitVm0 = 0x0F70;     // s_waitcnt operand: vmcnt(0) only
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
+constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit data, no swizzle
 
 // A workgroup owns one head for its whole life (persistent) and walks that head's tiles in
 // ticket order: one wave per 32 channels (8 waves for Dh = 256, two per SIMD, one workgroup per
@@ -48,13 +54,14 @@ constexpr unsigned kMaxSpin = 1u << 26;  // bounded wait: a lost predecessor yie
 // operand, 128 VGPRs at Dh = 256 -- in registers for the whole kernel, so the tile loop touches
 // HBM only for x and y. The conv of a tile is computed once, for all Dh channels.
 template <int DH> struct Fused {
-  static constexpr int kCPW = DH;                   // channels per workgroup
-  static constexpr int kNW = kCPW / 32;             // waves
-  static constexpr int kParts = DH / kCPW;          // workgroups per (sequence, head) tile
+  static constexpr int kNW = DH / 32;                // waves, 32 channels each
   static constexpr int kThreads = 64 * kNW;
-  static constexpr int kKS = DH / 16;               // MFMA k-steps
-  static constexpr int kLda = DH + 8;               // bf16 A-tile row stride (elements)
-  static constexpr int kLdx = kCPW + 4;             // fp32 own-channel row stride (floats)
+  static constexpr int kKS = DH / 16;                // MFMA k-steps
+  static constexpr int kLda = DH + 8;                // bf16 A-tile row stride (elements)
+  static constexpr int kLdx = DH + 4;                // fp32 conv-output row stride (floats)
+  static constexpr int kRowsPerLoad = 1024 / (2 * DH);  // x rows per wave-wide 16 B/lane load
+  static constexpr int kLoads = (kFusedRows + 3 + kRowsPerLoad - 1) / kRowsPerLoad;
+  static constexpr int kXRows = kLoads * kRowsPerLoad;  // staged rows (tile + 3-row halo)
 };
 
 __device__ __forceinline__ unsigned long long pack2(float lo, float hi) {
@@ -100,39 +107,134 @@ struct TileCtx {
   int j, tt, b, t0;
 };
 
-// Gates, in-tile scan, look-back and output for one tile (accumulators in, y out). Rows past the
-// end of the sequence (only in the last tile) are computed like the others from zero input --
-// they come after every real row, so they cannot change a real row's state -- and only their
-// stores are masked; h_T is then taken at row T-1 instead of at the end of the tile.
+// Stage the x rows t0-3 .. t0+63 of one (sequence, head) tile -- the tile plus the conv halo --
+// into LDS with direct buffer-to-LDS loads (16 bytes per lane, one contiguous 1 KB block per
+// load), spread over the waves. The buffer covers exactly sequence b, so its range check returns
+// zeros for rows before t = 0 (the causal zero padding; negative offsets wrap past the end) and
+// for rows past T-1 (which only feed rows that are not stored).
 template <int DH>
-__device__ __forceinline__ void fused_epilogue(
-    f32x16_t (&acc)[2][2], const float *xf, int xcol, int lane, const TileCtx &tc, int g, int cl,
-    int d, float kd, float ba2, float bx2, const float *__restrict__ h0, bf16_t *__restrict__ y,
-    float *__restrict__ h_T, int B, int T, int D, int H, int nTT, unsigned *ctrl,
-    unsigned long long *agg, unsigned long long *incl) {
+__device__ __forceinline__ void stage_x(const bf16_t *__restrict__ x, bf16_t *xr, int b, int t0,
+                                        int g, int w, int lane, int T, int D) {
+  typedef Fused<DH> F;
+  constexpr int kLanesPerRow = DH / 8;
+  constexpr int kPerWave = (F::kLoads + F::kNW - 1) / F::kNW;
+  const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t *>(x + static_cast<size_t>(b) * T * D), static_cast<short>(0),
+      T * D * 2, kBufferWord3);
+  // opaque: keeps the compiler from folding the lane's row into a 64-bit multiply-add per load
+  unsigned lane_off =
+      static_cast<unsigned>((lane / kLanesPerRow) * 2 * D + g * DH * 2 + (lane % kLanesPerRow) * 16);
+  asm volatile("" : "+v"(lane_off));
+#pragma unroll
+  for (int k = 0; k < kPerWave; ++k) {
+    const int i = w + k * F::kNW;  // wave-uniform
+    if (kPerWave * F::kNW == F::kLoads || i < F::kLoads) {
+      const unsigned row_off = static_cast<unsigned>((t0 - 3 + i * F::kRowsPerLoad) * 2 * D);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(seq, (lds_void *)(xr + i * F::kRowsPerLoad * DH),
+                                               16, row_off + lane_off, 0, 0, 0);
+    }
+  }
+}
+
+// Conv prologue of one tile, fp32, from the staged rows (LDS row k holds time t0 - 3 + k, zero
+// before t = 0) into xa (bf16, the MFMA A operand) and xf (fp32, for the input term). Thread role:
+// channel pair pc0/pc0+1, rows pr0 .. pr0+PRPG-1. The role is re-derived from an opaque copy of
+// the thread index on every call so that none of it stays live (and gets spilled) across the
+// rest of the tile. A wave spans whole row groups only when a row group is >= 64 lanes wide
+// (Dh >= 128); then the row index is wave-uniform and stays scalar.
+template <int DH>
+__device__ __forceinline__ void conv_prologue(const bf16_t *xr, bf16_t *xa, float *xf,
+                                              const uint32_t *cws, int tid) {
+  typedef Fused<DH> F;
+  constexpr int PP = DH / 2;
+  constexpr int PRPG = kFusedRows * PP / F::kThreads;
+  constexpr int PSUB = PRPG > 4 ? 4 : PRPG;  // rows per batch (bounds live registers)
+  int tidv = tid;
+  asm volatile("" : "+v"(tidv));
+  const int pc0 = 2 * (tidv % PP);
+  const int pr0 = PP % 64 == 0 ? __builtin_amdgcn_readfirstlane((tidv / PP) * PRPG)
+                               : (tidv / PP) * PRPG;
+  // Words hold a bf16 pair of the two channels (taps: cws[k] = w_k of both). The conv output
+  // w0 x_{t-3} + w1 x_{t-2} + w2 x_{t-1} + w3 x_t is two bf16 dot products per channel (the
+  // products are exact in fp32), on time pairs (x_k, x_{k+1}) of one channel gathered with a
+  // byte permute.
+  uint32_t cw[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) cw[k] = cws[k * PP + (pc0 >> 1)];
+  constexpr uint32_t kLoPair = 0x05040100u, kHiPair = 0x07060302u;  // low / high halves of 2 words
+  const bf16x2_t w01l = as_bf16x2(__builtin_amdgcn_perm(cw[1], cw[0], kLoPair));
+  const bf16x2_t w23l = as_bf16x2(__builtin_amdgcn_perm(cw[3], cw[2], kLoPair));
+  const bf16x2_t w01h = as_bf16x2(__builtin_amdgcn_perm(cw[1], cw[0], kHiPair));
+  const bf16x2_t w23h = as_bf16x2(__builtin_amdgcn_perm(cw[3], cw[2], kHiPair));
+#pragma unroll
+  for (int rb = 0; rb < PRPG; rb += PSUB) {
+    uint32_t xv[PSUB + 3];
+#pragma unroll
+    for (int k = 0; k < PSUB + 3; ++k)
+      xv[k] = *reinterpret_cast<const uint32_t *>(xr + (pr0 + rb + k) * DH + pc0);
+    bf16x2_t pl[PSUB + 2], ph[PSUB + 2];  // (x_k, x_{k+1}) of the low / high channel
+#pragma unroll
+    for (int k = 0; k < PSUB + 2; ++k) {
+      pl[k] = as_bf16x2(__builtin_amdgcn_perm(xv[k + 1], xv[k], kLoPair));
+      ph[k] = as_bf16x2(__builtin_amdgcn_perm(xv[k + 1], xv[k], kHiPair));
+    }
+#pragma unroll
+    for (int r = 0; r < PSUB; ++r) {
+      const float o0 = __builtin_amdgcn_fdot2_f32_bf16(
+          pl[r + 2], w23l, __builtin_amdgcn_fdot2_f32_bf16(pl[r], w01l, 0.0f, false), false);
+      const float o1 = __builtin_amdgcn_fdot2_f32_bf16(
+          ph[r + 2], w23h, __builtin_amdgcn_fdot2_f32_bf16(ph[r], w01h, 0.0f, false), false);
+      const int row = pr0 + rb + r;
+      *reinterpret_cast<uint32_t *>(xa + row * F::kLda + pc0) = pack_bf16x2(o0, o1);
+      *reinterpret_cast<float2 *>(xf + row * F::kLdx + pc0) = make_float2(o0, o1);
+    }
+  }
+}
+
+// Gates and in-tile scan of one tile, in the accumulator layout. Accumulator jj of this lane
+// holds tile row rt*32 + 8*(jj/4) + 4*half + (jj%4): run k = rt*4 + jj/4 covers 4 consecutive
+// rows; in time order the runs alternate between the halves (run index 2k + half). On return
+// acc[rt][0][jj] is the product of a from the start of its run and acc[rt][1][jj] the state
+// reached from 0 at the start of its run; (qz[k], cz[k]) is the start of this lane's run k as an
+// affine map of the tile's carry-in; (At, Ut) is the whole tile's map.
+// expm1(log a): kds = kd 2^-nh with nh (wave-uniform) the smallest power that brings every
+// channel's kd into the polynomial's range [-1/4, 0]; the polynomial gives e' = expm1(z 2^-nh)
+// and nh doublings e <- e (e + 2) (exact algebra of expm1(2z) = expm1(z)(expm1(z) + 2), no
+// cancellation) recover e. nh = 0 for decays with a^c >= e^-1/4, which is every channel of the
+// usual configurations; the loop is wave-uniform, so that case costs nothing per element.
+template <int DH>
+__device__ __forceinline__ void gate_scan(f32x16_t (&acc)[2][2], const float *xf, int lane, int cl,
+                                          float kds, int nh, float ba2, float bx2, float (&cz)[8],
+                                          float (&qz)[8], float &At, float &Ut) {
   typedef Fused<DH> F;
   const int half = lane >> 5;
-  const int lrow = lane & 31;
-  // Accumulator jj of this lane holds tile row rt*32 + 8*(jj/4) + 4*half + (jj%4): run
-  // k = rt*4 + jj/4 covers 4 consecutive rows; in time order the runs alternate between the
-  // halves (run index 2k + half).
-  // (a) recurrence gate -> z = log a, overwriting the pa accumulator; track the smallest z.
-  float zmin = 0.0f;
+  // (a) recurrence gate -> e = expm1(log a), overwriting the pa accumulator. The sigmoids take
+  // exp2(-log2(e) (acc + b)), with ba2 = -log2(e) b_a folded into one FMA.
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
-      const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(acc[rt][0][jj] + ba2));
-      const float z = kd * r;
-      acc[rt][0][jj] = z;
-      zmin = fminf(zmin, z);
+      const float r = __builtin_amdgcn_rcpf(
+          1.0f + __builtin_amdgcn_exp2f(fmaf(acc[rt][0][jj], -kLog2e, ba2)));
+      acc[rt][0][jj] = expm1_poly(kds * r);
       if ((jj & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
-  // expm1 leaves its Taylor range only for fast decays; test once per tile for the whole wave.
-  const bool wide = __any(zmin < -0.25f);
+  if (nh > 0) {
+    for (int i = 0; i < nh; ++i)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) acc[rt][0][jj] *= acc[rt][0][jj] + 2.0f;
+    // a = exp(log a) >= 0: clamp what rounding (or an overflowing kd) may leave below -1
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) acc[rt][0][jj] = fmaxf(acc[rt][0][jj], -1.0f);
+  }
   // (b) input gate, normaliser, runs of 4 steps, and the chain over the 16 runs in time order:
   // this lane's run k pairs with the partner half's run k (runs 2k and 2k+1 of the tile).
-  float cz[8], qz[8];  // per own run: state from 0 at its start, product of a before it
+  // One base address per lane, all rows as constant offsets from it.
+  const float *xfl = xf + 4 * half * F::kLdx + cl;
   float c = 0.0f, qp = 1.0f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -141,20 +243,16 @@ __device__ __forceinline__ void fused_epilogue(
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
       const int jj = jb * 4 + e4;
-      const int row = rt * 32 + 8 * jb + 4 * half + e4;
-      const float z = acc[rt][0][jj];
-      float e = expm1_poly(z);
-      if (wide) {
-        if (z < -0.25f) e = __builtin_amdgcn_exp2f(z * kLog2e) - 1.0f;
-      }
+      const float e = acc[rt][0][jj];
       const float a = 1.0f + e;
       const float m = __builtin_amdgcn_sqrtf(-e * (2.0f + e));
-      const float ig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(acc[rt][1][jj] + bx2));
-      const float u = m * (ig * xf[row * F::kLdx + xcol]);
+      const float ig = __builtin_amdgcn_rcpf(
+          1.0f + __builtin_amdgcn_exp2f(fmaf(acc[rt][1][jj], -kLog2e, bx2)));
+      const float u = m * (ig * xfl[(rt * 32 + 8 * jb + e4) * F::kLdx]);
       S = fmaf(a, S, u);
       Pp *= a;
-      acc[rt][0][jj] = Pp;  // prefix product within the run
-      acc[rt][1][jj] = S;   // state within the run from 0
+      acc[rt][0][jj] = Pp;
+      acc[rt][1][jj] = S;
     }
     const float pa_ = __shfl_xor(Pp, 32, 64);
     const float pu_ = __shfl_xor(S, 32, 64);
@@ -168,88 +266,18 @@ __device__ __forceinline__ void fused_epilogue(
     // keep the scheduler from hoisting later runs' loads and transcendentals (live ranges)
     __builtin_amdgcn_sched_barrier(0);
   }
-  const float At = qp, Ut = c;  // the tile as one affine map of this channel
-
-  // (d) decoupled look-back on half 0 (one channel per lane).
-  float h_in = 0.0f;
-  if (half == 0) {
-    const size_t slot = (static_cast<size_t>(tc.j) * H + g) * DH + cl;  // j = tt*B + b
-    if (tc.tt + 1 < nTT) st_relaxed(agg + slot, pack2(At, Ut));
-    const float hstart = h0 ? h0[static_cast<size_t>(tc.b) * D + d] : 0.0f;
-    if (tc.tt == 0) {
-      h_in = hstart;
-    } else {
-      float Aacc = 1.0f, Uacc = 0.0f;
-      int jt = tc.tt - 1;
-      unsigned spins = 0;
-      for (;;) {
-        const size_t ps = ((static_cast<size_t>(jt) * B + tc.b) * H + g) * DH + cl;
-        const unsigned long long vi = ld_relaxed(incl + ps);
-        if (vi != kEmpty) {
-          h_in = fmaf(Aacc, lo_f(vi), Uacc);
-          break;
-        }
-        const unsigned long long va = ld_relaxed(agg + ps);
-        if (va != kEmpty) {
-          Uacc = fmaf(Aacc, hi_f(va), Uacc);
-          Aacc *= lo_f(va);
-          if (--jt < 0) {
-            h_in = fmaf(Aacc, hstart, Uacc);
-            break;
-          }
-          continue;
-        }
-        if (++spins > kMaxSpin) {
-          atomicAdd(ctrl + 1, 1u);
-          h_in = __builtin_nanf("");
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-    const float h_end = fmaf(At, h_in, Ut);
-    if (tc.tt + 1 < nTT)
-      st_relaxed(incl + slot, pack2(h_end, 0.0f));
-    else if (h_T && tc.t0 + kFusedRows == T)
-      h_T[static_cast<size_t>(tc.b) * D + d] = h_end;
-  }
-  h_in = __shfl(h_in, lrow, 64);
-
-  // (e) fix-up and store y. Row addresses are wave-uniform: a scalar row pointer plus the lane's
-  // 32-bit offset (its channel and its half's 4-row shift). Dv is re-materialised through an
-  // empty asm so that the compiler cannot hoist the 32 row offsets out of the tile loop (it
-  // would keep them in VGPRs, spill them and reload one per store).
-  unsigned Dv = static_cast<unsigned>(D);
-  asm volatile("" : "+s"(Dv));
-  bf16_t *yt = y + (static_cast<size_t>(tc.b) * T + tc.t0) * D;  // this tile's row 0
-  const unsigned lane_off = static_cast<unsigned>(d - g * DH) + 4u * half * Dv;
-  char *yh = reinterpret_cast<char *>(yt + g * DH);
-  float carry[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) carry[k] = fmaf(qz[k], h_in, cz[k]);
-  if (tc.t0 + kFusedRows <= T) {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const int r = rt * 32 + 8 * (jj >> 2) + (jj & 3);  // row of half 0; half 1: 4 further
-        const float hv = fmaf(acc[rt][0][jj], carry[rt * 4 + (jj >> 2)], acc[rt][1][jj]);
-        *reinterpret_cast<bf16_t *>(yh + (r * Dv + lane_off) * 2u) = f32_to_bf16(hv);
-      }
-  } else {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const int r = rt * 32 + 8 * (jj >> 2) + (jj & 3);
-        const float hv = fmaf(acc[rt][0][jj], carry[rt * 4 + (jj >> 2)], acc[rt][1][jj]);
-        const int t = tc.t0 + r + 4 * half;
-        if (t < T) *reinterpret_cast<bf16_t *>(yh + (r * Dv + lane_off) * 2u) = f32_to_bf16(hv);
-        if (t == T - 1 && h_T) h_T[static_cast<size_t>(tc.b) * D + d] = hv;
-      }
-  }
+  At = qp;
+  Ut = c;
 }
 
+// One tile per loop iteration, software-pipelined with the conv of the next tile:
+//   [barrier] MFMA(k) | stage rows of k+1, claim k+2 | gates + scan(k) | wait for the staged rows
+//   [barrier] publish aggregate(k), issue the first look-back loads | conv prologue(k+1) |
+//   finish look-back(k), publish inclusive(k) | fix-up and store y(k).
+// The look-back's memory round trip overlaps the next tile's conv. Rows past the end of the
+// sequence (only in the last tile) are computed like the others from zero input -- they come
+// after every real row, so they cannot change a real row's state -- and only their stores are
+// masked; h_T is then taken at row T-1 instead of at the end of the tile.
 template <int DH>
 __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ conv_w,
@@ -259,26 +287,24 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
     float *__restrict__ h_T, int B, int T, int D, int H, int nTT, unsigned *ctrl,
     unsigned long long *agg, unsigned long long *incl) {
   typedef Fused<DH> F;
-  // A tile: bf16(-log2(e) * conv output), so the accumulators come out in log2 units and the
-  // sigmoids need no extra multiply (the bf16 rounding error is the same as for the plain conv
-  // output). xf: the plain fp32 conv output of this part's channels, for the input term.
+  constexpr int PP = DH / 2;  // channel pairs
+  // xa: the conv output in bf16, the MFMA A operand; xf: the same in fp32 for the input term;
+  // xr: the staged x rows.
   __shared__ __attribute__((aligned(16))) bf16_t xa[kFusedRows * F::kLda];
   __shared__ __attribute__((aligned(16))) float xf[kFusedRows * F::kLdx];
-  __shared__ int s_tile[2];
+  __shared__ __attribute__((aligned(16))) bf16_t xr[F::kXRows * DH];
+  __shared__ uint32_t cws[4 * PP];  // conv taps of the head, bf16 pairs
+  __shared__ int s_tile[3];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lrow = lane & 31;
   const int half = lane >> 5;
-  const int P2 = H * F::kParts;
-  const int pair = blockIdx.x % P2;
-  const int g = pair / F::kParts;
-  const int part = pair % F::kParts;
+  const int g = blockIdx.x % H;
   const int ntiles = B * nTT;
-  unsigned *ticket = ctrl + 2 + pair;
-  const int xcol = w * 32 + lrow;           // this lane's channel within the part
-  const int cl = part * F::kCPW + xcol;     // ... within the head
+  unsigned *ticket = ctrl + 2 + g;
+  const int cl = w * 32 + lrow;  // this lane's channel within the head
   const int d = g * DH + cl;
   const float kd = decay_coeff(Lambda[d]);
   const float ba2 = -kLog2e * b_a[d], bx2 = -kLog2e * b_x[d];
@@ -293,72 +319,43 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
       wx[ks] = load_bf16x8(wx_row + ks * 16);
     }
   }
+  // kThreads == 4 * PP: one tap pair per thread
+  cws[tid] = *reinterpret_cast<const uint32_t *>(conv_w + static_cast<size_t>(tid / PP) * D +
+                                                 g * DH + 2 * (tid % PP));
+  // log a = kd r >= kd: halve until every channel of the wave is inside the polynomial's range
+  // (capped: beyond 2^-40, |kd| > 2.7e11 and a = 0 to fp32 precision; the clamp then gives it)
+  int nh = 0;
+  while (nh < 40 && __any(kd * __builtin_ldexpf(1.0f, -nh) < -0.25f)) ++nh;
+  nh = __builtin_amdgcn_readfirstlane(nh);
+  const float kds = kd * __builtin_ldexpf(1.0f, -nh);
 
-  // conv-prologue role of this thread: channel pair pc0/pc0+1, rows pr0 .. pr0+PRPG-1
-  constexpr int PP = DH / 2;
-  constexpr int PRPG = kFusedRows * PP / F::kThreads;
-  constexpr int PSUB = PRPG > 16 ? 16 : PRPG;  // rows per load batch (bounds live registers)
-  const int pc0 = 2 * (tid % PP);
-  // a wave spans whole row groups only when a row group is >= 64 lanes wide (Dh >= 128); then
-  // the row index is wave-uniform and all row arithmetic stays scalar
-  const int pr0 = PP % 64 == 0 ? __builtin_amdgcn_readfirstlane((tid / PP) * PRPG)
-                               : (tid / PP) * PRPG;
-  const int pd0 = g * DH + pc0;
-  const int pcf = pc0 - part * F::kCPW;
-  const bool pmine = __builtin_amdgcn_readfirstlane(pcf >= 0 && pcf < F::kCPW);  // per wave
+  // Tickets run two tiles ahead: while tile k computes, the rows of tile k+1 (claimed during
+  // tile k-1) are staged by all waves after the MFMA, and the ticket of tile k+2 is claimed then
+  // and published before the mid-tile barrier. s_tile is a ring of three.
+  if (tid == 0) {
+    s_tile[0] = static_cast<int>(atomicAdd(ticket, 1u));
+    s_tile[1] = static_cast<int>(atomicAdd(ticket, 1u));
+  }
+  __syncthreads();
+  {
+    const int j0 = __builtin_amdgcn_readfirstlane(s_tile[0]);
+    if (j0 < ntiles) stage_x<DH>(x, xr, j0 % B, (j0 / B) * kFusedRows, g, w, lane, T, D);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  }
 
-  for (int it = 0;; ++it) {
-    if (tid == 0) s_tile[it & 1] = static_cast<int>(atomicAdd(ticket, 1u));
-    __syncthreads();
+  int slot = 0;  // it % 3
+  for (;;) {
+    __syncthreads();  // this tile's conv in xa / xf; staging buffer free; tickets visible
     TileCtx tc;
-    tc.j = __builtin_amdgcn_readfirstlane(s_tile[it & 1]);
+    tc.j = __builtin_amdgcn_readfirstlane(s_tile[slot]);
     if (tc.j >= ntiles) break;
+    const int slot1 = slot == 2 ? 0 : slot + 1;
+    const int slot2 = slot1 == 2 ? 0 : slot1 + 1;
+    const int jn = __builtin_amdgcn_readfirstlane(s_tile[slot1]);
     tc.tt = tc.j / B;
     tc.b = tc.j % B;
     tc.t0 = tc.tt * kFusedRows;
-
-    // ---- conv prologue (fp32). Thread = (channel pair p, run of rows r0..). Every load is
-    // unconditional so that all of them are in flight at once: row indices past the end are
-    // clamped to T-1 (those rows only feed rows >= T, whose results are discarded), and the three
-    // halo rows before t = 0 are zeroed by a wave-uniform branch in the first tile only.
-    // Offsets within one sequence fit in 32 bits (T * D < 2^31 is checked by the launcher).
-    {
-      uint32_t cw[4];  // the pair's conv taps (bf16x2); re-read per tile (cache hits) to save VGPRs
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        cw[k] = *reinterpret_cast<const uint32_t *>(conv_w + static_cast<size_t>(k) * D + pd0);
-      const char *xb = reinterpret_cast<const char *>(x + static_cast<size_t>(tc.b) * T * D);
-#pragma unroll
-      for (int rb = 0; rb < PRPG; rb += PSUB) {
-        uint32_t xv[PSUB + 3];
-#pragma unroll
-        for (int k = 0; k < PSUB + 3; ++k) {
-          const int t = min(max(tc.t0 + pr0 + rb - 3 + k, 0), T - 1);  // scalar
-          xv[k] = *reinterpret_cast<const uint32_t *>(xb + static_cast<unsigned>(t * D) * 2u +
-                                                      static_cast<unsigned>(pd0) * 2u);
-        }
-        if (tc.t0 + pr0 + rb == 0) {  // wave-uniform
-          xv[0] = 0u;
-          xv[1] = 0u;
-          xv[2] = 0u;
-        }
-#pragma unroll
-        for (int r = 0; r < PSUB; ++r) {
-          const float o0 = fmaf(bf16lo(cw[3]), bf16lo(xv[r + 3]),
-                                fmaf(bf16lo(cw[2]), bf16lo(xv[r + 2]),
-                                     fmaf(bf16lo(cw[1]), bf16lo(xv[r + 1]),
-                                          bf16lo(cw[0]) * bf16lo(xv[r]))));
-          const float o1 = fmaf(bf16hi(cw[3]), bf16hi(xv[r + 3]),
-                                fmaf(bf16hi(cw[2]), bf16hi(xv[r + 2]),
-                                     fmaf(bf16hi(cw[1]), bf16hi(xv[r + 1]),
-                                          bf16hi(cw[0]) * bf16hi(xv[r]))));
-          const int row = pr0 + rb + r;
-          *reinterpret_cast<uint32_t *>(xa + row * F::kLda + pc0) =
-              pack_bf16x2(-kLog2e * o0, -kLog2e * o1);
-          if (pmine) *reinterpret_cast<float2 *>(xf + row * F::kLdx + pcf) = make_float2(o0, o1);
-        }
-      }
-    }
+    conv_prologue<DH>(xr, xa, xf, cws, tid);
     __syncthreads();
 
     // ---- gate projections on MFMA: 64 rows x (32 channels x 2 gates) per wave.
@@ -378,8 +375,117 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
       }
     }
 
-    fused_epilogue<DH>(acc, xf, xcol, lane, tc, g, cl, d, kd, ba2, bx2, h0, y, h_T, B, T, D, H,
-                       nTT, ctrl, agg, incl);
+    // ---- stage the next tile's rows (the prologue that read the buffer finished before the
+    // barrier above) and claim the tile after it; both complete during the gate math.
+    if (jn < ntiles) stage_x<DH>(x, xr, jn % B, (jn / B) * kFusedRows, g, w, lane, T, D);
+    unsigned claim = 0;
+    if (tid == 0) claim = atomicAdd(ticket, 1u);
+
+    float cz[8], qz[8], At, Ut;
+    gate_scan<DH>(acc, xf, lane, cl, kds, nh, ba2, bx2, cz, qz, At, Ut);
+
+
+    // ---- decoupled look-back on half 0 (one channel per lane): publish this tile's aggregate
+    // and put the first predecessor's two words in flight...
+    const size_t slot_me = (static_cast<size_t>(tc.j) * H + g) * DH + cl;  // j = tt*B + b
+    unsigned long long vi = kEmpty, va = kEmpty;
+    if (half == 0) {
+      if (tc.tt + 1 < nTT) st_relaxed(agg + slot_me, pack2(At, Ut));
+      if (tc.tt > 0) {
+        const size_t ps = ((static_cast<size_t>(tc.tt - 1) * B + tc.b) * H + g) * DH + cl;
+        vi = ld_relaxed(incl + ps);
+        va = ld_relaxed(agg + ps);
+      }
+    }
+
+    // ... and finish the look-back: combine aggregates until an inclusive state (or the start
+    // of the sequence) is found, then publish this tile's inclusive state.
+    float h_in = 0.0f;
+    if (half == 0) {
+      const float *h0b = h0 ? h0 + static_cast<size_t>(tc.b) * D + d : nullptr;
+      if (tc.tt == 0) {
+        h_in = h0b ? *h0b : 0.0f;
+      } else {
+        float Aacc = 1.0f, Uacc = 0.0f;
+        int jt = tc.tt - 1;
+        unsigned spins = 0;
+        for (;;) {
+          if (vi != kEmpty) {
+            h_in = fmaf(Aacc, lo_f(vi), Uacc);
+            break;
+          }
+          if (va != kEmpty) {
+            Uacc = fmaf(Aacc, hi_f(va), Uacc);
+            Aacc *= lo_f(va);
+            if (--jt < 0) {
+              h_in = fmaf(Aacc, h0b ? *h0b : 0.0f, Uacc);
+              break;
+            }
+          } else {
+            if (++spins > kMaxSpin) {
+              atomicAdd(ctrl + 1, 1u);
+              h_in = __builtin_nanf("");
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+          // both words in flight at once: one round trip per step
+          const size_t ps = ((static_cast<size_t>(jt) * B + tc.b) * H + g) * DH + cl;
+          vi = ld_relaxed(incl + ps);
+          va = ld_relaxed(agg + ps);
+        }
+      }
+      const float h_end = fmaf(At, h_in, Ut);
+      if (tc.tt + 1 < nTT)
+        st_relaxed(incl + slot_me, pack2(h_end, 0.0f));
+      else if (h_T && tc.t0 + kFusedRows == T)
+        h_T[static_cast<size_t>(tc.b) * D + d] = h_end;
+    }
+    h_in = __shfl(h_in, lrow, 64);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (tid == 0) s_tile[slot2] = static_cast<int>(claim);
+
+    // ---- fix-up and store y. Each run of 4 rows converts two rows per bf16 pair and stores
+    // the halves separately. Row addresses are wave-uniform: a scalar row pointer plus the
+    // lane's 32-bit byte offset (its channel and its half's 4-row shift). Dv is re-materialised
+    // through an empty asm so that the compiler cannot hoist the 32 row offsets out of the tile
+    // loop (it would keep them in registers, spill them and reload one per store).
+    unsigned Dv = static_cast<unsigned>(D);
+    asm volatile("" : "+s"(Dv));
+    const char *yg = reinterpret_cast<const char *>(
+        y + (static_cast<size_t>(tc.b) * T + tc.t0) * D + g * DH);  // tile row 0, head g
+    const unsigned lane_off = (static_cast<unsigned>(cl) + 4u * half * Dv) * 2u;
+    float carry[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) carry[k] = fmaf(qz[k], h_in, cz[k]);
+    if (tc.t0 + kFusedRows <= T) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < 16; jj += 2) {
+          const int r = rt * 32 + 8 * (jj >> 2) + (jj & 3);  // row of half 0; half 1: 4 further
+          const float c_ = carry[rt * 4 + (jj >> 2)];
+          uint32_t pk = pack_bf16x2(fmaf(acc[rt][0][jj], c_, acc[rt][1][jj]),
+                                    fmaf(acc[rt][0][jj + 1], c_, acc[rt][1][jj + 1]));
+          asm volatile("" : "+v"(pk));  // keep one conversion for the pair
+          char *row0 = const_cast<char *>(yg) + r * Dv * 2u;
+          *reinterpret_cast<bf16_t *>(row0 + lane_off) = static_cast<bf16_t>(pk);
+          *reinterpret_cast<bf16_t *>(row0 + Dv * 2u + lane_off) = static_cast<bf16_t>(pk >> 16);
+        }
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const int r = rt * 32 + 8 * (jj >> 2) + (jj & 3);
+          const float hv = fmaf(acc[rt][0][jj], carry[rt * 4 + (jj >> 2)], acc[rt][1][jj]);
+          const int t = tc.t0 + r + 4 * half;
+          char *row0 = const_cast<char *>(yg) + r * Dv * 2u;
+          if (t < T) *reinterpret_cast<bf16_t *>(row0 + lane_off) = f32_to_bf16(hv);
+          if (t == T - 1 && h_T) h_T[static_cast<size_t>(tc.b) * D + d] = hv;
+        }
+    }
+    slot = slot1;
   }
 }
 
@@ -391,8 +497,9 @@ size_t fused_slots(int B, int T, int H, int Dh) {
 }
 
 bool fused_supported(int io, int T, int D, int Dh) {
+  // byte offsets within one sequence, halo included, stay below 2^32 and wrap past its end
   return io == kBF16 && (Dh == 32 || Dh == 64 || Dh == 128 || Dh == 256) &&
-         static_cast<long long>(T) * D < (1LL << 31);
+         (static_cast<long long>(T) + 3) * D < (1LL << 31);
 }
 
 hipError_t launch_fused(const void *x, const void *conv_w, const void *W_a, const float *b_a,
@@ -422,9 +529,8 @@ hipError_t launch_fused(const void *x, const void *conv_w, const void *W_a, cons
   // workgroups that only start once others exit find the tickets used up and leave.
 #define RGLRU_FUSED_CASE(DHV)                                                                   \
   case DHV: {                                                                                   \
-    const int P2 = H * Fused<DHV>::kParts;                                                      \
-    const int per = std::max(1, (cus + P2 - 1) / P2);                                       \
-    fused_forward<DHV><<<P2 * per, Fused<DHV>::kThreads, 0, s>>>(                               \
+    const int per = std::max(1, (cus + H - 1) / H);                                             \
+    fused_forward<DHV><<<H * per, Fused<DHV>::kThreads, 0, s>>>(                                \
         xx, cw, wa, b_a, wx, b_x, Lambda, h0, yy, h_T, B, T, D, H, nTT, ctrl, agg, incl);       \
     break;                                                                                      \
   }
