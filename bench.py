@@ -74,8 +74,9 @@ def cpu_baseline(w, inp):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    # the warm-up also brings the GPU clocks up to their steady state (a few hundred ms)
+    ap.add_argument("--warmup", type=int, default=3000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="rg2b")
     args = ap.parse_args()

@@ -14,9 +14,10 @@
 // tile only ever waits for tiles with smaller tickets of the same head, all of which have been
 // claimed by running workgroups: forward progress does not depend on how the hardware schedules
 // workgroups. Per tile:
-//   1. conv in fp32 from x (3-row halo) into LDS (a bf16 copy as the MFMA A operand);
+//   1. conv in fp32 from the tile's x rows (3-row halo), staged in LDS during the previous tile,
+//      into LDS (a bf16 copy as the MFMA A operand, an fp32 copy for the input term);
 //   2. [64 x Dh] x [Dh x 2Dh] on v_mfma_f32_32x32x16_bf16, fp32 accumulators; the B operand is
-//      this head's W_a / W_x rows, fetched per tile into registers (hot in L2);
+//      this head's W_a / W_x rows, resident in registers for the kernel's life;
 //   3. gates elementwise in the accumulator layout -> (a, u) per element;
 //   4. scan inside the tile: each lane owns one channel and four runs of 4 consecutive steps per
 //      32-row tile, interleaved with its partner lane (lane ^ 32); in-lane scans of the runs,
@@ -112,12 +113,12 @@ struct TileCtx {
 // load), spread over the waves. The buffer covers exactly sequence b, so its range check returns
 // zeros for rows before t = 0 (the causal zero padding; negative offsets wrap past the end) and
 // for rows past T-1 (which only feed rows that are not stored).
-template <int DH>
+template <int DH, int NW>
 __device__ __forceinline__ void stage_x(const bf16_t *__restrict__ x, bf16_t *xr, int b, int t0,
                                         int g, int w, int lane, int T, int D) {
   typedef Fused<DH> F;
   constexpr int kLanesPerRow = DH / 8;
-  constexpr int kPerWave = (F::kLoads + F::kNW - 1) / F::kNW;
+  constexpr int kPerWave = (F::kLoads + NW - 1) / NW;
   const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16_t *>(x + static_cast<size_t>(b) * T * D), static_cast<short>(0),
       T * D * 2, kBufferWord3);
@@ -127,8 +128,8 @@ __device__ __forceinline__ void stage_x(const bf16_t *__restrict__ x, bf16_t *xr
   asm volatile("" : "+v"(lane_off));
 #pragma unroll
   for (int k = 0; k < kPerWave; ++k) {
-    const int i = w + k * F::kNW;  // wave-uniform
-    if (kPerWave * F::kNW == F::kLoads || i < F::kLoads) {
+    const int i = w + k * NW;  // wave-uniform
+    if (kPerWave * NW == F::kLoads || i < F::kLoads) {
       const unsigned row_off = static_cast<unsigned>((t0 - 3 + i * F::kRowsPerLoad) * 2 * D);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(seq, (lds_void *)(xr + i * F::kRowsPerLoad * DH),
                                                16, row_off + lane_off, 0, 0, 0);
@@ -270,14 +271,12 @@ __device__ __forceinline__ void gate_scan(f32x16_t (&acc)[2][2], const float *xf
   Ut = c;
 }
 
-// One tile per loop iteration, software-pipelined with the conv of the next tile:
-//   [barrier] MFMA(k) | stage rows of k+1, claim k+2 | gates + scan(k) | wait for the staged rows
-//   [barrier] publish aggregate(k), issue the first look-back loads | conv prologue(k+1) |
-//   finish look-back(k), publish inclusive(k) | fix-up and store y(k).
-// The look-back's memory round trip overlaps the next tile's conv. Rows past the end of the
-// sequence (only in the last tile) are computed like the others from zero input -- they come
-// after every real row, so they cannot change a real row's state -- and only their stores are
-// masked; h_T is then taken at row T-1 instead of at the end of the tile.
+// One tile per loop iteration:
+//   [barrier] claim k+1 | conv(k) from the staged rows | [barrier] MFMA(k) | publish k+1 and stage
+//   its rows | gates + scan(k) | look-back(k) | wait for the staged rows | fix-up and store y(k).
+// Rows past the end of the sequence (only in the last tile) are computed like the others from
+// zero input -- they come after every real row, so they cannot change a real row's state -- and
+// only their stores are masked; h_T is then taken at row T-1 instead of at the end of the tile.
 template <int DH>
 __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ conv_w,
@@ -329,17 +328,15 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
   nh = __builtin_amdgcn_readfirstlane(nh);
   const float kds = kd * __builtin_ldexpf(1.0f, -nh);
 
-  // Tickets run two tiles ahead: while tile k computes, the rows of tile k+1 (claimed during
-  // tile k-1) are staged by all waves after the MFMA, and the ticket of tile k+2 is claimed then
-  // and published before the mid-tile barrier. s_tile is a ring of three.
-  if (tid == 0) {
-    s_tile[0] = static_cast<int>(atomicAdd(ticket, 1u));
-    s_tile[1] = static_cast<int>(atomicAdd(ticket, 1u));
-  }
+  // Tickets run one tile ahead: tile k+1 is claimed at the start of tile k, and after the MFMA
+  // wave 0 publishes it and stages its rows, so the ticket round trip and the x loads overlap
+  // the conv, the MFMA and the gate math. (Claiming further ahead lets a tile wait behind two
+  // of its owner's tiles, and its successors in time wait on it.) s_tile is a ring of three.
+  if (tid == 0) s_tile[0] = static_cast<int>(atomicAdd(ticket, 1u));
   __syncthreads();
   {
     const int j0 = __builtin_amdgcn_readfirstlane(s_tile[0]);
-    if (j0 < ntiles) stage_x<DH>(x, xr, j0 % B, (j0 / B) * kFusedRows, g, w, lane, T, D);
+    if (j0 < ntiles) stage_x<DH, F::kNW>(x, xr, j0 % B, (j0 / B) * kFusedRows, g, w, lane, T, D);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
   }
 
@@ -350,8 +347,8 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
     tc.j = __builtin_amdgcn_readfirstlane(s_tile[slot]);
     if (tc.j >= ntiles) break;
     const int slot1 = slot == 2 ? 0 : slot + 1;
-    const int slot2 = slot1 == 2 ? 0 : slot1 + 1;
-    const int jn = __builtin_amdgcn_readfirstlane(s_tile[slot1]);
+    unsigned claim = 0;
+    if (tid == 0) claim = atomicAdd(ticket, 1u);
     tc.tt = tc.j / B;
     tc.b = tc.j % B;
     tc.t0 = tc.tt * kFusedRows;
@@ -376,10 +373,12 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
     }
 
     // ---- stage the next tile's rows (the prologue that read the buffer finished before the
-    // barrier above) and claim the tile after it; both complete during the gate math.
-    if (jn < ntiles) stage_x<DH>(x, xr, jn % B, (jn / B) * kFusedRows, g, w, lane, T, D);
-    unsigned claim = 0;
-    if (tid == 0) claim = atomicAdd(ticket, 1u);
+    // barrier above); they land during the gate math.
+    if (w == 0) {
+      const int jn = __builtin_amdgcn_readfirstlane(claim);
+      if (lane == 0) s_tile[slot1] = jn;
+      if (jn < ntiles) stage_x<DH, 1>(x, xr, jn % B, (jn / B) * kFusedRows, g, 0, lane, T, D);
+    }
 
     float cz[8], qz[8], At, Ut;
     gate_scan<DH>(acc, xf, lane, cl, kds, nh, ba2, bx2, cz, qz, At, Ut);
@@ -442,8 +441,9 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
         h_T[static_cast<size_t>(tc.b) * D + d] = h_end;
     }
     h_in = __shfl(h_in, lrow, 64);
+    // The staged rows must have landed before the barrier that opens the next tile; waiting here
+    // (the look-back has mostly waited already) keeps this tile's stores out of the wait.
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    if (tid == 0) s_tile[slot2] = static_cast<int>(claim);
 
     // ---- fix-up and store y. Each run of 4 rows converts two rows per bf16 pair and stores
     // the halves separately. Row addresses are wave-uniform: a scalar row pointer plus the
