@@ -57,6 +57,88 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -d OUT/trace -o bench --output-format csv -- "
+             "python3 REPO/bench.py --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'fused_forward|copyBuffer' -d "
+             "OUT/fetch -o fetch --output-format csv -- python3 REPO/bench.py --steps 5 "
+             "--warmup 5 --no-cpu-baseline --copy-calibration 256",
+    "write": "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'fused_forward|copyBuffer' -d "
+             "OUT/write -o write --output-format csv -- python3 REPO/bench.py --steps 5 "
+             "--warmup 5 --no-cpu-baseline --copy-calibration 256",
+}
+
+
+def _counter_rows(path):
+    import csv
+    return list(csv.DictReader(open(path)))
+
+
+def traffic_summary(fetch_csv, write_csv, workload, copy_mib=256):
+    """HBM bytes per launch of the fused kernel from two rocprofv3 counter passes (FETCH_SIZE and
+    WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for the device copy
+    of copy_mib MiB in the same run (which reads and writes exactly copy_mib MiB)."""
+    out = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _counter_rows(path) if r["Counter_Name"] == name]
+        fused = [float(r["Counter_Value"]) for r in rows if "fused_forward" in r["Kernel_Name"]]
+        copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if not fused or not copy:
+            raise SystemExit(f"{path}: no fused_forward or copy dispatches with {name}")
+        copy_kib = max(copy)  # the calibration copies are by far the largest
+        factor = copy_mib * 1024.0 / copy_kib
+        out[name] = (sum(fused) / len(fused), len(fused), copy_kib, factor)
+    hbm = sum(v[0] * v[3] for v in out.values()) * 1024.0
+    path = os.path.join(ROOT, "profiles", f"traffic_fused_{workload}.txt")
+    with open(path, "w") as f:
+        f.write("# HBM traffic of the fused forward kernel, from rocprofv3 counters.\n")
+        f.write("# Made by (REPO = this repository, OUT = a scratch directory; run from /tmp):\n")
+        f.write(f"#   {PROFILE_CMDS['fetch']}\n#   {PROFILE_CMDS['write']}\n")
+        f.write("#   python3 REPO/bench.py --traffic-summary OUT/fetch/fetch_counter_collection.csv "
+                "OUT/write/write_counter_collection.csv\n")
+        f.write("# Each counter (KiB per dispatch, summed over the chip) is scaled by copy MiB * 1024 /\n"
+                "# what it reads for the device copy of that size in the same run.\n")
+        f.write(f"workload: {workload}\n")
+        f.write(f"source_hash: {kernel_source_hash()}\n")
+        for name, (kib, n, copy_kib, factor) in out.items():
+            f.write(f"{name.lower()}_kib_per_launch: {kib:.1f}\n")
+            f.write(f"{name.lower()}_dispatches: {n}\n")
+            f.write(f"{name.lower()}_copy_{copy_mib}mib_kib: {copy_kib:.1f}\n")
+            f.write(f"{name.lower()}_calibration_factor: {factor:.4f}\n")
+        f.write(f"hbm_bytes_per_launch: {hbm:.0f}\n")
+    print(open(path).read(), end="")
+
+
+def trace_summary(stats_csv, workload, bench_line_path=None):
+    """Condensed rocprofv3 --kernel-trace --stats summary (per-kernel calls and durations)."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_fused_{workload}.txt")
+    with open(path, "w") as f:
+        f.write("# rocprofv3 kernel-trace statistics of the default bench run.\n")
+        f.write("# Made by (REPO = this repository, OUT = a scratch directory; run from /tmp):\n")
+        f.write(f"#   {PROFILE_CMDS['trace']}\n")
+        f.write("#   python3 REPO/bench.py --trace-summary OUT/trace/bench_kernel_stats.csv "
+                "[OUT/trace/stdout.txt]\n")
+        f.write(f"workload: {workload}\n")
+        f.write(f"source_hash: {kernel_source_hash()}\n")
+        f.write(f"{'calls':>7} {'avg_us':>9} {'min_us':>9} {'max_us':>9}  kernel\n")
+        for r in rows:
+            name = r["Name"].split("(")[0].replace("void ", "")
+            f.write(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.2f} "
+                    f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}  {name}\n")
+        per_call = sum(float(r["AverageNs"]) for r in rows
+                       if "fused_forward" in r["Name"] or "fused_reset" in r["Name"]) / 1e3
+        f.write(f"fused_call_us (fused_forward + fused_reset, one rglru_forward): {per_call:.2f}\n")
+        if bench_line_path:
+            for line in open(bench_line_path):
+                if line.startswith('{"metric"'):
+                    d = json.loads(line)
+                    f.write(f"bench_ms_per_step: {d['ms_per_step']}\n")
+                    f.write(f"bench_roofline_kernel_ms: {d['roofline']['kernel_ms']}\n")
+    print(open(path).read(), end="")
+
+
 def cpu_baseline(w, inp):
     """The fp64 oracle, as it stands, on the host cores: the full workload (B=8, T=2048, D=2560,
     all heads) takes a few seconds of wall time on a multi-core host."""
@@ -79,7 +161,25 @@ def main():
     ap.add_argument("--warmup", type=int, default=3000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="rg2b")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed region, copy a MIB-MiB device buffer three times (the "
+                         "known-size reference for rocprofv3 byte counters)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_fused_<workload>.txt from two rocprofv3 counter "
+                         "passes and exit (no GPU needed)")
+    ap.add_argument("--trace-summary", nargs="+", metavar="CSV",
+                    help="write profiles/kernel_trace_fused_<workload>.txt from a rocprofv3 "
+                         "kernel_stats.csv (and optionally the bench stdout) and exit")
     args = ap.parse_args()
+    if args.traffic_summary or args.trace_summary:
+        from workloads import WORKLOADS
+        wname = WORKLOADS[args.workload].name
+        if args.traffic_summary:
+            traffic_summary(*args.traffic_summary, wname)
+        if args.trace_summary:
+            trace_summary(args.trace_summary[0], wname,
+                          args.trace_summary[1] if len(args.trace_summary) > 1 else None)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards over batch and heads without communication; see DESIGN.md)",
@@ -200,6 +300,12 @@ def main():
         "wall_s_timed": round(wall, 4),
         "alg_gbs_end_to_end": round((n * 2 * eb + wbytes) / (ms * 1e-3) / 1e9, 1),
     }
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(line), flush=True)

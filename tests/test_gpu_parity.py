@@ -233,6 +233,30 @@ def test_plans_agree():
         assert err(host(hc), host(hd)) < (1e-4 if plan == "chunked" else 1e-2)
 
 
+def test_fused_ignores_workspace_contents():
+    """The fused plan clears its look-back words on every call, so neither garbage nor the words
+    of earlier calls (of other shapes, on the same buffer) can leak into a result."""
+    shapes = [(2, 300, 512, 2), (1, 130, 256, 1), (3, 200, 512, 2)]
+    cases = [case("bf16", *s, seed=5 + i) for i, s in enumerate(shapes)]
+    need = max(rg.rglru_forward_workspace_size(*s, "bf16") for s in shapes)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda", generator=gen)
+    refs = [oracle_forward(c) for c in cases]
+    for rep in range(2):
+        for c, (y_ref, h_ref), s in zip(cases, refs, shapes):
+            g = to_device(c)
+            y = torch.empty_like(g["x"])
+            hT = torch.empty((s[0], s[2]), dtype=torch.float32, device="cuda")
+            rg.rglru_forward_planned(g["x"], g["conv_w"], g["W_a"], g["b_a"], g["W_x"], g["b_x"],
+                                     g["Lam"], g["h0"], y, hT, ws, "fused", 0)
+            torch.cuda.synchronize()
+            assert err(host(y), y_ref) < TOL["bf16"], (rep, s)
+            assert err(host(hT), h_ref) < TOL["bf16"], (rep, s)
+        # the words the calls left behind become garbage of another kind for the next round
+        ws[: need // 2] = torch.randint(0, 256, (need // 2,), dtype=torch.uint8, device="cuda",
+                                        generator=gen)
+
+
 def test_workspace_too_small_is_reported():
     inp = case("bf16", 1, 64, 512, 2)
     g = to_device(inp)
