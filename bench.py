@@ -62,10 +62,10 @@ PROFILE_CMDS = {
              "python3 REPO/bench.py --no-cpu-baseline",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'fused_forward|copyBuffer' -d "
              "OUT/fetch -o fetch --output-format csv -- python3 REPO/bench.py --steps 5 "
-             "--warmup 5 --no-cpu-baseline --copy-calibration 256",
+             "--warmup 5 --no-cpu-baseline --no-decode --copy-calibration 256",
     "write": "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'fused_forward|copyBuffer' -d "
              "OUT/write -o write --output-format csv -- python3 REPO/bench.py --steps 5 "
-             "--warmup 5 --no-cpu-baseline --copy-calibration 256",
+             "--warmup 5 --no-cpu-baseline --no-decode --copy-calibration 256",
 }
 
 
@@ -139,6 +139,42 @@ def trace_summary(stats_csv, workload, bench_line_path=None):
     print(open(path).read(), end="")
 
 
+def decode_leg(torch, rg, reps=3):
+    """The batched decode step on its workload (1024 rows, D=4096, 16 heads, 256 consecutive
+    in-place steps): every step of the workload is timed, after one untimed pass."""
+    from workloads import WORKLOADS, make_inputs, to_device
+    w = WORKLOADS["decode"]
+    g = to_device(make_inputs(w, seed=0), torch.device("cuda:0"))
+    cs, h = g["conv_state"].clone(), g["h0"].clone()
+    y_t = torch.empty_like(g["x"][0])
+
+    def step(t):
+        rg.rglru_decode_step(g["x"][t], cs, h, y_t, g["conv_w"], g["W_a"], g["b_a"], g["W_x"],
+                             g["b_x"], g["Lam"])
+
+    for t in range(w.T):
+        step(t)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        for t in range(w.T):
+            step(t)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / (reps * w.T)
+    Dh = w.D // w.H
+    # per row and channel: x_t 2 B, conv_state 3 rows in and out 12 B, h in and out 8 B, y_t 2 B;
+    # per step: the gate weights 2 H Dh^2 bf16
+    nbytes = w.B * w.D * 24 + 2 * w.H * Dh * Dh * 2
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": w.name, "us_per_step": round(us, 2),
+            "rows_per_s": round(w.B / (us * 1e-6), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes": nbytes}}
+
+
 def cpu_baseline(w, inp, min_seconds=2.0):
     """The fp64 oracle, as it stands, on the host cores (OpenMP over (sequence, head)): whole
     forwards of the full workload, repeated until min_seconds of wall time have passed (a few
@@ -165,6 +201,7 @@ def main():
     # the warm-up also brings the GPU clocks up to their steady state (a few hundred ms)
     ap.add_argument("--warmup", type=int, default=3000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step leg")
     ap.add_argument("--workload", default="rg2b")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, copy a MIB-MiB device buffer three times (the "
@@ -305,6 +342,8 @@ def main():
         "wall_s_timed": round(wall, 4),
         "alg_gbs_end_to_end": round((n * 2 * eb + wbytes) / (ms * 1e-3) / 1e9, 1),
     }
+    if not args.no_decode:
+        line["decode"] = decode_leg(torch, rg)
     if args.copy_calibration:
         src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

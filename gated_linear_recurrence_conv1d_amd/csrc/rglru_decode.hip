@@ -8,31 +8,70 @@
 // Every element of conv_state, h and y_t belongs to exactly one workgroup, which reads it before
 // it writes it, so the in-place update needs no synchronisation beyond the workgroup's own.
 //
-//  * decode_mfma<DH>: bf16 I/O, DH in {32, 64, 128, 256}. A 64-row tile of one head: conv in fp32
-//    into LDS (fp32 copy for the gate math, bf16 copy as the MFMA A operand), the same MFMA gate
-//    tile as the forward, then the nonlinearity and state update straight from the accumulators.
+//  * decode_mfma<DH>: bf16 I/O, DH in {32, 64, 128, 256}. A 32-row tile of one head: conv in fp32
+//    into LDS (fp32 copy for the gate math, bf16 copy as the MFMA A operand), the gate
+//    projections on v_mfma_f32_32x32x16_bf16 with the weights streamed from L2 two k-steps
+//    ahead, then the nonlinearity and state update straight from the accumulators. Every load
+//    that can be issued early is (the states it updates, all conv-state rows of a thread), since
+//    a decode step is one pass over memory with little compute to hide latency behind.
 //  * decode_valu<T>: any Dh <= 256, fp32 or bf16, one workgroup per (row, head).
 #include "rglru_launch.h"
 #include "rglru_mfma.h"
 
 namespace rglru {
 
+// Decode tile: 32 rows of one head, 4 waves. Wave w owns channel groups (32 channels each)
+// w*kGPW .. w*kGPW+kGPW-1 for the 32 rows (waves past the last group only help with the conv).
+// Small tiles give several workgroups per CU, whose load, compute and store phases overlap.
+template <int DH> struct DecodeTile {
+  static constexpr int kRows = 32;
+  static constexpr int kGroups = DH / 32;
+  static constexpr int kGPW = kGroups >= kWaves ? kGroups / kWaves : 1;
+  static constexpr int kLda = DH + 8;  // LDS row stride in bf16 (16 B pad against conflicts)
+  static constexpr int kKS = DH / 16;  // MFMA k-steps
+  // Row of accumulator j in lane l (v_mfma_f32_32x32x16_bf16 layout).
+  __device__ static int acc_row(int j, int lane) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
+};
+
 template <int DH>
-__global__ __launch_bounds__(kThreads) void decode_mfma(
+__global__ __launch_bounds__(kThreads, 2) void decode_mfma(
     const bf16_t *__restrict__ x_t, bf16_t *__restrict__ cs, float *__restrict__ h,
     bf16_t *__restrict__ y_t, const bf16_t *__restrict__ conv_w, const bf16_t *__restrict__ W_a,
     const float *__restrict__ b_a, const bf16_t *__restrict__ W_x,
     const float *__restrict__ b_x, const float *__restrict__ Lambda, int N, int D) {
-  typedef GateTile<DH> C;
-  __shared__ __attribute__((aligned(16))) bf16_t lds_a[kTileRows * C::kLda];
-  __shared__ float lds_xc[kTileRows * DH];
+  typedef DecodeTile<DH> C;
+  constexpr int kKS = C::kKS;
+  __shared__ __attribute__((aligned(16))) bf16_t lds_a[C::kRows * C::kLda];
+  __shared__ float lds_xc[C::kRows * DH];
 
-  const int n0 = blockIdx.x * kTileRows;
+  const int n0 = blockIdx.x * C::kRows;
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int lrow = lane & 31;
+  const int khalf = (lane >> 5) * 8;
+  const int gq0 = w * C::kGPW;
+  const bool active = gq0 < C::kGroups;
+
+  // The fp32 states this wave will update are loaded first: they do not depend on the conv.
+  float hv[C::kGPW][16];
+  const size_t woff = static_cast<size_t>(g) * DH * DH;
+  if (active) {
+#pragma unroll
+    for (int gi = 0; gi < C::kGPW; ++gi)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int n = min(n0 + C::acc_row(j, lane), N - 1);  // clamped; stores masked
+        hv[gi][j] = h[static_cast<size_t>(n) * D + g * DH + (gq0 + gi) * 32 + lrow];
+      }
+  }
+
+  // Conv and conv-state shift: thread = (channel pair p, rows r0 .. r0+RPG-1); all loads are
+  // issued before any store (rows past N read row N-1 and store nothing).
   {
     constexpr int P = DH / 2;
-    constexpr int RPG = kTileRows * P / kThreads;
+    constexpr int RPG = C::kRows * P / kThreads;
     const int p = tid % P;
     const int r0 = (tid / P) * RPG;
     const int d0 = g * DH + 2 * p;
@@ -43,20 +82,29 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(
       w0[j] = bf16lo(wv);
       w1[j] = bf16hi(wv);
     }
-    for (int r = r0; r < r0 + RPG; ++r) {
+    uint32_t c0[RPG], c1[RPG], c2[RPG], xv[RPG];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const int n = min(n0 + r0 + i, N - 1);
+      const uint32_t *c = reinterpret_cast<const uint32_t *>(cs + static_cast<size_t>(n) * 3 * D + d0);
+      c0[i] = c[0];
+      c1[i] = c[D / 2];
+      c2[i] = c[D];
+      xv[i] = *reinterpret_cast<const uint32_t *>(x_t + static_cast<size_t>(n) * D + d0);
+    }
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const int r = r0 + i;
       const int n = n0 + r;
-      float y0 = 0.0f, y1 = 0.0f;
+      const float y0 = fmaf(w0[3], bf16lo(xv[i]),
+                            fmaf(w0[2], bf16lo(c2[i]), fmaf(w0[1], bf16lo(c1[i]), w0[0] * bf16lo(c0[i]))));
+      const float y1 = fmaf(w1[3], bf16hi(xv[i]),
+                            fmaf(w1[2], bf16hi(c2[i]), fmaf(w1[1], bf16hi(c1[i]), w1[0] * bf16hi(c0[i]))));
       if (n < N) {
         uint32_t *c = reinterpret_cast<uint32_t *>(cs + static_cast<size_t>(n) * 3 * D + d0);
-        const uint32_t c0 = c[0];
-        const uint32_t c1 = c[D / 2];
-        const uint32_t c2 = c[D];
-        const uint32_t xv = *reinterpret_cast<const uint32_t *>(x_t + static_cast<size_t>(n) * D + d0);
-        y0 = fmaf(w0[3], bf16lo(xv), fmaf(w0[2], bf16lo(c2), fmaf(w0[1], bf16lo(c1), w0[0] * bf16lo(c0))));
-        y1 = fmaf(w1[3], bf16hi(xv), fmaf(w1[2], bf16hi(c2), fmaf(w1[1], bf16hi(c1), w1[0] * bf16hi(c0))));
-        c[0] = c1;
-        c[D / 2] = c2;
-        c[D] = xv;
+        c[0] = c1[i];
+        c[D / 2] = c2[i];
+        c[D] = xv[i];
       }
       *reinterpret_cast<uint32_t *>(lds_a + r * C::kLda + 2 * p) = pack_bf16x2(y0, y1);
       lds_xc[r * DH + 2 * p] = y0;
@@ -64,38 +112,57 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(
     }
   }
   __syncthreads();
-
-  const int w = tid >> 6;
-  const int lane = tid & 63;
-  int gq0, rq0;
-  bool active;
-  C::assign(w, gq0, rq0, active);
   if (!active) return;
-  f32x16_t acc[C::kGPW][C::kRPW][2];
-  const size_t woff = static_cast<size_t>(g) * DH * DH;
-  gate_tile_mfma<DH>(lds_a, W_a + woff, W_x + woff, gq0, rq0, lane, acc);
+
+  f32x16_t acc[C::kGPW][2];
+#pragma unroll
+  for (int gi = 0; gi < C::kGPW; ++gi) {
+    acc[gi][0] = f32x16_t{};
+    acc[gi][1] = f32x16_t{};
+  }
+  // weights from L2, two k-steps ahead of their MFMAs
+  constexpr int kPF = 2;
+  bf16x8_t bw[kPF][C::kGPW][2];
+  auto load_w = [&](int ks, bf16x8_t (&dst)[C::kGPW][2]) {
+#pragma unroll
+    for (int gi = 0; gi < C::kGPW; ++gi) {
+      const size_t wrow = woff + static_cast<size_t>((gq0 + gi) * 32 + lrow) * DH + ks * 16 + khalf;
+      dst[gi][0] = load_bf16x8(W_a + wrow);
+      dst[gi][1] = load_bf16x8(W_x + wrow);
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kPF && i < kKS; ++i) load_w(i, bw[i]);
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    const bf16x8_t af = load_bf16x8(lds_a + lrow * C::kLda + ks * 16 + khalf);
+#pragma unroll
+    for (int gi = 0; gi < C::kGPW; ++gi) {
+      acc[gi][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bw[ks % kPF][gi][0], acc[gi][0], 0, 0, 0);
+      acc[gi][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bw[ks % kPF][gi][1], acc[gi][1], 0, 0, 0);
+    }
+    if (ks + kPF < kKS) load_w(ks + kPF, bw[ks % kPF]);
+  }
 
 #pragma unroll
   for (int gi = 0; gi < C::kGPW; ++gi) {
-    const int cl = (gq0 + gi) * 32 + (lane & 31);
+    const int cl = (gq0 + gi) * 32 + lrow;
     const int d = g * DH + cl;
     const float ba = b_a[d], bx = b_x[d];
     const float kd = decay_coeff(Lambda[d]);
 #pragma unroll
-    for (int ri = 0; ri < C::kRPW; ++ri)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int row = C::acc_row(rq0 + ri, j, lane);
-        const int n = n0 + row;
-        if (n < N) {
-          float a, u;
-          gate(acc[gi][ri][0][j] + ba, acc[gi][ri][1][j] + bx, lds_xc[row * DH + cl], kd, a, u);
-          const size_t off = static_cast<size_t>(n) * D + d;
-          const float hn = fmaf(a, h[off], u);
-          h[off] = hn;
-          y_t[off] = f32_to_bf16(hn);
-        }
+    for (int j = 0; j < 16; ++j) {
+      const int row = C::acc_row(j, lane);
+      const int n = n0 + row;
+      if (n < N) {
+        float a, u;
+        gate(acc[gi][0][j] + ba, acc[gi][1][j] + bx, lds_xc[row * DH + cl], kd, a, u);
+        const size_t off = static_cast<size_t>(n) * D + d;
+        const float hn = fmaf(a, hv[gi][j], u);
+        h[off] = hn;
+        y_t[off] = f32_to_bf16(hn);
       }
+    }
   }
 }
 
@@ -149,7 +216,7 @@ hipError_t launch_decode(const void *x_t, void *conv_state, float *h, void *y_t,
                          hipStream_t s) {
   const int Dh = D / H;
   if (io == kBF16 && (Dh == 32 || Dh == 64 || Dh == 128 || Dh == 256)) {
-    dim3 grid((N + kTileRows - 1) / kTileRows, H);
+    dim3 grid((N + 31) / 32, H);  // DecodeTile<>::kRows rows per workgroup
     const bf16_t *xx = static_cast<const bf16_t *>(x_t);
     bf16_t *cc = static_cast<bf16_t *>(conv_state);
     bf16_t *yy = static_cast<bf16_t *>(y_t);
