@@ -52,6 +52,8 @@ def _load():
         lib.rglru_oracle_preacts.restype = None
         lib.rglru_oracle_decode_step.argtypes = [i, i, i] + [dp] * 10
         lib.rglru_oracle_decode_step.restype = None
+        lib.rglru_oracle_backward.argtypes = [i, i, i, i] + [dp] * 18
+        lib.rglru_oracle_backward.restype = None
         lib.rglru_oracle_threads.argtypes = []
         lib.rglru_oracle_threads.restype = ctypes.c_int
         _lib = lib
@@ -118,3 +120,25 @@ def decode_step(x_t, conv_state, h, conv_w, W_a, b_a, W_x, b_x, Lam):
                                      _ptr(_f64(conv_w)), _ptr(W_a), _ptr(_f64(b_a)),
                                      _ptr(_f64(W_x)), _ptr(_f64(b_x)), _ptr(_f64(Lam)))
     return y, cs, hh
+
+
+def backward(x, conv_w, W_a, b_a, W_x, b_x, Lam, h0, dy, dh_T=None):
+    """Gradients of L = sum(dy * y) + sum(dh_T * h_T) through the forward, in float64:
+    dict with dx [B,T,D], dconv_w [4,D], dW_a, dW_x [H,Dh,Dh], db_a, db_x, dLam [D] and dh0 [B,D]
+    (None when h0 is None)."""
+    x = _f64(x)
+    B, T, D = x.shape
+    W_a = _f64(W_a)
+    H = W_a.shape[0]
+    Dh = D // H
+    out = {"dx": np.empty((B, T, D)), "dconv_w": np.empty((4, D)), "dW_a": np.empty((H, Dh, Dh)),
+           "db_a": np.empty(D), "dW_x": np.empty((H, Dh, Dh)), "db_x": np.empty(D),
+           "dLam": np.empty(D), "dh0": None if h0 is None else np.empty((B, D))}
+    h0a = None if h0 is None else _f64(h0)
+    dha = None if dh_T is None else _f64(dh_T)
+    _load().rglru_oracle_backward(
+        B, T, D, H, _ptr(x), _ptr(_f64(conv_w)), _ptr(W_a), _ptr(_f64(b_a)), _ptr(_f64(W_x)),
+        _ptr(_f64(b_x)), _ptr(_f64(Lam)), _ptr(h0a), _ptr(_f64(dy)), _ptr(dha),
+        _ptr(out["dx"]), _ptr(out["dconv_w"]), _ptr(out["dW_a"]), _ptr(out["db_a"]),
+        _ptr(out["dW_x"]), _ptr(out["db_x"]), _ptr(out["dLam"]), _ptr(out["dh0"]))
+    return out

@@ -189,3 +189,129 @@ void rglru_oracle_decode_step(int N, int D, int H, const double *x_t, double *co
     free(xc);
   }
 }
+
+/* Gradients of the forward above, by reverse-mode differentiation of the same definition, term by
+ * term. The loss is L = sum_{b,t,d} dy[b][t][d] * y[b][t][d] + sum_{b,d} dh_T[b][d] * h_T[b][d]
+ * (dh_T may be NULL: zero). Outputs (all fully written):
+ *   dx [B][T][D], dconv_w [4][D], dW_a, dW_x [H][Dh][Dh] (out, in), db_a, db_x, dLambda [D],
+ *   dh0 [B][D] (may be NULL: not written).
+ * For one channel, with delta_t = dL/dh_t (dy_t plus a_{t+1} delta_{t+1} carried back in time):
+ *   u = m*i*xc:      dm = delta*i*xc,  di = delta*m*xc,  dxc += delta*m*i
+ *   h = a*hprev + u: da = delta*hprev,  carried back: delta*a
+ *   m = sqrt(1-a^2), a = exp(z):  dz = da*a + dm*(-a*a/m)   (dm/dz = -a^2/m; where m == 0, that is
+ *                                 a == 1 exactly, the term takes its limit, 0)
+ *   z = -c*r*sp:     dr = -c*sp*dz,  dsp = -c*r*dz,  sp = softplus(-Lambda): dLambda += -sigmoid(-Lambda)*dsp
+ *   r = sigmoid(pa): dpa = dr*r*(1-r);  i = sigmoid(px): dpx = di*i*(1-i)
+ *   pa = b_a + W_a xc:  db_a += dpa,  dW_a[o][i] += dpa[o]*xc[i],  dxc[i] += W_a[o][i]*dpa[o]
+ *   xc[t] = sum_j w_j x[t-3+j]:  dw_j += dxc[t]*x[t-3+j],  dx[t-3+j] += w_j*dxc[t]
+ * Heads touch disjoint channels and parameters, so the loop over heads runs in parallel. */
+void rglru_oracle_backward(int B, int T, int D, int H, const double *x, const double *conv_w,
+                           const double *W_a, const double *b_a, const double *W_x,
+                           const double *b_x, const double *Lambda, const double *h0,
+                           const double *dy, const double *dh_T, double *dx, double *dconv_w,
+                           double *dW_a, double *db_a, double *dW_x, double *db_x,
+                           double *dLambda, double *dh0) {
+  int Dh = D / H;
+  const int K = RGLRU_ORACLE_W - 1;
+  memset(dx, 0, sizeof(double) * (size_t)B * T * D);
+  memset(dconv_w, 0, sizeof(double) * (size_t)RGLRU_ORACLE_W * D);
+  memset(dW_a, 0, sizeof(double) * (size_t)H * Dh * Dh);
+  memset(dW_x, 0, sizeof(double) * (size_t)H * Dh * Dh);
+  memset(db_a, 0, sizeof(double) * (size_t)D);
+  memset(db_x, 0, sizeof(double) * (size_t)D);
+  memset(dLambda, 0, sizeof(double) * (size_t)D);
+#pragma omp parallel for schedule(dynamic)
+  for (int g = 0; g < H; ++g) {
+    double *xc = (double *)malloc(sizeof(double) * (size_t)T * Dh);
+    double *pa = (double *)malloc(sizeof(double) * (size_t)T * Dh);
+    double *px = (double *)malloc(sizeof(double) * (size_t)T * Dh);
+    double *hs = (double *)malloc(sizeof(double) * (size_t)T * Dh);
+    double *dxc = (double *)malloc(sizeof(double) * (size_t)T * Dh);
+    double *dpa = (double *)malloc(sizeof(double) * (size_t)Dh);
+    double *dpx = (double *)malloc(sizeof(double) * (size_t)Dh);
+    double *delta = (double *)malloc(sizeof(double) * (size_t)Dh);
+    for (int b = 0; b < B; ++b) {
+      const double *xs = x + (size_t)b * T * D;
+      /* forward again, keeping xc, the pre-activations and the states */
+      for (int t = 0; t < T; ++t) {
+        for (int i = 0; i < Dh; ++i) xc[(size_t)t * Dh + i] = conv_at(xs, conv_w, D, t, g * Dh + i);
+        for (int o = 0; o < Dh; ++o) {
+          int d = g * Dh + o;
+          const double *wa = W_a + ((size_t)g * Dh + o) * Dh;
+          const double *wx = W_x + ((size_t)g * Dh + o) * Dh;
+          double sa = b_a[d], sx = b_x[d];
+          for (int i = 0; i < Dh; ++i) {
+            sa += wa[i] * xc[(size_t)t * Dh + i];
+            sx += wx[i] * xc[(size_t)t * Dh + i];
+          }
+          pa[(size_t)t * Dh + o] = sa;
+          px[(size_t)t * Dh + o] = sx;
+          double hprev = t > 0 ? hs[(size_t)(t - 1) * Dh + o] : (h0 ? h0[(size_t)b * D + d] : 0.0);
+          hs[(size_t)t * Dh + o] = rglru_step(hprev, xc[(size_t)t * Dh + o], sa, sx, Lambda[d]);
+        }
+      }
+      /* backward in time */
+      for (int o = 0; o < Dh; ++o) delta[o] = dh_T ? dh_T[(size_t)b * D + g * Dh + o] : 0.0;
+      for (int t = T - 1; t >= 0; --t) {
+        for (int o = 0; o < Dh; ++o) {
+          int d = g * Dh + o;
+          double dl = delta[o] + dy[((size_t)b * T + t) * D + d];
+          double r = sigmoid(pa[(size_t)t * Dh + o]);
+          double ig = sigmoid(px[(size_t)t * Dh + o]);
+          double sp = softplus(-Lambda[d]);
+          double z = -RGLRU_ORACLE_C * r * sp;
+          double a = exp(z);
+          double m = sqrt(1.0 - a * a);
+          double xcv = xc[(size_t)t * Dh + o];
+          double hprev = t > 0 ? hs[(size_t)(t - 1) * Dh + o] : (h0 ? h0[(size_t)b * D + d] : 0.0);
+          double dm = dl * ig * xcv;
+          double di = dl * m * xcv;
+          double da = dl * hprev;
+          double dz = da * a + (m > 0.0 ? dm * (-a * a / m) : 0.0);
+          double dr = -RGLRU_ORACLE_C * sp * dz;
+          double dsp = -RGLRU_ORACLE_C * r * dz;
+          dLambda[d] += -sigmoid(-Lambda[d]) * dsp;
+          dpa[o] = dr * r * (1.0 - r);
+          dpx[o] = di * ig * (1.0 - ig);
+          dxc[(size_t)t * Dh + o] = dl * m * ig;
+          delta[o] = dl * a;
+        }
+        for (int o = 0; o < Dh; ++o) {
+          int d = g * Dh + o;
+          db_a[d] += dpa[o];
+          db_x[d] += dpx[o];
+          double *gwa = dW_a + ((size_t)g * Dh + o) * Dh;
+          double *gwx = dW_x + ((size_t)g * Dh + o) * Dh;
+          const double *wa = W_a + ((size_t)g * Dh + o) * Dh;
+          const double *wx = W_x + ((size_t)g * Dh + o) * Dh;
+          for (int i = 0; i < Dh; ++i) {
+            gwa[i] += dpa[o] * xc[(size_t)t * Dh + i];
+            gwx[i] += dpx[o] * xc[(size_t)t * Dh + i];
+            dxc[(size_t)t * Dh + i] += wa[i] * dpa[o] + wx[i] * dpx[o];
+          }
+        }
+      }
+      if (dh0)
+        for (int o = 0; o < Dh; ++o) dh0[(size_t)b * D + g * Dh + o] = delta[o];
+      /* through the conv */
+      for (int t = 0; t < T; ++t)
+        for (int i = 0; i < Dh; ++i) {
+          int d = g * Dh + i;
+          for (int j = 0; j <= K; ++j) {
+            int s = t - K + j;
+            if (s < 0) continue;
+            dconv_w[(size_t)j * D + d] += dxc[(size_t)t * Dh + i] * xs[(size_t)s * D + d];
+            dx[((size_t)b * T + s) * D + d] += conv_w[(size_t)j * D + d] * dxc[(size_t)t * Dh + i];
+          }
+        }
+    }
+    free(xc);
+    free(pa);
+    free(px);
+    free(hs);
+    free(dxc);
+    free(dpa);
+    free(dpx);
+    free(delta);
+  }
+}
