@@ -56,6 +56,10 @@ _lib.rglru_scan_preacts.argtypes = [_vp] * 7 + [_i] * 5 + [_vp, _sz, _vp, _i, _i
 _lib.rglru_scan_preacts.restype = _i
 _lib.rglru_decode_step.argtypes = [_vp] * 10 + [_i] * 4 + [_vp]
 _lib.rglru_decode_step.restype = _i
+_lib.rglru_backward_workspace_size.argtypes = [_i] * 5
+_lib.rglru_backward_workspace_size.restype = _sz
+_lib.rglru_backward.argtypes = [_vp] * 19 + [_i] * 5 + [_vp, _sz, _vp]
+_lib.rglru_backward.restype = _i
 
 
 class RglruError(RuntimeError):
@@ -189,6 +193,28 @@ def rglru_decode_step(x_t, conv_state, h, y_t, conv_w, W_a, b_a, W_x, b_x, Lambd
            "rglru_decode_step")
 
 
+def rglru_backward_workspace_size(B, T, D, H, dtype) -> int:
+    return int(_lib.rglru_backward_workspace_size(B, T, D, H, _dt(dtype)))
+
+
+def rglru_backward(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, dy, dh_T, dx, dconv_w, dW_a,
+                   db_a, dW_x, db_x, dLambda, dh0, workspace, stream=None):
+    io = x.dtype
+    B, T, D = x.shape
+    H = W_a.shape[0]
+    f32 = torch.float32
+    ptrs = [_ptr(x, io, "x"), _ptr(conv_w, io, "conv_w"), _ptr(W_a, io, "W_a"),
+            _ptr(b_a, f32, "b_a"), _ptr(W_x, io, "W_x"), _ptr(b_x, f32, "b_x"),
+            _ptr(Lambda, f32, "Lambda"), _ptr(h0, f32, "h0"), _ptr(y, io, "y"),
+            _ptr(dy, io, "dy"), _ptr(dh_T, f32, "dh_T"), _ptr(dx, io, "dx"),
+            _ptr(dconv_w, f32, "dconv_w"), _ptr(dW_a, f32, "dW_a"), _ptr(db_a, f32, "db_a"),
+            _ptr(dW_x, f32, "dW_x"), _ptr(db_x, f32, "db_x"), _ptr(dLambda, f32, "dLambda"),
+            _ptr(dh0, f32, "dh0")]
+    _check(_lib.rglru_backward(*ptrs, B, T, D, H, _dt(io), _ptr(workspace, None, "workspace"),
+                               workspace.numel() * workspace.element_size(), _stream(stream)),
+           "rglru_backward")
+
+
 # ---- convenience wrappers (allocate outputs with torch, then call the entry points above) ----
 def pre_buffer(x):
     """An empty pre-activation buffer in the layout rglru_gate_preacts writes."""
@@ -221,3 +247,28 @@ def decode_step(x_t, conv_state, h, conv_w, W_a, b_a, W_x, b_x, Lambda, stream=N
     y_t = torch.empty_like(x_t)
     rglru_decode_step(x_t, conv_state, h, y_t, conv_w, W_a, b_a, W_x, b_x, Lambda, stream)
     return y_t
+
+
+def backward(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, dy, dh_T=None, want_dh0=True,
+             workspace=None, stream=None):
+    """Gradients through the forward. Returns a dict with dx (x's dtype) and fp32 dconv_w [4,D],
+    dW_a, dW_x [H,Dh,Dh], db_a, db_x, dLam [D] and dh0 [B,D] (None unless want_dh0)."""
+    B, T, D = x.shape
+    H = W_a.shape[0]
+    Dh = D // H
+    dev = x.device
+    f32 = torch.float32
+    out = {"dx": torch.empty_like(x), "dconv_w": torch.empty((4, D), dtype=f32, device=dev),
+           "dW_a": torch.empty((H, Dh, Dh), dtype=f32, device=dev),
+           "db_a": torch.empty(D, dtype=f32, device=dev),
+           "dW_x": torch.empty((H, Dh, Dh), dtype=f32, device=dev),
+           "db_x": torch.empty(D, dtype=f32, device=dev),
+           "dLam": torch.empty(D, dtype=f32, device=dev),
+           "dh0": torch.empty((B, D), dtype=f32, device=dev) if want_dh0 else None}
+    if workspace is None:
+        workspace = torch.empty(rglru_backward_workspace_size(B, T, D, H, x.dtype),
+                                dtype=torch.uint8, device=dev)
+    rglru_backward(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, dy, dh_T, out["dx"],
+                   out["dconv_w"], out["dW_a"], out["db_a"], out["dW_x"], out["db_x"],
+                   out["dLam"], out["dh0"], workspace, stream)
+    return out

@@ -305,4 +305,60 @@ rglru_status rglru_decode_step(const void *x_t, void *conv_state, float *h, void
                                          Lambda, N, D, H, io, static_cast<hipStream_t>(stream)));
 }
 
+size_t rglru_backward_workspace_size(int B, int T, int D, int H, rglru_dtype dt) {
+  if (check_shape(B, T, D, H, dt) != RGLRU_OK) return 0;
+  return rglru::backward_layout(B, T, D, H, dt == RGLRU_BF16 ? kBF16 : kF32).total;
+}
+
+rglru_status rglru_backward(const void *x, const void *conv_w, const void *W_a, const float *b_a,
+                            const void *W_x, const float *b_x, const float *Lambda,
+                            const float *h0, const void *y, const void *dy, const float *dh_T,
+                            void *dx, float *dconv_w, float *dW_a, float *db_a, float *dW_x,
+                            float *db_x, float *dLambda, float *dh0, int B, int T, int D, int H,
+                            rglru_dtype dt, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  rglru_status st = check_shape(B, T, D, H, dt);
+  if (st != RGLRU_OK) return st;
+  if (!x || !conv_w || !W_a || !b_a || !W_x || !b_x || !Lambda || !y || !dy || !dx ||
+      !dconv_w || !dW_a || !db_a || !dW_x || !db_x || !dLambda)
+    return RGLRU_ERR_INVALID_ARG;
+  const void *vec16[] = {x, conv_w, W_a, W_x, y, dy, dx};
+  for (const void *p : vec16)
+    if (!aligned(p, 16)) return RGLRU_ERR_INVALID_ARG;
+  const void *vec4[] = {b_a, b_x, Lambda, h0, dh_T, dconv_w, dW_a, db_a, dW_x, db_x, dLambda, dh0};
+  for (const void *p : vec4)
+    if (p && !aligned(p, 4)) return RGLRU_ERR_INVALID_ARG;
+  const int io = dt == RGLRU_BF16 ? kBF16 : kF32;
+  const rglru::BwdLayout L = rglru::backward_layout(B, T, D, H, io);
+  if (L.nC > 65535) return RGLRU_ERR_UNSUPPORTED;  // one grid row per chunk
+  if (!workspace || workspace_bytes < L.total) return RGLRU_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return RGLRU_ERR_INVALID_ARG;
+  // outputs must not overlap the inputs, the workspace or each other
+  const size_t io_bytes = static_cast<size_t>(B) * T * D * elem_bytes(dt);
+  const size_t wbytes = static_cast<size_t>(H) * (D / H) * (D / H) * sizeof(float);
+  const size_t dvec = static_cast<size_t>(D) * sizeof(float);
+  const size_t bd = static_cast<size_t>(B) * D * sizeof(float);
+  struct Span {
+    const void *p;
+    size_t n;
+  };
+  const Span outs[] = {{dx, io_bytes}, {dconv_w, 4 * dvec}, {dW_a, wbytes}, {db_a, dvec},
+                       {dW_x, wbytes}, {db_x, dvec},        {dLambda, dvec}, {dh0, bd}};
+  const size_t pbytes = static_cast<size_t>(D / H) * (D / H) * elem_bytes(dt) * H;
+  const Span ins[] = {{x, io_bytes},  {y, io_bytes},   {dy, io_bytes},   {conv_w, 4 * D * elem_bytes(dt)},
+                      {W_a, pbytes},  {W_x, pbytes},   {b_a, dvec},      {b_x, dvec},
+                      {Lambda, dvec}, {h0, bd},        {dh_T, bd},       {workspace, L.total}};
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+    for (size_t j = 0; j < sizeof(ins) / sizeof(ins[0]); ++j)
+      if (overlaps(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) return RGLRU_ERR_INVALID_ARG;
+    for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+      if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return RGLRU_ERR_INVALID_ARG;
+  }
+  (void)hipGetLastError();
+  return hip_status(rglru::launch_backward(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, dy, dh_T,
+                                           dx, dconv_w, dW_a, db_a, dW_x, db_x, dLambda, dh0, B,
+                                           T, D, H, io, workspace,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

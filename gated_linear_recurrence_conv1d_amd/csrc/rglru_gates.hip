@@ -16,14 +16,15 @@
 
 namespace rglru {
 
-template <int DH>
+template <int DH, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void gates_mfma(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ conv_w,
     const bf16_t *__restrict__ W_a, const float *__restrict__ b_a,
     const bf16_t *__restrict__ W_x, const float *__restrict__ b_x, uint32_t *__restrict__ pre,
     int T, int D) {
   typedef GateTile<DH> C;
-  __shared__ __attribute__((aligned(16))) bf16_t lds_a[kTileRows * C::kLda];
+  // conv output rounded to bf16; with SPLIT also its residual, in the second half
+  __shared__ __attribute__((aligned(16))) bf16_t lds_a[(SPLIT ? 2 : 1) * kTileRows * C::kLda];
 
   const int t0 = blockIdx.x * kTileRows;
   const int g = blockIdx.y;
@@ -60,7 +61,11 @@ __global__ __launch_bounds__(kThreads) void gates_mfma(
       float c0 = bf16lo(v), c1 = bf16hi(v);
       float y0 = fmaf(w0[3], c0, fmaf(w0[2], a0[2], fmaf(w0[1], a0[1], w0[0] * a0[0])));
       float y1 = fmaf(w1[3], c1, fmaf(w1[2], a1[2], fmaf(w1[1], a1[1], w1[0] * a1[0])));
-      *reinterpret_cast<uint32_t *>(lds_a + (r0 + r) * C::kLda + 2 * p) = pack_bf16x2(y0, y1);
+      const uint32_t hi = pack_bf16x2(y0, y1);
+      *reinterpret_cast<uint32_t *>(lds_a + (r0 + r) * C::kLda + 2 * p) = hi;
+      if constexpr (SPLIT)
+        *reinterpret_cast<uint32_t *>(lds_a + (kTileRows + r0 + r) * C::kLda + 2 * p) =
+            pack_bf16x2(y0 - bf16lo(hi), y1 - bf16hi(hi));
       a0[0] = a0[1]; a0[1] = a0[2]; a0[2] = c0;
       a1[0] = a1[1]; a1[1] = a1[2]; a1[2] = c1;
     }
@@ -76,7 +81,8 @@ __global__ __launch_bounds__(kThreads) void gates_mfma(
 
   f32x16_t acc[C::kGPW][C::kRPW][2];
   const size_t woff = static_cast<size_t>(g) * DH * DH;
-  gate_tile_mfma<DH>(lds_a, W_a + woff, W_x + woff, gq0, rq0, lane, acc);
+  gate_tile_mfma<DH, SPLIT>(lds_a, W_a + woff, W_x + woff, gq0, rq0, lane, acc,
+                            lds_a + kTileRows * C::kLda);
 
   // ---- epilogue: bias, fp16 pair, store.
 #pragma unroll
@@ -142,7 +148,7 @@ __global__ __launch_bounds__(256) void gates_valu(
 // ----------------------------------------------------------------------------------------------
 hipError_t launch_gates(const void *x, const void *conv_w, const void *W_a, const float *b_a,
                         const void *W_x, const float *b_x, void *pre, int B, int T, int D, int H,
-                        int io, hipStream_t s) {
+                        int io, hipStream_t s, bool split) {
   const int Dh = D / H;
   if (io == kBF16 && (Dh == 32 || Dh == 64 || Dh == 128 || Dh == 256)) {
     dim3 grid((T + kTileRows - 1) / kTileRows, H, B);
@@ -151,13 +157,21 @@ hipError_t launch_gates(const void *x, const void *conv_w, const void *W_a, cons
     const bf16_t *wa = static_cast<const bf16_t *>(W_a);
     const bf16_t *wx = static_cast<const bf16_t *>(W_x);
     uint32_t *pp = static_cast<uint32_t *>(pre);
+#define RGLRU_GATES_CASE(DHV)                                                                   \
+  case DHV:                                                                                      \
+    if (split)                                                                                   \
+      gates_mfma<DHV, true><<<grid, kThreads, 0, s>>>(xx, cw, wa, b_a, wx, b_x, pp, T, D);       \
+    else                                                                                         \
+      gates_mfma<DHV, false><<<grid, kThreads, 0, s>>>(xx, cw, wa, b_a, wx, b_x, pp, T, D);      \
+    break;
     switch (Dh) {
-      case 32: gates_mfma<32><<<grid, kThreads, 0, s>>>(xx, cw, wa, b_a, wx, b_x, pp, T, D); break;
-      case 64: gates_mfma<64><<<grid, kThreads, 0, s>>>(xx, cw, wa, b_a, wx, b_x, pp, T, D); break;
-      case 128: gates_mfma<128><<<grid, kThreads, 0, s>>>(xx, cw, wa, b_a, wx, b_x, pp, T, D); break;
-      case 256: gates_mfma<256><<<grid, kThreads, 0, s>>>(xx, cw, wa, b_a, wx, b_x, pp, T, D); break;
+      RGLRU_GATES_CASE(32)
+      RGLRU_GATES_CASE(64)
+      RGLRU_GATES_CASE(128)
+      RGLRU_GATES_CASE(256)
       default: return hipErrorInvalidValue;
     }
+#undef RGLRU_GATES_CASE
     return hipGetLastError();
   }
   dim3 grid((T + kValuRows - 1) / kValuRows, H, B);

@@ -12,10 +12,11 @@ enum IoType { kF32 = 0, kBF16 = 1 };
 // Bytes of one (pa, px) pre-activation pair in the workspace.
 inline size_t pre_pair_bytes(int io) { return io == kBF16 ? 4 : 8; }
 
-// Gate projections: conv + block-diagonal matmuls + biases -> pre[B][T][D] pairs.
+// Gate projections: conv + block-diagonal matmuls + biases -> pre[B][T][D] pairs. split (bf16
+// MFMA path only): the conv output enters the contraction as bf16 hi + lo instead of bf16.
 hipError_t launch_gates(const void *x, const void *conv_w, const void *W_a, const float *b_a,
                         const void *W_x, const float *b_x, void *pre, int B, int T, int D, int H,
-                        int io, hipStream_t s);
+                        int io, hipStream_t s, bool split = false);
 
 // Direct scan: one lane per (b, d) over all T steps.
 hipError_t launch_scan_direct(const void *x, const void *pre, const void *conv_w,
@@ -47,5 +48,24 @@ hipError_t launch_fused(const void *x, const void *conv_w, const void *W_a, cons
                         const void *W_x, const float *b_x, const float *Lambda, const float *h0,
                         void *y, float *h_T, int B, int T, int D, int H, void *ctrl_ws,
                         hipStream_t s);
+
+// Backward (gradients of every input and parameter). Time is cut into chunks of kBwdChunk steps
+// for the reverse scan. BwdLayout gives the workspace carve (byte offsets, 256-byte aligned) and
+// the row split of the dW contraction; launch_backward assumes a workspace of layout.total bytes.
+constexpr int kBwdChunk = 64;
+struct BwdLayout {
+  int nC;                     // chunks per sequence
+  int S;                      // row splits of the dW contraction
+  long long rows_per_split;   // rows of the flattened (b, t) index per split
+  bool mfma_dxc, mfma_dw;     // which contractions run on MFMA
+  size_t o_pre, o_dpre, o_dlo, o_dxc, o_sums, o_carry, o_part, o_pcw, o_pw, o_wti, total;
+};
+BwdLayout backward_layout(int B, int T, int D, int H, int io);
+hipError_t launch_backward(const void *x, const void *conv_w, const void *W_a, const float *b_a,
+                           const void *W_x, const float *b_x, const float *Lambda,
+                           const float *h0, const void *y, const void *dy, const float *dh_T,
+                           void *dx, float *dconv_w, float *dW_a, float *db_a, float *dW_x,
+                           float *db_x, float *dLambda, float *dh0, int B, int T, int D, int H,
+                           int io, void *workspace, hipStream_t s);
 
 }  // namespace rglru

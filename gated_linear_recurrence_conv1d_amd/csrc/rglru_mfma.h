@@ -55,14 +55,18 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t *p) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// acc[gi][ri][gate] += A(rows of row tile r0+ri) * W_gate(rows of group g0+gi)^T over k = 0..DH.
+// acc[gi][ri][gate] = A(rows of row tile r0+ri) * W_gate(rows of group g0+gi)^T over k = 0..DH.
 // lds_a: [64][kLda] bf16 conv output of the tile. Wa_g / Wx_g: this head's [DH][DH] weights.
-template <int DH>
+// SPLIT: lds_lo holds the bf16 residual of the conv output (xc - hi) and A = hi + lo, which makes
+// the contraction accurate to about 2^-16 of its terms instead of 2^-9 (the weights are exact).
+template <int DH, bool SPLIT = false>
 __device__ __forceinline__ void gate_tile_mfma(const bf16_t *lds_a, const bf16_t *Wa_g,
                                                const bf16_t *Wx_g, int g0, int r0, int lane,
                                                f32x16_t (&acc)[GateTile<DH>::kGPW]
-                                                              [GateTile<DH>::kRPW][2]) {
+                                                              [GateTile<DH>::kRPW][2],
+                                               const bf16_t *lds_lo = nullptr) {
   typedef GateTile<DH> C;
+  constexpr int kParts = SPLIT ? 2 : 1;
   const int lrow = lane & 31;
   const int khalf = (lane >> 5) * 8;
 #pragma unroll
@@ -74,10 +78,13 @@ __device__ __forceinline__ void gate_tile_mfma(const bf16_t *lds_a, const bf16_t
     }
 #pragma unroll 2
   for (int k0 = 0; k0 < DH; k0 += 16) {
-    bf16x8_t af[C::kRPW];
+    bf16x8_t af[kParts][C::kRPW];
 #pragma unroll
-    for (int ri = 0; ri < C::kRPW; ++ri)
-      af[ri] = load_bf16x8(lds_a + ((r0 + ri) * 32 + lrow) * C::kLda + k0 + khalf);
+    for (int ri = 0; ri < C::kRPW; ++ri) {
+      const int off = ((r0 + ri) * 32 + lrow) * C::kLda + k0 + khalf;
+      af[0][ri] = load_bf16x8(lds_a + off);
+      if constexpr (SPLIT) af[kParts - 1][ri] = load_bf16x8(lds_lo + off);
+    }
     bf16x8_t bf[C::kGPW][2];
 #pragma unroll
     for (int gi = 0; gi < C::kGPW; ++gi) {
@@ -86,14 +93,16 @@ __device__ __forceinline__ void gate_tile_mfma(const bf16_t *lds_a, const bf16_t
       bf[gi][1] = load_bf16x8(Wx_g + wrow);
     }
 #pragma unroll
-    for (int gi = 0; gi < C::kGPW; ++gi)
+    for (int p = 0; p < kParts; ++p)
 #pragma unroll
-      for (int ri = 0; ri < C::kRPW; ++ri) {
-        acc[gi][ri][0] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ri], bf[gi][0], acc[gi][ri][0], 0, 0, 0);
-        acc[gi][ri][1] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ri], bf[gi][1], acc[gi][ri][1], 0, 0, 0);
-      }
+      for (int gi = 0; gi < C::kGPW; ++gi)
+#pragma unroll
+        for (int ri = 0; ri < C::kRPW; ++ri) {
+          acc[gi][ri][0] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p][ri], bf[gi][0], acc[gi][ri][0], 0, 0, 0);
+          acc[gi][ri][1] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p][ri], bf[gi][1], acc[gi][ri][1], 0, 0, 0);
+        }
   }
 }
 

@@ -148,6 +148,44 @@ rglru_status rglru_decode_step(const void *x_t, void *conv_state, float *h, void
                                const void *W_x, const float *b_x, const float *Lambda, int N,
                                int D, int H, rglru_dtype dt, void *stream);
 
+/* Bytes of device workspace rglru_backward needs for this shape (0 when the shape is invalid).
+ * About 4 B (bf16) or 8 B (fp32) of pre-activations, the same again of gate gradients and 4 B of
+ * conv-output gradient per element of x, plus chunk summaries and partial sums. */
+size_t rglru_backward_workspace_size(int B, int T, int D, int H, rglru_dtype dt);
+
+/* Gradients of a scalar loss L through rglru_forward, given dL/dy and dL/dh_T. The forward is
+ * differentiated exactly (chain rule through the conv, the gate projections, the log-space gates
+ * and the scan); the pages print no backward -- they place the method's memory-bound cost in
+ * training (Soham De's Griffin thread, muskviewer.com, the tweet on the Pallas kernel and HBM
+ * accesses), and the forward it differentiates is the one described above. The reverse-time
+ * adjoint delta_t = dy_t + a_{t+1} delta_{t+1} is scanned in chunks of 64 steps, so the pass has
+ * parallelism over time as well as over (b, d).
+ *  x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0   the forward's inputs (h0 NULL: zeros)
+ *  y       [B][T][D] dtype            the forward's output for these inputs; h[t-1] is read from
+ *                                     it (rounded to dtype, like the stored activations of any
+ *                                     training step)
+ *  dy      [B][T][D] dtype            dL/dy
+ *  dh_T    [B][D] f32 or NULL         dL/dh_T (NULL: zeros)
+ *  dx      [B][T][D] dtype, out       dL/dx, rounded to dtype
+ *  dconv_w [4][D] f32, out            dL/dconv_w
+ *  dW_a, dW_x [H][Dh][Dh] f32, out    dL/dW ([out][in], as the weights)
+ *  db_a, db_x, dLambda [D] f32, out
+ *  dh0     [B][D] f32 or NULL, out    dL/dh0 (written when not NULL, also when h0 is NULL)
+ *  workspace / workspace_bytes        at least rglru_backward_workspace_size(); contents on entry
+ *                                     are ignored
+ * Parameter gradients are fp32 whatever dtype is: each is a sum over all B*T rows. The gate
+ * contractions run on bf16 MFMA with fp32 accumulation for bf16 with Dh in {32, 64, 128, 256}
+ * (dW on MFMA for Dh in {128, 256}), on the fp32 vector ALU otherwise. Every sum over rows is taken
+ * in a fixed order (no floating-point atomics), so results are bitwise reproducible. Outputs must
+ * not overlap the inputs, the workspace or each other (RGLRU_ERR_INVALID_ARG). */
+rglru_status rglru_backward(const void *x, const void *conv_w, const void *W_a, const float *b_a,
+                            const void *W_x, const float *b_x, const float *Lambda,
+                            const float *h0, const void *y, const void *dy, const float *dh_T,
+                            void *dx, float *dconv_w, float *dW_a, float *db_a, float *dW_x,
+                            float *db_x, float *dLambda, float *dh0, int B, int T, int D, int H,
+                            rglru_dtype dt, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

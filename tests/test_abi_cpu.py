@@ -145,3 +145,46 @@ def test_gate_and_scan_stage_checks():
     assert lib.rglru_scan_preacts(FAKE, 0x8000000000, FAKE + 0x1000, FAKE + 0x2000, None,
                                   0x7000000000, None, 2, 64, 512, 2, rg.RGLRU_BF16, None, 0,
                                   None, rg.RGLRU_PLAN_CHUNKED, 16) == rg.RGLRU_ERR_WORKSPACE
+
+
+def bwd(**kw):
+    """rglru_backward with fake, well separated device addresses (B=2, T=64, D=512, H=2)."""
+    base = 0x100000000
+    names = ["x", "conv_w", "W_a", "b_a", "W_x", "b_x", "Lam", "h0", "y", "dy", "dh_T", "dx",
+             "dconv_w", "dW_a", "db_a", "dW_x", "db_x", "dLam", "dh0"]
+    a = {n: base + k * 0x1000000 for k, n in enumerate(names)}
+    a.update(B=2, T=64, D=512, H=2, dt=rg.RGLRU_BF16, ws=base + 40 * 0x1000000, wsb=1 << 40)
+    a.update(kw)
+    return lib.rglru_backward(*[a[n] for n in names], a["B"], a["T"], a["D"], a["H"], a["dt"],
+                              a["ws"], a["wsb"], None)
+
+
+def test_backward_workspace_size():
+    B, T, D, H = 8, 2048, 2560, 10
+    n = B * T * D
+    # pre-activation pairs, gate-gradient pairs, conv-output gradients
+    assert rg.rglru_backward_workspace_size(B, T, D, H, "bf16") >= n * (4 + 4 + 4)
+    assert rg.rglru_backward_workspace_size(B, T, D, H, "f32") >= n * (8 + 8 + 4)
+    assert rg.rglru_backward_workspace_size(B, T, D, 7, "bf16") == 0
+    assert rg.rglru_backward_workspace_size(1, 1, 1024, 2, "bf16") == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), rg.RGLRU_ERR_INVALID_ARG),
+    (dict(y=None), rg.RGLRU_ERR_INVALID_ARG),
+    (dict(dy=None), rg.RGLRU_ERR_INVALID_ARG),
+    (dict(dW_x=None), rg.RGLRU_ERR_INVALID_ARG),
+    (dict(dLam=None), rg.RGLRU_ERR_INVALID_ARG),
+    (dict(T=0), rg.RGLRU_ERR_INVALID_ARG),
+    (dict(H=3), rg.RGLRU_ERR_INVALID_ARG),
+    (dict(D=1024, H=2), rg.RGLRU_ERR_UNSUPPORTED),
+    (dict(dt=9), rg.RGLRU_ERR_UNSUPPORTED),
+    (dict(dx=0x100000000 + 8), rg.RGLRU_ERR_INVALID_ARG),        # misaligned
+    (dict(dx=0x100000000 + 9 * 0x1000000), rg.RGLRU_ERR_INVALID_ARG),   # dx aliases dy
+    (dict(db_a=0x100000000 + 13 * 0x1000000 + 64), rg.RGLRU_ERR_INVALID_ARG),  # inside dW_a
+    (dict(dh0=0x100000000 + 40 * 0x1000000), rg.RGLRU_ERR_INVALID_ARG),  # in the workspace
+    (dict(ws=None), rg.RGLRU_ERR_WORKSPACE),
+    (dict(wsb=1000), rg.RGLRU_ERR_WORKSPACE),
+])
+def test_backward_argument_checks(kw, status):
+    assert bwd(**kw) == status

@@ -125,6 +125,16 @@ def make_inputs(w: Workload, seed: int = 0, *, B: Optional[int] = None, T: Optio
                 conv_state=cs, B=B, T=T, D=D, H=H, dtype=w.dtype)
 
 
+def make_cotangents(inp: dict, seed: int = 1) -> dict:
+    """Seeded output gradients for a backward check: dy ~N(0, 1) [B,T,D] rounded to the I/O
+    dtype and dh_T ~N(0, 1) [B,D] float32, drawn in that order from their own generator."""
+    rng = np.random.default_rng(seed)
+    B, T, D = inp["B"], inp["T"], inp["D"]
+    dy = round_to_dtype(rng.standard_normal((B, T, D), dtype=np.float32), inp["dtype"])
+    dh_T = rng.standard_normal((B, D), dtype=np.float32)
+    return dict(dy=dy, dh_T=dh_T)
+
+
 def to_device(inp: dict, device="cuda"):
     """torch tensors on `device` for the GPU side: I/O-dtype tensors for x, conv_w, W_a, W_x and
     conv_state (exact, since the values are already representable), float32 for the rest."""
