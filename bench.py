@@ -175,6 +175,54 @@ def decode_leg(torch, rg, reps=3):
                          "algorithmic_bytes": nbytes}}
 
 
+def backward_leg(torch, rg, w, g, y, warmup=200, reps=100):
+    """rglru_backward on the same workload, from the forward's y and seeded dy, dh_T: the whole
+    call (all its kernels) timed with events on the current stream. Algorithmic bytes: x, y and
+    dy in and dx out (I/O dtype), the parameters in, their fp32 gradients out, dh_T in, dh0
+    out."""
+    B, T, D, H = w.B, w.T, w.D, w.H
+    Dh = D // H
+    io = g["x"].dtype
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    dy = torch.randn(g["x"].shape, generator=gen, device="cuda", dtype=torch.float32).to(io)
+    dh_T = torch.randn((B, D), generator=gen, device="cuda", dtype=torch.float32)
+    ws = torch.empty(rg.rglru_backward_workspace_size(B, T, D, H, io), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        return rg.backward(g["x"], g["conv_w"], g["W_a"], g["b_a"], g["W_x"], g["b_x"], g["Lam"],
+                           g["h0"], y, dy, dh_T, workspace=ws)
+
+    out = call()
+    for _ in range(warmup):
+        rg.rglru_backward(g["x"], g["conv_w"], g["W_a"], g["b_a"], g["W_x"], g["b_x"], g["Lam"],
+                          g["h0"], y, dy, dh_T, out["dx"], out["dconv_w"], out["dW_a"],
+                          out["db_a"], out["dW_x"], out["db_x"], out["dLam"], out["dh0"], ws)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        rg.rglru_backward(g["x"], g["conv_w"], g["W_a"], g["b_a"], g["W_x"], g["b_x"], g["Lam"],
+                          g["h0"], y, dy, dh_T, out["dx"], out["dconv_w"], out["dW_a"],
+                          out["db_a"], out["dW_x"], out["db_x"], out["dLam"], out["dh0"], ws)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    n = B * T * D
+    eb = 2 if io == torch.bfloat16 else 4
+    params = 2 * H * Dh * Dh * eb + 4 * D * eb + 3 * 4 * D
+    grads = 2 * H * Dh * Dh * 4 + 4 * D * 4 + 3 * 4 * D
+    nbytes = 4 * n * eb + params + grads + 2 * 4 * B * D
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": w.name, "ms": round(ms, 4), "value": n / (ms * 1e-3),
+            "unit": "tokens·channels/s", "reps": reps, "warmup": warmup,
+            "workspace_bytes": ws.numel(),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes": nbytes,
+                         "note": "whole backward call (all kernels) against x, y, dy in + dx out"}}
+
+
 def cpu_baseline(w, inp, min_seconds=2.0):
     """The fp64 oracle, as it stands, on the host cores (OpenMP over (sequence, head)): whole
     forwards of the full workload, repeated until min_seconds of wall time have passed (a few
@@ -202,6 +250,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step leg")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--workload", default="rg2b")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, copy a MIB-MiB device buffer three times (the "
@@ -342,6 +391,8 @@ def main():
         "wall_s_timed": round(wall, 4),
         "alg_gbs_end_to_end": round((n * 2 * eb + wbytes) / (ms * 1e-3) / 1e9, 1),
     }
+    if not args.no_backward:
+        line["backward"] = backward_leg(torch, rg, w, g, ys[0])
     if not args.no_decode:
         line["decode"] = decode_leg(torch, rg)
     if args.copy_calibration:

@@ -331,6 +331,7 @@ rglru_status rglru_backward(const void *x, const void *conv_w, const void *W_a, 
   const int io = dt == RGLRU_BF16 ? kBF16 : kF32;
   const rglru::BwdLayout L = rglru::backward_layout(B, T, D, H, io);
   if (L.nC > 65535) return RGLRU_ERR_UNSUPPORTED;  // one grid row per chunk
+  if (static_cast<long long>(B) * T >= (1LL << 31)) return RGLRU_ERR_UNSUPPORTED;  // row index
   if (!workspace || workspace_bytes < L.total) return RGLRU_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return RGLRU_ERR_INVALID_ARG;
   // outputs must not overlap the inputs, the workspace or each other

@@ -25,7 +25,7 @@
 //  4. dxc_mfma / dxc_valu: dxc += [dpa dpx] [W_a ; W_x] per head (bf16 MFMA or fp32 VALU).
 //  5. conv_bwd: dx from dxc and conv_w; per-chunk partials of dconv_w.
 //  6. dw_mfma / dw_valu: per head and row split, partial dW = dp^T xc with xc recomputed from x.
-//  7. bwd_reduce: fixed-order sums of all partials (deterministic: no floating-point atomics).
+//  7. colsum: fixed-order sums of all partials (deterministic: no floating-point atomics).
 #include <algorithm>
 
 #include "rglru_launch.h"
@@ -414,161 +414,231 @@ __global__ __launch_bounds__(kBwdThreads) void conv_bwd(const T *__restrict__ x,
 }
 
 // ---- 6a: dW partials on MFMA (bf16, Dh in {128, 256}) ---------------------------------------
-// Output tile 128 (m = 2o + q) x 128 (i) of head g, contraction over the rows [kb, ke) of the
-// flattened (b, t) index; 4 waves in a 2 x 2 grid, each 64 x 64 = 2 x 2 MFMA tiles. Per step of 64
-// rows, dp and the conv output xc (recomputed from x in fp32) are written to LDS transposed, k
-// contiguous, so both MFMA operands read 16 B per lane.
+// One workgroup: a 256 (m = 2o + q, both gates interleaved) x Dh (i) tile of head g, contracted
+// over the rows [kb, ke) of the flattened (b, t) index in steps of 32 rows; 8 waves (two per
+// SIMD) in a 4 x 2 grid, each 64 x Dh/2 (2 x Dh/64 MFMA tiles, fp32 accumulators). Per step, dp
+// and the conv output xc (recomputed from x in fp32) are written to LDS transposed, k
+// contiguous, as pairs of rows: a row of 32 k plus 4 pad is 72 bytes, so the 4-byte stores of
+// one instruction (16 row pairs x 2 octets of m per half-wave) hit 32 distinct banks and the
+// 16-byte operand reads, taken as two 8-byte halves, distinct banks too. The LDS holds two
+// steps: step s+1's loads are issued before step s's MFMAs and stored into the other buffer
+// after them, one barrier per step.
 // Precision: with both operands rounded to bf16 a dW element errs by up to 2^-9 of its largest
 // terms, and the gate gradients are heavy tailed (dz carries 1/m), so single elements of dW miss
 // by a few percent of the tensor's rms. Each operand is therefore split into bf16 hi + lo and
-// the product taken as hi*hi + lo*hi + hi*lo (the lo*lo term is below 2^-16), three MFMAs per
-// tile step with fp32 accumulation.
-// pw: [S][H][2 Dh][Dh] fp32.
-constexpr int kDwRows = 64;
-constexpr int kDwLd = kDwRows + 8;  // bf16 per LDS row (16 B pad)
+// the product taken as hi*hi + lo*hi + hi*lo (the lo*lo term is below 2^-16): three MFMAs.
+// pw: [S][2 gates][H][Dh][Dh] fp32.
+constexpr int kDwRows = 32;            // rows per step
+constexpr int kDwLd = kDwRows + 4;     // LDS row stride in bf16 (72 bytes)
+constexpr int kDwM = 256;              // m per workgroup
+constexpr int kDwThreads = 512;
+
+template <int DH> struct DwTile {
+  static_assert(DH == 128 || DH == 256, "dW MFMA tile needs Dh in {128, 256}");
+  static constexpr int kMt = 2 * DH / kDwM;        // m tiles per head
+  static constexpr int kWN = DH / 64;              // 32-column MFMA tiles per wave
+  static constexpr int kAElems = 2 * kDwM * kDwLd;  // [hi, lo][m][k]
+  static constexpr int kBElems = 2 * DH * kDwLd;    // [hi, lo][i][k]
+  static constexpr int kBufElems = kAElems + kBElems;
+};
+
+__device__ __forceinline__ bf16x8_t lds_read_8x2(const bf16_t *p) {
+  const uint2 lo = *reinterpret_cast<const uint2 *>(p);
+  const uint2 hi = *reinterpret_cast<const uint2 *>(p + 4);
+  const u32x4_t v = {lo.x, lo.y, hi.x, hi.y};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
 
 template <int DH>
-__global__ __launch_bounds__(256) void dw_mfma(const bf16_t *__restrict__ x,
-                                               const uint32_t *__restrict__ dpre,
-                                               const uint32_t *__restrict__ dlo,
-                                               const bf16_t *__restrict__ conv_w,
-                                               float *__restrict__ pw, int Tn, int D, int H,
-                                               long long rows, long long rows_per_split) {
-  static_assert(DH == 128 || DH == 256, "dW MFMA tile needs Dh in {128, 256}");
-  constexpr int kMt = 2 * DH / 128;
-  __shared__ __attribute__((aligned(16))) bf16_t la[2][128 * kDwLd];  // [hi, lo][m][k]
-  __shared__ __attribute__((aligned(16))) bf16_t lb[2][128 * kDwLd];  // [hi, lo][i][k]
-  const int mt = blockIdx.x % kMt;
-  const int nt = blockIdx.x / kMt;
+__global__ __launch_bounds__(kDwThreads, 1) void dw_mfma(const bf16_t *__restrict__ x,
+                                                         const uint32_t *__restrict__ dpre,
+                                                         const uint32_t *__restrict__ dlo,
+                                                         const bf16_t *__restrict__ conv_w,
+                                                         float *__restrict__ pw, int Tn, int D,
+                                                         int H, int rows, int rows_per_split) {
+  typedef DwTile<DH> C;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * C::kBufElems];
+  const int mt = blockIdx.x;
   const int g = blockIdx.y;
   const int sp = blockIdx.z;
-  const long long kb = static_cast<long long>(sp) * rows_per_split;
-  const long long ke = min(kb + rows_per_split, rows);
+  const int kb = sp * rows_per_split;
+  const int ke = min(kb + rows_per_split, rows);
+  const int nsteps = (ke - kb + kDwRows - 1) / kDwRows;
   const int tid = threadIdx.x;
-  // loader role: 4 consecutive rows (q) x 8 consecutive columns (j)
-  const int lq = tid & 15;   // row quad 0..15
-  const int lj = tid >> 4;   // column octet 0..15
-  // A columns m = mt*128 + 8 lj .. +7, i.e. the pairs o = (mt*128 + 8 lj)/2 .. +3 of this head
-  const size_t a_col = static_cast<size_t>(g) * DH + (mt * 128 + 8 * lj) / 2;  // uint32 pairs
-  const size_t b_col = static_cast<size_t>(g) * DH + nt * 128 + 8 * lj;       // bf16 channels
-  float cw[4][8];
+  // loader roles: rows 2 lq, 2 lq + 1 of the step; A: 4 pairs (8 m) at octet lj; B: 8 channels
+  // at octet lj (only lj < DH / 8 load B)
+  const int lq = tid & 15;
+  const int lj = tid >> 4;
+  const bool bload = lj < DH / 8;
+  const size_t a_col = static_cast<size_t>(g) * DH + (mt * kDwM + 8 * lj) / 2;  // uint32 pairs
+  const int ich = 8 * (bload ? lj : 0);                                       // B channels
+  const size_t b_col = static_cast<size_t>(g) * DH + ich;
+  // conv taps of this thread's 8 channels as bf16 pairs (w0, w1) and (w2, w3): the conv output
+  // is two bf16 dot products per channel with fp32 accumulation (the products are exact)
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  constexpr uint32_t kLoPair = 0x05040100u, kHiPair = 0x07060302u;  // low / high halves
+  bf16x2_t w01[8], w23[8];
+  {
+    u32x4_t cwv[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(conv_w + static_cast<size_t>(j) * D + b_col);
+    for (int j = 0; j < 4; ++j)
+      cwv[j] = *reinterpret_cast<const u32x4_t *>(conv_w + static_cast<size_t>(j) * D + b_col);
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      cw[j][2 * h] = bf16lo(v[h]);
-      cw[j][2 * h + 1] = bf16hi(v[h]);
+      w01[2 * h] = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(cwv[1][h], cwv[0][h], kLoPair));
+      w01[2 * h + 1] = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(cwv[1][h], cwv[0][h], kHiPair));
+      w23[2 * h] = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(cwv[3][h], cwv[2][h], kLoPair));
+      w23[2 * h + 1] = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(cwv[3][h], cwv[2][h], kHiPair));
     }
   }
+  // prefetch registers: the rows of the next step
+  u32x4_t ra[2][2];  // [hi, lo][row u]
+  u32x4_t rx[5];     // x rows r0 - 3 .. r0 + 1
+  auto load_dp = [&](int st, u32x4_t (&pa)[2][2]) {
+    const int r0 = kb + st * kDwRows + 2 * lq;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int rr = r0 + u;
+      if (rr < ke) {
+        const size_t off = static_cast<size_t>(rr) * D + a_col;
+        pa[0][u] = *reinterpret_cast<const u32x4_t *>(dpre + off);
+        pa[1][u] = *reinterpret_cast<const u32x4_t *>(dlo + off);
+      } else {
+        pa[0][u] = u32x4_t{0u, 0u, 0u, 0u};
+        pa[1][u] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto load_x = [&](int st) {
+    const int r0 = kb + st * kDwRows + 2 * lq;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      const int rr = r0 - 3 + k;
+      if (bload && rr >= 0 && rr < ke)
+        rx[k] = *reinterpret_cast<const u32x4_t *>(x + static_cast<size_t>(rr) * D + b_col);
+      else
+        rx[k] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  // conv, hi/lo split and transposed stores of one step into buffer `buf`
+  auto store_step = [&](int st, int buf, const u32x4_t (&pa)[2][2]) {
+    bf16_t *A = lds + buf * C::kBufElems;
+    bf16_t *Bm = A + C::kAElems;
+    // A: m = 8 lj + cc is half cc & 1 (dpa even, dpx odd) of pair cc >> 1; rows 2 lq, 2 lq + 1
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+#pragma unroll
+      for (int part = 0; part < 2; ++part)
+        *reinterpret_cast<uint32_t *>(A + (part * kDwM + 8 * lj + cc) * kDwLd + 2 * lq) =
+            __builtin_amdgcn_perm(pa[part][1][cc >> 1], pa[part][0][cc >> 1],
+                                  (cc & 1) ? kHiPair : kLoPair);
+    if (!bload) return;
+    const int k0 = kb + st * kDwRows;
+    const int r0 = k0 + 2 * lq;
+    // Does this step hold one of the first three rows of a sequence (uniform over the
+    // workgroup)? Only then do conv taps need masking at the sequence start.
+    const int f = k0 % Tn;
+    const bool edge = f <= 2 || Tn - f <= kDwRows - 1 + 2;
+    // tap j of output row u reads loaded row u + j; at a sequence start the taps before time 0
+    // read zero instead (the rows loaded there belong to the previous sequence)
+    const int t0 = r0 % Tn;
+    float xcv[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // time of row r0 + u within its sequence (it wraps at most once: u <= 1)
+      int t = t0 + u;
+      if (t >= Tn) t -= Tn;
+      uint32_t xw[4][4];  // [tap][word]
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = !edge || t - 3 + j >= 0;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) xw[j][h] = ok ? rx[u + j][h] : 0u;
+      }
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        const uint32_t sel = (cc & 1) ? kHiPair : kLoPair;
+        const int h = cc >> 1;
+        const bf16x2_t p01 = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(xw[1][h], xw[0][h], sel));
+        const bf16x2_t p23 = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(xw[3][h], xw[2][h], sel));
+        xcv[u][cc] = __builtin_amdgcn_fdot2_f32_bf16(
+            p23, w23[cc], __builtin_amdgcn_fdot2_f32_bf16(p01, w01[cc], 0.0f, false), false);
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      const uint32_t hv = pack_bf16x2(xcv[0][cc], xcv[1][cc]);
+      const uint32_t lv = pack_bf16x2(xcv[0][cc] - bf16lo(hv), xcv[1][cc] - bf16hi(hv));
+      *reinterpret_cast<uint32_t *>(Bm + (8 * lj + cc) * kDwLd + 2 * lq) = hv;
+      *reinterpret_cast<uint32_t *>(Bm + (DH + 8 * lj + cc) * kDwLd + 2 * lq) = lv;
+    }
+  };
+
   const int w = tid >> 6;
   const int lane = tid & 63;
-  const int wm = (w & 1) * 64, wn = (w >> 1) * 64;
+  const int wm = (w & 3) * 64, wn = (w >> 2) * (DH / 2);
   const int lrow = lane & 31;
   const int khalf = (lane >> 5) * 8;
-  f32x16_t acc[2][2];
+  f32x16_t acc[2][C::kWN];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) acc[a][c] = f32x16_t{};
+    for (int c = 0; c < C::kWN; ++c) acc[a][c] = f32x16_t{};
 
-  for (long long k0 = kb; k0 < ke; k0 += kDwRows) {
-    // ---- load; conv in fp32
-    uint32_t av[2][4][4];  // [hi, lo][row u][pair h]: 4 pairs = 8 values of m
-    float xcv[4][8];       // [row u][column]
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const long long rr = k0 + 4 * lq + u;
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc) xcv[u][cc] = 0.0f;
-      if (rr < ke) {
-        const int bb = static_cast<int>(rr / Tn);
-        const int t = static_cast<int>(rr % Tn);
-        const size_t rowoff = (static_cast<size_t>(bb) * Tn + t) * D;
-        const u32x4_t vh = *reinterpret_cast<const u32x4_t *>(dpre + rowoff + a_col);
-        const u32x4_t vl = *reinterpret_cast<const u32x4_t *>(dlo + rowoff + a_col);
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          av[0][u][h] = vh[h];
-          av[1][u][h] = vl[h];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int ts = t - 3 + j;
-          if (ts >= 0) {
-            const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(
-                x + (static_cast<size_t>(bb) * Tn + ts) * D + b_col);
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              xcv[u][2 * h] = fmaf(cw[j][2 * h], bf16lo(xv[h]), xcv[u][2 * h]);
-              xcv[u][2 * h + 1] = fmaf(cw[j][2 * h + 1], bf16hi(xv[h]), xcv[u][2 * h + 1]);
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < 4; ++h) av[0][u][h] = av[1][u][h] = 0u;
-      }
-    }
-    __syncthreads();  // the previous step's MFMA reads are done
-    // ---- transpose into LDS: row m (or i), 4 consecutive k per 8-byte store
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const int h = cc >> 1;
-#pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        const uint32_t(&q)[4][4] = av[part];
-        uint32_t a01, a23;
-        if (cc & 1) {  // m odd: the dpx halves
-          a01 = (q[0][h] >> 16) | (q[1][h] & 0xffff0000u);
-          a23 = (q[2][h] >> 16) | (q[3][h] & 0xffff0000u);
-        } else {       // m even: the dpa halves
-          a01 = (q[0][h] & 0xffffu) | (q[1][h] << 16);
-          a23 = (q[2][h] & 0xffffu) | (q[3][h] << 16);
-        }
-        *reinterpret_cast<uint2 *>(&la[part][(8 * lj + cc) * kDwLd + 4 * lq]) = make_uint2(a01, a23);
-      }
-      const uint32_t h01 = pack_bf16x2(xcv[0][cc], xcv[1][cc]);
-      const uint32_t h23 = pack_bf16x2(xcv[2][cc], xcv[3][cc]);
-      const uint32_t l01 = pack_bf16x2(xcv[0][cc] - bf16lo(h01), xcv[1][cc] - bf16hi(h01));
-      const uint32_t l23 = pack_bf16x2(xcv[2][cc] - bf16lo(h23), xcv[3][cc] - bf16hi(h23));
-      *reinterpret_cast<uint2 *>(&lb[0][(8 * lj + cc) * kDwLd + 4 * lq]) = make_uint2(h01, h23);
-      *reinterpret_cast<uint2 *>(&lb[1][(8 * lj + cc) * kDwLd + 4 * lq]) = make_uint2(l01, l23);
-    }
-    __syncthreads();
-    // ---- MFMA over the 64 rows: hi*hi + lo*hi + hi*lo
+  auto mfma_step = [&](int buf) {
+    const bf16_t *A = lds + buf * C::kBufElems;
+    const bf16_t *Bm = A + C::kAElems;
 #pragma unroll
     for (int kk = 0; kk < kDwRows; kk += 16) {
-      bf16x8_t af[2][2], bfr[2][2];  // [hi, lo][tile]
+      bf16x8_t af[2][2];  // [hi, lo][m tile]
 #pragma unroll
       for (int part = 0; part < 2; ++part)
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          af[part][a] = load_bf16x8(&la[part][(wm + a * 32 + lrow) * kDwLd + kk + khalf]);
-          bfr[part][a] = load_bf16x8(&lb[part][(wn + a * 32 + lrow) * kDwLd + kk + khalf]);
-        }
-#pragma unroll
-      for (int p = 0; p < 3; ++p)
-#pragma unroll
         for (int a = 0; a < 2; ++a)
+          af[part][a] = lds_read_8x2(A + (part * kDwM + wm + a * 32 + lrow) * kDwLd + kk + khalf);
 #pragma unroll
-          for (int c = 0; c < 2; ++c)
-            acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p == 1][a], bfr[p == 2][c],
+      for (int c = 0; c < C::kWN; ++c) {
+        bf16x8_t bfr[2];  // [hi, lo] of column tile c
+#pragma unroll
+        for (int part = 0; part < 2; ++part)
+          bfr[part] = lds_read_8x2(Bm + (part * DH + wn + c * 32 + lrow) * kDwLd + kk + khalf);
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+            acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p == 1][a], bfr[p == 2],
                                                                 acc[a][c], 0, 0, 0);
+      }
     }
+  };
+  // Step st: operands in LDS buffer st & 1; step st + 1 is loaded before its MFMAs and
+  // converted into the other buffer after them.
+  load_dp(0, ra);
+  load_x(0);
+  store_step(0, 0, ra);
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    const bool more = st + 1 < nsteps;
+    if (more) {
+      load_dp(st + 1, ra);
+      load_x(st + 1);
+    }
+    mfma_step(st & 1);
+    if (more) store_step(st + 1, (st + 1) & 1, ra);
+    __syncthreads();
   }
-  // ---- partial out: pw[sp][g][m][i]
-  float *dst = pw + (static_cast<size_t>(sp) * H + g) * (2 * DH) * DH;
+  // ---- partial out: pw[sp][gate][g][o][i], m = 2 o + gate
+  const size_t gstride = static_cast<size_t>(H) * DH * DH;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int j = 0; j < 16; ++j) {
+      const int m = mt * kDwM + wm + a * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+      float *dst = pw + (static_cast<size_t>(sp) * 2 + (m & 1)) * gstride +
+                   (static_cast<size_t>(g) * DH + (m >> 1)) * DH + wn + lrow;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int m = mt * 128 + wm + a * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-        const int i = nt * 128 + wn + c * 32 + lrow;
-        dst[static_cast<size_t>(m) * DH + i] = acc[a][c][j];
-      }
+      for (int c = 0; c < C::kWN; ++c) dst[c * 32] = acc[a][c][j];
+    }
 }
 
 // ---- 6b: dW partials on the vector ALU ------------------------------------------------------
@@ -579,22 +649,22 @@ __global__ __launch_bounds__(256) void dw_valu(const T *__restrict__ x,
                                                const typename DPair<T>::type *__restrict__ dlo,
                                                const T *__restrict__ conv_w,
                                                float *__restrict__ pw, int Tn, int D, int H,
-                                               int Dh, long long rows, long long rows_per_split) {
+                                               int Dh, int rows, int rows_per_split) {
   __shared__ float sa[16][64], sb[16][64];
   const int nMt = (2 * Dh + 63) / 64;
   const int mt = blockIdx.x % nMt;
   const int nt = blockIdx.x / nMt;
   const int g = blockIdx.y;
   const int sp = blockIdx.z;
-  const long long kb = static_cast<long long>(sp) * rows_per_split;
-  const long long ke = min(kb + rows_per_split, rows);
+  const int kb = sp * rows_per_split;
+  const int ke = min(kb + rows_per_split, rows);
   const int tid = threadIdx.x;
   const int tm = (tid & 15) * 4, tn = (tid >> 4) * 4;
   float acc[4][4] = {};
-  for (long long k0 = kb; k0 < ke; k0 += 16) {
+  for (int k0 = kb; k0 < ke; k0 += 16) {
     for (int q = tid; q < 16 * 64; q += 256) {
       const int r = q / 64, col = q % 64;
-      const long long rr = k0 + r;
+      const int rr = k0 + r;
       float va = 0.0f, vb = 0.0f;
       if (rr < ke) {
         const int bb = static_cast<int>(rr / Tn);
@@ -636,67 +706,55 @@ __global__ __launch_bounds__(256) void dw_valu(const T *__restrict__ x,
     }
     __syncthreads();
   }
-  float *dst = pw + (static_cast<size_t>(sp) * H + g) * (2 * Dh) * Dh;
+  const size_t gstride = static_cast<size_t>(H) * Dh * Dh;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int m = mt * 64 + tm + u;
     if (m >= 2 * Dh) continue;
+    float *dst = pw + (static_cast<size_t>(sp) * 2 + (m & 1)) * gstride +
+                 (static_cast<size_t>(g) * Dh + (m >> 1)) * Dh;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int i = nt * 64 + tn + v;
-      if (i < Dh) dst[static_cast<size_t>(m) * Dh + i] = acc[u][v];
+      if (i < Dh) dst[i] = acc[u][v];
     }
   }
 }
 
 // ---- 7: fixed-order reduction of the partials ----------------------------------------------
-// Index ranges: [0, D) -> db_a, db_x, dLambda; [D, 5D) -> dconv_w; then 2 H Dh^2 -> dW_a, dW_x.
-__global__ __launch_bounds__(256) void bwd_reduce(const float *__restrict__ part,
-                                                  const float *__restrict__ pcw,
-                                                  const float *__restrict__ pw,
-                                                  const float *__restrict__ Lambda,
-                                                  float *__restrict__ db_a,
-                                                  float *__restrict__ db_x,
-                                                  float *__restrict__ dLambda,
-                                                  float *__restrict__ dconv_w,
-                                                  float *__restrict__ dW_a,
-                                                  float *__restrict__ dW_x, int D, int H,
-                                                  int Dh, int P, int S) {
-  const size_t idx = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-  const size_t nW = static_cast<size_t>(H) * Dh * Dh;
-  if (idx < static_cast<size_t>(D)) {
-    const size_t Pd = static_cast<size_t>(P) * D;
-    float sa = 0.0f, sx = 0.0f, sr = 0.0f;
-    for (int p = 0; p < P; ++p) {
-      sa += part[static_cast<size_t>(p) * D + idx];
-      sx += part[Pd + static_cast<size_t>(p) * D + idx];
-      sr += part[2 * Pd + static_cast<size_t>(p) * D + idx];
-    }
-    db_a[idx] = sa;
-    db_x[idx] = sx;
-    // d softplus(-L)/dL = -sigmoid(-L); dLambda = 8 sigmoid(-L) sum r dz
-    const float sig = 1.0f / (1.0f + expf(Lambda[idx]));
-    dLambda[idx] = kGateC * sig * sr;
-  } else if (idx < static_cast<size_t>(5) * D) {
-    const size_t q = idx - D;  // = j * D + d
-    const int j = static_cast<int>(q / D);
-    const int d = static_cast<int>(q % D);
-    float sacc = 0.0f;
-    for (int p = 0; p < P; ++p) sacc += pcw[(static_cast<size_t>(p) * 4 + j) * D + d];
-    dconv_w[q] = sacc;
-  } else if (idx < static_cast<size_t>(5) * D + 2 * nW) {
-    const size_t q = idx - static_cast<size_t>(5) * D;  // = gate * nW + (g Dh + o) Dh + i
-    const int gate = static_cast<int>(q / nW);
-    const size_t r = q % nW;
-    const int i = static_cast<int>(r % Dh);
-    const size_t go = r / Dh;
-    const int o = static_cast<int>(go % Dh);
-    const int g = static_cast<int>(go / Dh);
-    const size_t src = (static_cast<size_t>(g) * 2 * Dh + 2 * o + gate) * Dh + i;
-    const size_t stride = static_cast<size_t>(H) * 2 * Dh * Dh;
-    float sacc = 0.0f;
-    for (int s = 0; s < S; ++s) sacc += pw[static_cast<size_t>(s) * stride + src];
-    (gate ? dW_x : dW_a)[r] = sacc;
+// Segment y of the launch: out[j] = sum_{p < P} in[p ld + j] for j < n, as four interleaved
+// partial sums (p = q, q + 4, ...) combined ((s0 + s1) + s2) + s3 -- a fixed order, so the
+// result does not depend on scheduling. With `lambda` set, out[j] is scaled by 8 sigmoid(-L_j)
+// (dLambda from the sums of r dz).
+struct ColSum {
+  const float *in;
+  size_t ld, n;
+  int P;
+  float *out;
+  const float *lambda;
+};
+constexpr int kMaxSeg = 6;
+struct ColSums {
+  ColSum seg[kMaxSeg];
+};
+
+__global__ __launch_bounds__(256) void colsum(ColSums segs) {
+  __shared__ float red[4][64];
+  const ColSum &sg = segs.seg[blockIdx.y];
+  const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const size_t j = static_cast<size_t>(blockIdx.x) * 64 + c;
+  if (static_cast<size_t>(blockIdx.x) * 64 >= sg.n) return;  // whole block past this segment
+  float acc = 0.0f;
+  if (j < sg.n) {
+#pragma unroll 8
+    for (int p = q; p < sg.P; p += 4) acc += sg.in[static_cast<size_t>(p) * sg.ld + j];
+  }
+  red[q][c] = acc;
+  __syncthreads();
+  if (q == 0 && j < sg.n) {
+    float v = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+    if (sg.lambda) v *= kGateC / (1.0f + expf(sg.lambda[j]));
+    sg.out[j] = v;
   }
 }
 
@@ -708,14 +766,16 @@ BwdLayout backward_layout(int B, int T, int D, int H, int io) {
   const long long rows = static_cast<long long>(B) * T;
   L.mfma_dxc = io == kBF16 && (Dh == 32 || Dh == 64 || Dh == 128 || Dh == 256);
   L.mfma_dw = io == kBF16 && (Dh == 128 || Dh == 256);
-  const int tiles = L.mfma_dw ? (2 * Dh / 128) * (Dh / 128)
-                              : ((2 * Dh + 63) / 64) * ((Dh + 63) / 64);
+  // Row splits of the dW contraction. MFMA: one 256 x Dh tile per workgroup and one workgroup
+  // per CU (its LDS), so about as many workgroups as the 256 CUs of the chip, never more (a
+  // second round would double the time). Vector ALU: about 1024 workgroups of 64 x 64 tiles.
+  const long long tiles = L.mfma_dw ? static_cast<long long>(2 * Dh / kDwM) * H
+                                    : static_cast<long long>((2 * Dh + 63) / 64) * ((Dh + 63) / 64) * H;
   const int step = L.mfma_dw ? kDwRows : 16;
   const long long steps = (rows + step - 1) / step;
-  // enough row splits for about 1024 workgroups, each at least one step of rows
-  long long S = (1024 + static_cast<long long>(tiles) * H - 1) / (static_cast<long long>(tiles) * H);
+  long long S = L.mfma_dw ? kBwdCUs / tiles : (1024 + tiles - 1) / tiles;
   S = std::max<long long>(1, std::min<long long>(S, std::min<long long>(steps, 65535)));
-  L.rows_per_split = (steps + S - 1) / S * step;
+  L.rows_per_split = static_cast<int>((steps + S - 1) / S * step);
   L.S = static_cast<int>((rows + L.rows_per_split - 1) / L.rows_per_split);
   const size_t n = static_cast<size_t>(B) * T * D;
   const size_t pairb = io == kBF16 ? 4 : 8;
@@ -763,7 +823,10 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
   // pre-activations recomputed with the conv output split into bf16 hi + lo: the gradients
   // amplify pre-activation errors (through r (1 - r) and 1/m), so the backward does not reuse
   // the forward's bf16-operand rounding
-  hipError_t e = launch_gates(x, conv_w, W_a, b_a, W_x, b_x, pre, B, Tn, D, H, io, s, true);
+  const bool resident = io == kBF16 && static_cast<long long>(Tn) * D * 4 < (1LL << 31);
+  hipError_t e = resident && resident_preacts_supported(Dh)
+                     ? launch_resident_preacts(x, conv_w, W_a, b_a, W_x, b_x, pre, B, Tn, D, H, s)
+                     : launch_gates(x, conv_w, W_a, b_a, W_x, b_x, pre, B, Tn, D, H, io, s, true);
   if (e != hipSuccess) return e;
   const size_t lanes = static_cast<size_t>(B) * D;
   const dim3 lgrid(static_cast<unsigned>((lanes + kBwdThreads - 1) / kBwdThreads), L.nC);
@@ -778,7 +841,10 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
       const size_t nw = static_cast<size_t>(H) * Dh * 2 * Dh;
       wt_prep<<<static_cast<unsigned>((nw + 255) / 256), 256, 0, s>>>(W_a, W_x, wti, H, Dh);
       const dim3 grid((Tn + kTileRows - 1) / kTileRows, H, B);
-      switch (Dh) {
+      if (resident && resident_dxc_supported(Dh)) {
+        e = launch_resident_dxc(dpre, wti, dxc, B, Tn, D, H, s);
+        if (e != hipSuccess) return e;
+      } else switch (Dh) {
         case 32: dxc_mfma<32><<<grid, kThreads, 0, s>>>(dpre, wti, dxc, Tn, D); break;
         case 64: dxc_mfma<64><<<grid, kThreads, 0, s>>>(dpre, wti, dxc, Tn, D); break;
         case 128: dxc_mfma<128><<<grid, kThreads, 0, s>>>(dpre, wti, dxc, Tn, D); break;
@@ -792,16 +858,15 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
     dxc_valu<T><<<grid, 256, 0, s>>>(dpre, dlo, W_a, W_x, dxc, Tn, D, Dh);
   }
   conv_bwd<T><<<lgrid, kBwdThreads, 0, s>>>(x, dxc, conv_w, dx, pcw, B, Tn, D, L.nC);
-  const long long rows = static_cast<long long>(B) * Tn;
+  const int rows = B * Tn;  // < 2^31, checked by the caller
   if constexpr (sizeof(T) == 2) {
     if (L.mfma_dw) {
-      const dim3 grid((2 * Dh / 128) * (Dh / 128), H, L.S);
       if (Dh == 256)
-        dw_mfma<256><<<grid, 256, 0, s>>>(x, dpre, dlo, conv_w, pw, Tn, D, H, rows,
-                                          L.rows_per_split);
+        dw_mfma<256><<<dim3(DwTile<256>::kMt, H, L.S), kDwThreads, 0, s>>>(
+            x, dpre, dlo, conv_w, pw, Tn, D, H, rows, L.rows_per_split);
       else
-        dw_mfma<128><<<grid, 256, 0, s>>>(x, dpre, dlo, conv_w, pw, Tn, D, H, rows,
-                                          L.rows_per_split);
+        dw_mfma<128><<<dim3(DwTile<128>::kMt, H, L.S), kDwThreads, 0, s>>>(
+            x, dpre, dlo, conv_w, pw, Tn, D, H, rows, L.rows_per_split);
     }
   }
   if (!L.mfma_dw) {
@@ -809,9 +874,21 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
     dw_valu<T><<<grid, 256, 0, s>>>(x, dpre, dlo, conv_w, pw, Tn, D, H, Dh, rows,
                                      L.rows_per_split);
   }
-  const size_t nred = static_cast<size_t>(5) * D + 2 * static_cast<size_t>(H) * Dh * Dh;
-  bwd_reduce<<<static_cast<unsigned>((nred + 255) / 256), 256, 0, s>>>(
-      part, pcw, pw, Lambda, db_a, db_x, dLambda, dconv_w, dW_a, dW_x, D, H, Dh, B * L.nC, L.S);
+  // fixed-order sums of the partials
+  const int P = B * L.nC;
+  const size_t PD = static_cast<size_t>(P) * D;
+  const size_t nW = static_cast<size_t>(H) * Dh * Dh;
+  ColSums cs;
+  cs.seg[0] = ColSum{part, static_cast<size_t>(D), static_cast<size_t>(D), P, db_a, nullptr};
+  cs.seg[1] = ColSum{part + PD, static_cast<size_t>(D), static_cast<size_t>(D), P, db_x, nullptr};
+  cs.seg[2] = ColSum{part + 2 * PD, static_cast<size_t>(D), static_cast<size_t>(D), P, dLambda,
+                     Lambda};
+  cs.seg[3] = ColSum{pcw, 4 * static_cast<size_t>(D), 4 * static_cast<size_t>(D), P, dconv_w,
+                     nullptr};
+  cs.seg[4] = ColSum{pw, 2 * nW, nW, L.S, dW_a, nullptr};
+  cs.seg[5] = ColSum{pw + nW, 2 * nW, nW, L.S, dW_x, nullptr};
+  const size_t nmax = std::max(nW, 4 * static_cast<size_t>(D));
+  colsum<<<dim3(static_cast<unsigned>((nmax + 63) / 64), kMaxSeg), 256, 0, s>>>(cs);
   return hipGetLastError();
 }
 

@@ -49,14 +49,27 @@ hipError_t launch_fused(const void *x, const void *conv_w, const void *W_a, cons
                         void *y, float *h_T, int B, int T, int D, int H, void *ctrl_ws,
                         hipStream_t s);
 
+// The backward's weight contractions as persistent workgroups with resident weights (bf16):
+// gate pre-activations with the conv output split into bf16 hi + lo (Dh in {32, 64, 128, 256}),
+// and dxc += dp [W_a ; W_x] from the interleaved transposed weights wti (Dh in {128, 256}).
+// Both need T * D * 4 < 2^31 (32-bit buffer offsets within one sequence).
+bool resident_preacts_supported(int Dh);
+bool resident_dxc_supported(int Dh);
+hipError_t launch_resident_preacts(const void *x, const void *conv_w, const void *W_a,
+                                   const float *b_a, const void *W_x, const float *b_x,
+                                   void *pre, int B, int T, int D, int H, hipStream_t s);
+hipError_t launch_resident_dxc(const void *dp, const void *wti, float *dxc, int B, int T, int D,
+                               int H, hipStream_t s);
+
 // Backward (gradients of every input and parameter). Time is cut into chunks of kBwdChunk steps
 // for the reverse scan. BwdLayout gives the workspace carve (byte offsets, 256-byte aligned) and
 // the row split of the dW contraction; launch_backward assumes a workspace of layout.total bytes.
 constexpr int kBwdChunk = 64;
+constexpr int kBwdCUs = 256;  // CUs the dW split is sized for (MI355X)
 struct BwdLayout {
   int nC;                     // chunks per sequence
   int S;                      // row splits of the dW contraction
-  long long rows_per_split;   // rows of the flattened (b, t) index per split
+  int rows_per_split;         // rows of the flattened (b, t) index per split
   bool mfma_dxc, mfma_dw;     // which contractions run on MFMA
   size_t o_pre, o_dpre, o_dlo, o_dxc, o_sums, o_carry, o_part, o_pcw, o_pw, o_wti, total;
 };
