@@ -28,19 +28,30 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "RG-LRU fwd tokens·channels/s + % HBM peak, B=8 T=2048 D=2560 bf16"
 KERNEL_SOURCES = ["rglru_device.h", "rglru_mfma.h", "rglru_gates.hip", "rglru_scan.hip",
                   "rglru_fused.hip"]
+BACKWARD_SOURCES = ["rglru_device.h", "rglru_mfma.h", "rglru_backward.hip", "rglru_bwd_tiles.hip",
+                    "rglru_gates.hip"]
+# kernels of one rglru_backward call (name prefixes in rocprofv3 output)
+BACKWARD_KERNELS = ["tile_preacts", "gates_mfma<256, true>", "bwd_summary", "bwd_carry", "bwd_emit",
+                    "wt_prep", "tile_dxc", "dxc_mfma", "dxc_valu", "conv_bwd", "dw_mfma", "dw_valu",
+                    "colsum"]
 
 
-def kernel_source_hash() -> str:
+def is_backward_kernel(name: str) -> bool:
+    n = name.replace("void ", "").replace("rglru::", "")
+    return any(n.startswith(k) for k in BACKWARD_KERNELS)
+
+
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, "gated_linear_recurrence_conv1d_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on the
-    current kernel sources (else None)."""
+def measured_traffic(kernel: str, workload: str, key="hbm_bytes_per_launch", sources=None):
+    """HBM bytes per launch (or per call) from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -49,10 +60,10 @@ def measured_traffic(kernel: str, workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_hash") != kernel_source_hash():
+    if vals.get("source_hash") != kernel_source_hash(sources):
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
 
@@ -62,10 +73,18 @@ PROFILE_CMDS = {
              "python3 REPO/bench.py --no-cpu-baseline",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'fused_forward|copyBuffer' -d "
              "OUT/fetch -o fetch --output-format csv -- python3 REPO/bench.py --steps 5 "
-             "--warmup 5 --no-cpu-baseline --no-decode --copy-calibration 256",
+             "--warmup 5 --no-cpu-baseline --no-decode --no-backward --copy-calibration 256",
     "write": "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'fused_forward|copyBuffer' -d "
              "OUT/write -o write --output-format csv -- python3 REPO/bench.py --steps 5 "
-             "--warmup 5 --no-cpu-baseline --no-decode --copy-calibration 256",
+             "--warmup 5 --no-cpu-baseline --no-decode --no-backward --copy-calibration 256",
+    "bwd_fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "
+                 "'tile_|bwd_|wt_prep|dxc_|conv_bwd|dw_|colsum|copyBuffer' -d OUT/bfetch -o fetch "
+                 "--output-format csv -- python3 REPO/bench.py --steps 5 --warmup 5 "
+                 "--no-cpu-baseline --no-decode --bwd-warmup 2 --bwd-reps 3 --copy-calibration 256",
+    "bwd_write": "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex "
+                 "'tile_|bwd_|wt_prep|dxc_|conv_bwd|dw_|colsum|copyBuffer' -d OUT/bwrite -o write "
+                 "--output-format csv -- python3 REPO/bench.py --steps 5 --warmup 5 "
+                 "--no-cpu-baseline --no-decode --bwd-warmup 2 --bwd-reps 3 --copy-calibration 256",
 }
 
 
@@ -109,6 +128,51 @@ def traffic_summary(fetch_csv, write_csv, workload, copy_mib=256):
     print(open(path).read(), end="")
 
 
+def backward_traffic_summary(fetch_csv, write_csv, workload, copy_mib=256):
+    """HBM bytes of one rglru_backward call: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) summed
+    over the backward's kernels, per call (dispatches of each kernel / calls), each counter scaled
+    by what it reads for the device copy of copy_mib MiB in the same run."""
+    import collections
+    per_kernel = collections.defaultdict(dict)
+    factors = {}
+    calls = None
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _counter_rows(path) if r["Counter_Name"] == name]
+        copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if not copy:
+            raise SystemExit(f"{path}: no copy dispatches with {name}")
+        factors[name] = copy_mib * 1024.0 / max(copy)
+        sums, counts = collections.defaultdict(float), collections.Counter()
+        for r in rows:
+            if is_backward_kernel(r["Kernel_Name"]):
+                k = r["Kernel_Name"].replace("void ", "").split("(")[0]
+                sums[k] += float(r["Counter_Value"])
+                counts[k] += 1
+        calls = max(counts.values()) if counts else 0
+        for k in sums:
+            per_kernel[k][name] = sums[k] / calls * factors[name] * 1024.0  # bytes per call
+    total = sum(v.get("FETCH_SIZE", 0.0) + v.get("WRITE_SIZE", 0.0) for v in per_kernel.values())
+    path = os.path.join(ROOT, "profiles", f"traffic_backward_{workload}.txt")
+    with open(path, "w") as f:
+        f.write("# HBM traffic of one rglru_backward call, from rocprofv3 counters.\n")
+        f.write("# Made by (REPO = this repository, OUT = a scratch directory; run from /tmp):\n")
+        f.write(f"#   {PROFILE_CMDS['bwd_fetch']}\n#   {PROFILE_CMDS['bwd_write']}\n")
+        f.write("#   python3 REPO/bench.py --backward-traffic-summary "
+                "OUT/bfetch/fetch_counter_collection.csv OUT/bwrite/write_counter_collection.csv\n")
+        f.write("# Counters are KiB per dispatch summed over the chip, scaled by copy MiB * 1024 / the\n"
+                "# counter's reading for the device copy of that size in the same run.\n")
+        f.write(f"workload: {workload}\n")
+        f.write(f"source_hash: {kernel_source_hash(BACKWARD_SOURCES)}\n")
+        f.write(f"calls: {calls}\n")
+        for name, fac in factors.items():
+            f.write(f"{name.lower()}_calibration_factor: {fac:.4f}\n")
+        f.write(f"{'read_MB':>9} {'write_MB':>9}  kernel\n")
+        for k, v in sorted(per_kernel.items(), key=lambda kv: -sum(kv[1].values())):
+            f.write(f"{v.get('FETCH_SIZE', 0) / 1e6:9.1f} {v.get('WRITE_SIZE', 0) / 1e6:9.1f}  {k}\n")
+        f.write(f"hbm_bytes_per_call: {total:.0f}\n")
+    print(open(path).read(), end="")
+
+
 def trace_summary(stats_csv, workload, bench_line_path=None):
     """Condensed rocprofv3 --kernel-trace --stats summary (per-kernel calls and durations)."""
     import csv
@@ -130,12 +194,17 @@ def trace_summary(stats_csv, workload, bench_line_path=None):
         per_call = sum(float(r["AverageNs"]) for r in rows
                        if "fused_forward" in r["Name"] or "fused_reset" in r["Name"]) / 1e3
         f.write(f"fused_call_us (fused_forward + fused_reset, one rglru_forward): {per_call:.2f}\n")
+        bwd = sum(float(r["AverageNs"]) for r in rows if is_backward_kernel(r["Name"])) / 1e3
+        f.write(f"backward_call_us (sum of the averages of the backward's kernels, one "
+                f"rglru_backward): {bwd:.2f}\n")
         if bench_line_path:
             for line in open(bench_line_path):
                 if line.startswith('{"metric"'):
                     d = json.loads(line)
                     f.write(f"bench_ms_per_step: {d['ms_per_step']}\n")
                     f.write(f"bench_roofline_kernel_ms: {d['roofline']['kernel_ms']}\n")
+                    if "backward" in d:
+                        f.write(f"bench_backward_ms: {d['backward']['ms']}\n")
     print(open(path).read(), end="")
 
 
@@ -214,13 +283,15 @@ def backward_leg(torch, rg, w, g, y, warmup=200, reps=100):
     grads = 2 * H * Dh * Dh * 4 + 4 * D * 4 + 3 * 4 * D
     nbytes = 4 * n * eb + params + grads + 2 * 4 * B * D
     gbs = nbytes / (ms * 1e-3) / 1e9
+    traffic = measured_traffic("backward", w.name, "hbm_bytes_per_call", BACKWARD_SOURCES)
     return {"workload": w.name, "ms": round(ms, 4), "value": n / (ms * 1e-3),
             "unit": "tokens·channels/s", "reps": reps, "warmup": warmup,
             "workspace_bytes": ws.numel(),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "algorithmic_bytes": nbytes,
-                         "note": "whole backward call (all kernels) against x, y, dy in + dx out"}}
+                         "algorithmic_bytes": nbytes, "traffic": traffic,
+                         "note": "whole backward call (all kernels) against x, y, dy in + dx out; "
+                                 "traffic = measured HBM bytes of all its kernels per call"}}
 
 
 def cpu_baseline(w, inp, min_seconds=2.0):
@@ -251,6 +322,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
+    ap.add_argument("--bwd-warmup", type=int, default=200)
+    ap.add_argument("--bwd-reps", type=int, default=100)
+    ap.add_argument("--backward-traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_backward_<workload>.txt from two counter CSVs")
     ap.add_argument("--workload", default="rg2b")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, copy a MIB-MiB device buffer three times (the "
@@ -262,11 +337,13 @@ def main():
                     help="write profiles/kernel_trace_fused_<workload>.txt from a rocprofv3 "
                          "kernel_stats.csv (and optionally the bench stdout) and exit")
     args = ap.parse_args()
-    if args.traffic_summary or args.trace_summary:
+    if args.traffic_summary or args.trace_summary or args.backward_traffic_summary:
         from workloads import WORKLOADS
         wname = WORKLOADS[args.workload].name
         if args.traffic_summary:
             traffic_summary(*args.traffic_summary, wname)
+        if args.backward_traffic_summary:
+            backward_traffic_summary(*args.backward_traffic_summary, wname)
         if args.trace_summary:
             trace_summary(args.trace_summary[0], wname,
                           args.trace_summary[1] if len(args.trace_summary) > 1 else None)
@@ -392,7 +469,7 @@ def main():
         "alg_gbs_end_to_end": round((n * 2 * eb + wbytes) / (ms * 1e-3) / 1e9, 1),
     }
     if not args.no_backward:
-        line["backward"] = backward_leg(torch, rg, w, g, ys[0])
+        line["backward"] = backward_leg(torch, rg, w, g, ys[0], args.bwd_warmup, args.bwd_reps)
     if not args.no_decode:
         line["decode"] = decode_leg(torch, rg)
     if args.copy_calibration:

@@ -45,6 +45,14 @@ template <> struct DPair<float> {
   __device__ __forceinline__ static void put(type *hi, type *, size_t o, float a, float x) {
     hi[o] = make_float2(a, x);
   }
+  template <int CH>
+  __device__ __forceinline__ static void put(type *hi, type *lo, size_t o, const float (&a)[CH],
+                                             const float (&x)[CH]) {
+    if constexpr (CH == 2)
+      *reinterpret_cast<float4 *>(hi + o) = make_float4(a[0], x[0], a[1], x[1]);
+    else
+      put(hi, lo, o, a[0], x[0]);
+  }
   __device__ __forceinline__ static void get(const type *hi, const type *, size_t o, float &a,
                                              float &x) {
     const float2 v = hi[o];
@@ -59,6 +67,19 @@ template <> struct DPair<bf16_t> {
     hi[o] = h;
     lo[o] = pack_bf16x2(a - bf16lo(h), x - bf16hi(h));  // the differences are exact in fp32
   }
+  template <int CH>
+  __device__ __forceinline__ static void put(type *hi, type *lo, size_t o, const float (&a)[CH],
+                                             const float (&x)[CH]) {
+    if constexpr (CH == 2) {
+      const uint32_t h0 = pack_bf16x2(a[0], x[0]), h1 = pack_bf16x2(a[1], x[1]);
+      *reinterpret_cast<uint2 *>(hi + o) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2 *>(lo + o) =
+          make_uint2(pack_bf16x2(a[0] - bf16lo(h0), x[0] - bf16hi(h0)),
+                     pack_bf16x2(a[1] - bf16lo(h1), x[1] - bf16hi(h1)));
+    } else {
+      put(hi, lo, o, a[0], x[0]);
+    }
+  }
   __device__ __forceinline__ static void get(const type *hi, const type *lo, size_t o, float &a,
                                              float &x) {
     const uint32_t h = hi[o], l = lo[o];
@@ -72,41 +93,101 @@ __device__ __forceinline__ float decay_of(float pa, float kd) {
   return 1.0f + expm1_nonpos(kd * fast_sigmoid(pa));
 }
 
+// The lane kernels below (chunk maps, gradients, conv backward) give each lane CH = 1 or 2
+// adjacent channels of one sequence, so that with CH = 2 every access moves twice the bytes per
+// instruction. Loads and stores of CH consecutive elements of one row:
+template <typename T, int CH> struct Lanes;
+template <> struct Lanes<bf16_t, 1> {
+  __device__ __forceinline__ static void load(const bf16_t *p, size_t i, float (&v)[1]) {
+    v[0] = bf16_to_f32(p[i]);
+  }
+  __device__ __forceinline__ static void store(bf16_t *p, size_t i, const float (&v)[1]) {
+    p[i] = f32_to_bf16(v[0]);
+  }
+};
+template <> struct Lanes<bf16_t, 2> {
+  __device__ __forceinline__ static void load(const bf16_t *p, size_t i, float (&v)[2]) {
+    const uint32_t u = *reinterpret_cast<const uint32_t *>(p + i);
+    v[0] = bf16lo(u);
+    v[1] = bf16hi(u);
+  }
+  __device__ __forceinline__ static void store(bf16_t *p, size_t i, const float (&v)[2]) {
+    *reinterpret_cast<uint32_t *>(p + i) = pack_bf16x2(v[0], v[1]);
+  }
+};
+template <> struct Lanes<float, 1> {
+  __device__ __forceinline__ static void load(const float *p, size_t i, float (&v)[1]) { v[0] = p[i]; }
+  __device__ __forceinline__ static void store(float *p, size_t i, const float (&v)[1]) { p[i] = v[0]; }
+};
+template <> struct Lanes<float, 2> {
+  __device__ __forceinline__ static void load(const float *p, size_t i, float (&v)[2]) {
+    const float2 u = *reinterpret_cast<const float2 *>(p + i);
+    v[0] = u.x;
+    v[1] = u.y;
+  }
+  __device__ __forceinline__ static void store(float *p, size_t i, const float (&v)[2]) {
+    *reinterpret_cast<float2 *>(p + i) = make_float2(v[0], v[1]);
+  }
+};
+// CH pre-activation pairs in their storage layout (PrePair) as one access.
+template <typename T, int CH> struct PreLanes {
+  typedef typename PrePair<T>::type P;
+  struct alignas(sizeof(P) * CH) type {
+    P v[CH];
+  };
+  __device__ __forceinline__ static type load(const P *p, size_t i) {
+    return *reinterpret_cast<const type *>(p + i);
+  }
+};
+
 // ---- pass 1: chunk maps --------------------------------------------------------------------
-template <typename T>
+template <typename T, int CH>
 __global__ __launch_bounds__(kBwdThreads) void bwd_summary(
     const typename PrePair<T>::type *__restrict__ pre, const T *__restrict__ dy,
     const float *__restrict__ Lambda, float2 *__restrict__ sums, int B, int Tn, int D, int nC) {
+  const int DL = D / CH;  // lanes per sequence
   const size_t idx = static_cast<size_t>(blockIdx.x) * kBwdThreads + threadIdx.x;
-  if (idx >= static_cast<size_t>(B) * D) return;
-  const int b = static_cast<int>(idx / D);
-  const int d = static_cast<int>(idx % D);
+  if (idx >= static_cast<size_t>(B) * DL) return;
+  const int b = static_cast<int>(idx / DL);
+  const int d0 = static_cast<int>(idx % DL) * CH;
   const int c = blockIdx.y;
   const int s = c * kBwdChunk;
   const int e = min(s + kBwdChunk, Tn);
-  const float kd = decay_coeff(Lambda[d]);
-  const size_t base = static_cast<size_t>(b) * Tn * D + d;
-  float P = 1.0f, g = 0.0f;
+  float kd[CH], P[CH], g[CH];
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    kd[k] = decay_coeff(Lambda[d0 + k]);
+    P[k] = 1.0f;
+    g[k] = 0.0f;
+  }
+  const size_t base = static_cast<size_t>(b) * Tn * D + d0;
   for (int t0 = e - 1; t0 >= s; t0 -= 8) {
-    float pa[8], dv[8];
+    typename PreLanes<T, CH>::type pp[8];
+    float dv[8][CH];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int t = t0 - u;
       if (t >= s) {
-        pa[u] = PrePair<T>::pa(pre[base + static_cast<size_t>(t) * D]);
-        dv[u] = Elem<T>::load(dy, base + static_cast<size_t>(t) * D);
+        const size_t o = base + static_cast<size_t>(t) * D;
+        pp[u] = PreLanes<T, CH>::load(pre, o);
+        Lanes<T, CH>::load(dy, o, dv[u]);
       }
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (t0 - u >= s) {
-        const float a = decay_of(pa[u], kd);
-        g = a * (dv[u] + g);
-        P *= a;
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+          const float a = decay_of(PrePair<T>::pa(pp[u].v[k]), kd[k]);
+          g[k] = a * (dv[u][k] + g[k]);
+          P[k] *= a;
+        }
       }
     }
   }
-  sums[(static_cast<size_t>(b) * nC + c) * D + d] = make_float2(P, g);
+#pragma unroll
+  for (int k = 0; k < CH; ++k)
+    sums[(static_cast<size_t>(b) * nC + c) * D + d0 + k] = make_float2(P[k], g[k]);
 }
 
 // ---- pass 2: carries across chunks, right to left ------------------------------------------
@@ -139,7 +220,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_carry(const float2 *__restric
 
 // ---- pass 3: per-element gradients ----------------------------------------------------------
 // part: [3][B * nC][D] partial sums of dpa, dpx and r dz over each chunk.
-template <typename T>
+template <typename T, int CH>
 __global__ __launch_bounds__(kBwdThreads) void bwd_emit(
     const T *__restrict__ x, const typename PrePair<T>::type *__restrict__ pre,
     const T *__restrict__ y, const T *__restrict__ dy, const float *__restrict__ h0,
@@ -147,78 +228,124 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_emit(
     const float *__restrict__ carry, typename DPair<T>::type *__restrict__ dpre,
     typename DPair<T>::type *__restrict__ dlo, float *__restrict__ dxc, float *__restrict__ part,
     int B, int Tn, int D, int nC) {
+  const int DL = D / CH;
   const size_t idx = static_cast<size_t>(blockIdx.x) * kBwdThreads + threadIdx.x;
-  if (idx >= static_cast<size_t>(B) * D) return;
-  const int b = static_cast<int>(idx / D);
-  const int d = static_cast<int>(idx % D);
+  if (idx >= static_cast<size_t>(B) * DL) return;
+  const int b = static_cast<int>(idx / DL);
+  const int d0 = static_cast<int>(idx % DL) * CH;
   const int c = blockIdx.y;
   const int s = c * kBwdChunk;
   const int e = min(s + kBwdChunk, Tn);
-  float w[4];
+  float w[4][CH];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) w[j] = Elem<T>::load(conv_w, static_cast<size_t>(j) * D + d);
-  const float kd = decay_coeff(Lambda[d]);
-  const size_t base = static_cast<size_t>(b) * Tn * D + d;
-  const float hinit = h0 ? h0[idx] : 0.0f;
+  for (int j = 0; j < 4; ++j) Lanes<T, CH>::load(conv_w, static_cast<size_t>(j) * D + d0, w[j]);
+  float kd[CH], hinit[CH], g[CH], s_pa[CH], s_px[CH], s_rdz[CH];
+  const size_t cidx = (static_cast<size_t>(b) * nC + c) * D + d0;
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    kd[k] = decay_coeff(Lambda[d0 + k]);
+    hinit[k] = h0 ? h0[static_cast<size_t>(b) * D + d0 + k] : 0.0f;
+    g[k] = carry[cidx + k];
+    s_pa[k] = s_px[k] = s_rdz[k] = 0.0f;
+  }
+  const size_t base = static_cast<size_t>(b) * Tn * D + d0;
   // xw[j] = x[t - 3 + j] for the current t (zero before the sequence start)
-  float xw[4];
+  float xw[4][CH];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int q = e - 1 - 3 + j;
-    xw[j] = q >= 0 ? Elem<T>::load(x, base + static_cast<size_t>(q) * D) : 0.0f;
+    if (q >= 0) {
+      Lanes<T, CH>::load(x, base + static_cast<size_t>(q) * D, xw[j]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < CH; ++k) xw[j][k] = 0.0f;
+    }
   }
-  float g = carry[(static_cast<size_t>(b) * nC + c) * D + d];
-  float s_pa = 0.0f, s_px = 0.0f, s_rdz = 0.0f;
-  for (int t0 = e - 1; t0 >= s; t0 -= 8) {
-    typename PrePair<T>::type pp[8];
-    float dv[8], hp[8], xn[8];
+  // Groups of kG steps, double buffered: the loads of group i+1 are issued before group i's
+  // arithmetic and stores, so that waiting for them never waits behind this group's stores
+  // (loads and stores retire in issue order).
+  constexpr int kG = 4;
+  struct Group {
+    typename PreLanes<T, CH>::type pp[kG];
+    float dv[kG][CH], hp[kG][CH], xn[kG][CH];
+  };
+  auto load_group = [&](Group &G, int t0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kG; ++u) {
       const int t = t0 - u;
       if (t >= s) {
         const size_t o = base + static_cast<size_t>(t) * D;
-        pp[u] = pre[o];
-        dv[u] = Elem<T>::load(dy, o);
-        hp[u] = t > 0 ? Elem<T>::load(y, o - D) : hinit;
-        xn[u] = t >= 4 ? Elem<T>::load(x, o - 4 * static_cast<size_t>(D)) : 0.0f;
+        G.pp[u] = PreLanes<T, CH>::load(pre, o);
+        Lanes<T, CH>::load(dy, o, G.dv[u]);
+        if (t > 0) {
+          Lanes<T, CH>::load(y, o - D, G.hp[u]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < CH; ++k) G.hp[u][k] = hinit[k];
+        }
+        if (t >= 4) {
+          Lanes<T, CH>::load(x, o - 4 * static_cast<size_t>(D), G.xn[u]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < CH; ++k) G.xn[u][k] = 0.0f;
+        }
       }
     }
+  };
+  auto run_group = [&](const Group &G, int t0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kG; ++u) {
       const int t = t0 - u;
       if (t >= s) {
-        const float xc = fmaf(w[3], xw[3], fmaf(w[2], xw[2], fmaf(w[1], xw[1], w[0] * xw[0])));
-        const float r = fast_sigmoid(PrePair<T>::pa(pp[u]));
-        const float ig = fast_sigmoid(PrePair<T>::px(pp[u]));
-        const float em = expm1_nonpos(kd * r);
-        const float a = 1.0f + em;
-        const float m = __builtin_amdgcn_sqrtf(-em * (2.0f + em));
-        const float delta = dv[u] + g;
-        const float dm = delta * ig * xc;
-        const float di = delta * m * xc;
-        float dz = delta * hp[u] * a;
-        if (m > 0.0f) dz -= dm * (a * a / m);
-        const float dpa = kd * dz * (r * (1.0f - r));
-        const float dpx = di * (ig * (1.0f - ig));
+        float dpa[CH], dpx[CH], dd[CH];
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+          const float xc =
+              fmaf(w[3][k], xw[3][k], fmaf(w[2][k], xw[2][k], fmaf(w[1][k], xw[1][k], w[0][k] * xw[0][k])));
+          const float r = fast_sigmoid(PrePair<T>::pa(G.pp[u].v[k]));
+          const float ig = fast_sigmoid(PrePair<T>::px(G.pp[u].v[k]));
+          const float em = expm1_nonpos(kd[k] * r);
+          const float a = 1.0f + em;
+          const float m = __builtin_amdgcn_sqrtf(-em * (2.0f + em));
+          const float delta = G.dv[u][k] + g[k];
+          const float dm = delta * ig * xc;
+          const float di = delta * m * xc;
+          float dz = delta * G.hp[u][k] * a;
+          if (m > 0.0f) dz -= dm * (a * a) * __builtin_amdgcn_rcpf(m);
+          dpa[k] = kd[k] * dz * (r * (1.0f - r));
+          dpx[k] = di * (ig * (1.0f - ig));
+          dd[k] = delta * m * ig;
+          s_pa[k] += dpa[k];
+          s_px[k] += dpx[k];
+          s_rdz[k] = fmaf(r, dz, s_rdz[k]);
+          g[k] = a * delta;
+          xw[3][k] = xw[2][k];
+          xw[2][k] = xw[1][k];
+          xw[1][k] = xw[0][k];
+          xw[0][k] = G.xn[u][k];
+        }
         const size_t o = base + static_cast<size_t>(t) * D;
-        DPair<T>::put(dpre, dlo, o, dpa, dpx);
-        dxc[o] = delta * m * ig;
-        s_pa += dpa;
-        s_px += dpx;
-        s_rdz = fmaf(r, dz, s_rdz);
-        g = a * delta;
-        xw[3] = xw[2];
-        xw[2] = xw[1];
-        xw[1] = xw[0];
-        xw[0] = xn[u];
+        DPair<T>::template put<CH>(dpre, dlo, o, dpa, dpx);
+        Lanes<float, CH>::store(dxc, o, dd);
       }
     }
+  };
+  Group ga, gb;
+  load_group(ga, e - 1);
+  for (int t0 = e - 1; t0 >= s; t0 -= 2 * kG) {
+    if (t0 - kG >= s) load_group(gb, t0 - kG);
+    run_group(ga, t0);
+    if (t0 - kG < s) break;
+    if (t0 - 2 * kG >= s) load_group(ga, t0 - 2 * kG);
+    run_group(gb, t0 - kG);
   }
   const size_t P = static_cast<size_t>(B) * nC * D;
-  const size_t pidx = (static_cast<size_t>(b) * nC + c) * D + d;
-  part[pidx] = s_pa;
-  part[P + pidx] = s_px;
-  part[2 * P + pidx] = s_rdz;
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    part[cidx + k] = s_pa[k];
+    part[P + cidx + k] = s_px[k];
+    part[2 * P + cidx + k] = s_rdz[k];
+  }
 }
 
 // ---- 4a: dxc += [dpa dpx] [W_a ; W_x] on MFMA (bf16, Dh in {32, 64, 128, 256}) -------------
@@ -349,68 +476,106 @@ __global__ __launch_bounds__(256) void dxc_valu(const typename DPair<T>::type *_
 
 // ---- 5: conv backward -----------------------------------------------------------------------
 // pcw: [B * nC][4][D] partial sums of dconv_w over each chunk.
-template <typename T>
+template <typename T, int CH>
 __global__ __launch_bounds__(kBwdThreads) void conv_bwd(const T *__restrict__ x,
                                                         const float *__restrict__ dxc,
                                                         const T *__restrict__ conv_w,
                                                         T *__restrict__ dx,
                                                         float *__restrict__ pcw, int B, int Tn,
                                                         int D, int nC) {
+  const int DL = D / CH;
   const size_t idx = static_cast<size_t>(blockIdx.x) * kBwdThreads + threadIdx.x;
-  if (idx >= static_cast<size_t>(B) * D) return;
-  const int b = static_cast<int>(idx / D);
-  const int d = static_cast<int>(idx % D);
+  if (idx >= static_cast<size_t>(B) * DL) return;
+  const int b = static_cast<int>(idx / DL);
+  const int d0 = static_cast<int>(idx % DL) * CH;
   const int c = blockIdx.y;
   const int s = c * kBwdChunk;
   const int e = min(s + kBwdChunk, Tn);
-  float w[4];
+  float w[4][CH];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) w[j] = Elem<T>::load(conv_w, static_cast<size_t>(j) * D + d);
-  const size_t base = static_cast<size_t>(b) * Tn * D + d;
+  for (int j = 0; j < 4; ++j) Lanes<T, CH>::load(conv_w, static_cast<size_t>(j) * D + d0, w[j]);
+  const size_t base = static_cast<size_t>(b) * Tn * D + d0;
   // gw[k] = dxc[t + k] (zero at or past T); xw[j] = x[t - 3 + j] (zero before 0)
-  float gw[4], xw[4];
+  float gw[4][CH], xw[4][CH];
 #pragma unroll
-  for (int k = 0; k < 3; ++k)
-    gw[k + 1] = s + k < Tn ? dxc[base + static_cast<size_t>(s + k) * D] : 0.0f;
+  for (int k = 0; k < 3; ++k) {
+    if (s + k < Tn) {
+      Lanes<float, CH>::load(dxc, base + static_cast<size_t>(s + k) * D, gw[k + 1]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < CH; ++q) gw[k + 1][q] = 0.0f;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     const int q = s - 3 + j;
-    xw[j + 1] = q >= 0 ? Elem<T>::load(x, base + static_cast<size_t>(q) * D) : 0.0f;
+    if (q >= 0) {
+      Lanes<T, CH>::load(x, base + static_cast<size_t>(q) * D, xw[j + 1]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < CH; ++k) xw[j + 1][k] = 0.0f;
+    }
   }
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int t0 = s; t0 < e; t0 += 8) {
-    float gn[8], xn[8];
+  float acc[4][CH] = {};
+  // groups of kG steps, double buffered (loads of group i+1 ahead of group i's stores)
+  constexpr int kG = 4;
+  struct Group {
+    float gn[kG][CH], xn[kG][CH];
+  };
+  auto load_group = [&](Group &G, int t0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kG; ++u) {
       const int t = t0 + u;
       if (t < e) {
-        gn[u] = t + 3 < Tn ? dxc[base + static_cast<size_t>(t + 3) * D] : 0.0f;
-        xn[u] = Elem<T>::load(x, base + static_cast<size_t>(t) * D);
+        if (t + 3 < Tn) {
+          Lanes<float, CH>::load(dxc, base + static_cast<size_t>(t + 3) * D, G.gn[u]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < CH; ++k) G.gn[u][k] = 0.0f;
+        }
+        Lanes<T, CH>::load(x, base + static_cast<size_t>(t) * D, G.xn[u]);
       }
     }
+  };
+  auto run_group = [&](const Group &G, int t0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kG; ++u) {
       const int t = t0 + u;
       if (t < e) {
-        gw[0] = gw[1];
-        gw[1] = gw[2];
-        gw[2] = gw[3];
-        gw[3] = gn[u];
-        xw[0] = xw[1];
-        xw[1] = xw[2];
-        xw[2] = xw[3];
-        xw[3] = xn[u];
-        // dx[t] = sum_j w[j] dxc[t + 3 - j]
-        const float v = fmaf(w[0], gw[3], fmaf(w[1], gw[2], fmaf(w[2], gw[1], w[3] * gw[0])));
-        Elem<T>::store(dx, base + static_cast<size_t>(t) * D, v);
+        float v[CH];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = fmaf(gw[0], xw[j], acc[j]);
+        for (int k = 0; k < CH; ++k) {
+          gw[0][k] = gw[1][k];
+          gw[1][k] = gw[2][k];
+          gw[2][k] = gw[3][k];
+          gw[3][k] = G.gn[u][k];
+          xw[0][k] = xw[1][k];
+          xw[1][k] = xw[2][k];
+          xw[2][k] = xw[3][k];
+          xw[3][k] = G.xn[u][k];
+          // dx[t] = sum_j w[j] dxc[t + 3 - j]
+          v[k] = fmaf(w[0][k], gw[3][k], fmaf(w[1][k], gw[2][k], fmaf(w[2][k], gw[1][k], w[3][k] * gw[0][k])));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j][k] = fmaf(gw[0][k], xw[j][k], acc[j][k]);
+        }
+        Lanes<T, CH>::store(dx, base + static_cast<size_t>(t) * D, v);
       }
     }
+  };
+  Group ga, gb;
+  load_group(ga, s);
+  for (int t0 = s; t0 < e; t0 += 2 * kG) {
+    if (t0 + kG < e) load_group(gb, t0 + kG);
+    run_group(ga, t0);
+    if (t0 + kG >= e) break;
+    if (t0 + 2 * kG < e) load_group(ga, t0 + 2 * kG);
+    run_group(gb, t0 + kG);
   }
   const size_t prow = (static_cast<size_t>(b) * nC + c) * 4;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) pcw[(prow + j) * D + d] = acc[j];
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int k = 0; k < CH; ++k) pcw[(prow + j) * D + d0 + k] = acc[j][k];
 }
 
 // ---- 6a: dW partials on MFMA (bf16, Dh in {128, 256}) ---------------------------------------
@@ -722,14 +887,15 @@ __global__ __launch_bounds__(256) void dw_valu(const T *__restrict__ x,
 }
 
 // ---- 7: fixed-order reduction of the partials ----------------------------------------------
-// Segment y of the launch: out[j] = sum_{p < P} in[p ld + j] for j < n, as four interleaved
-// partial sums (p = q, q + 4, ...) combined ((s0 + s1) + s2) + s3 -- a fixed order, so the
-// result does not depend on scheduling. With `lambda` set, out[j] is scaled by 8 sigmoid(-L_j)
-// (dLambda from the sums of r dz).
+// Segment y of the launch: out[j] = sum_{p < P} in[p ld + j] for j < n. A 256-thread block
+// covers C = 256 / G columns with G interleaved partial sums each (p = q, q + G, ...), combined
+// pairwise in a fixed tree -- a fixed order, so the result does not depend on scheduling. G is
+// 16 for segments with many partials (the per-chunk vectors), 4 otherwise. With `lambda` set,
+// out[j] is scaled by 8 sigmoid(-L_j) (dLambda from the sums of r dz).
 struct ColSum {
   const float *in;
   size_t ld, n;
-  int P;
+  int P, G;
   float *out;
   const float *lambda;
 };
@@ -739,20 +905,25 @@ struct ColSums {
 };
 
 __global__ __launch_bounds__(256) void colsum(ColSums segs) {
-  __shared__ float red[4][64];
+  __shared__ float red[256];
   const ColSum &sg = segs.seg[blockIdx.y];
-  const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
-  const size_t j = static_cast<size_t>(blockIdx.x) * 64 + c;
-  if (static_cast<size_t>(blockIdx.x) * 64 >= sg.n) return;  // whole block past this segment
+  const int G = sg.G, C = 256 / G;
+  const int c = threadIdx.x % C, q = threadIdx.x / C;
+  const size_t j = static_cast<size_t>(blockIdx.x) * C + c;
+  if (static_cast<size_t>(blockIdx.x) * C >= sg.n) return;  // whole block past this segment
   float acc = 0.0f;
   if (j < sg.n) {
-#pragma unroll 8
-    for (int p = q; p < sg.P; p += 4) acc += sg.in[static_cast<size_t>(p) * sg.ld + j];
+#pragma unroll 4
+    for (int p = q; p < sg.P; p += G) acc += sg.in[static_cast<size_t>(p) * sg.ld + j];
   }
-  red[q][c] = acc;
+  red[threadIdx.x] = acc;
   __syncthreads();
+  for (int h = G / 2; h > 0; h >>= 1) {  // fixed pairwise tree over the G partial sums
+    if (q < h) red[threadIdx.x] += red[threadIdx.x + h * C];
+    __syncthreads();
+  }
   if (q == 0 && j < sg.n) {
-    float v = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+    float v = red[c];
     if (sg.lambda) v *= kGateC / (1.0f + expf(sg.lambda[j]));
     sg.out[j] = v;
   }
@@ -829,12 +1000,23 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
                      : launch_gates(x, conv_w, W_a, b_a, W_x, b_x, pre, B, Tn, D, H, io, s, true);
   if (e != hipSuccess) return e;
   const size_t lanes = static_cast<size_t>(B) * D;
-  const dim3 lgrid(static_cast<unsigned>((lanes + kBwdThreads - 1) / kBwdThreads), L.nC);
   const unsigned lblocks = static_cast<unsigned>((lanes + kBwdThreads - 1) / kBwdThreads);
-  bwd_summary<T><<<lgrid, kBwdThreads, 0, s>>>(pre, dy, Lambda, sums, B, Tn, D, L.nC);
+  // lane kernels: two adjacent channels per lane when D is even
+  const bool pair = D % 2 == 0;
+  const dim3 lgrid(pair ? (lblocks + 1) / 2 : lblocks, L.nC);
+  if (pair) {
+    bwd_summary<T, 2><<<lgrid, kBwdThreads, 0, s>>>(pre, dy, Lambda, sums, B, Tn, D, L.nC);
+  } else {
+    bwd_summary<T, 1><<<lgrid, kBwdThreads, 0, s>>>(pre, dy, Lambda, sums, B, Tn, D, L.nC);
+  }
   bwd_carry<<<lblocks, kBwdThreads, 0, s>>>(sums, dh_T, carry, dh0, B, D, L.nC);
-  bwd_emit<T><<<lgrid, kBwdThreads, 0, s>>>(x, pre, y, dy, h0, conv_w, Lambda, carry, dpre, dlo,
-                                            dxc, part, B, Tn, D, L.nC);
+  if (pair) {
+    bwd_emit<T, 2><<<lgrid, kBwdThreads, 0, s>>>(x, pre, y, dy, h0, conv_w, Lambda, carry, dpre,
+                                                 dlo, dxc, part, B, Tn, D, L.nC);
+  } else {
+    bwd_emit<T, 1><<<lgrid, kBwdThreads, 0, s>>>(x, pre, y, dy, h0, conv_w, Lambda, carry, dpre,
+                                                 dlo, dxc, part, B, Tn, D, L.nC);
+  }
   if constexpr (sizeof(T) == 2) {
     if (L.mfma_dxc) {
       bf16_t *wti = reinterpret_cast<bf16_t *>(ws + L.o_wti);
@@ -857,7 +1039,11 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
     const dim3 grid((Tn + kBwdValuRows - 1) / kBwdValuRows, H, B);
     dxc_valu<T><<<grid, 256, 0, s>>>(dpre, dlo, W_a, W_x, dxc, Tn, D, Dh);
   }
-  conv_bwd<T><<<lgrid, kBwdThreads, 0, s>>>(x, dxc, conv_w, dx, pcw, B, Tn, D, L.nC);
+  if (pair) {
+    conv_bwd<T, 2><<<lgrid, kBwdThreads, 0, s>>>(x, dxc, conv_w, dx, pcw, B, Tn, D, L.nC);
+  } else {
+    conv_bwd<T, 1><<<lgrid, kBwdThreads, 0, s>>>(x, dxc, conv_w, dx, pcw, B, Tn, D, L.nC);
+  }
   const int rows = B * Tn;  // < 2^31, checked by the caller
   if constexpr (sizeof(T) == 2) {
     if (L.mfma_dw) {
@@ -879,16 +1065,20 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
   const size_t PD = static_cast<size_t>(P) * D;
   const size_t nW = static_cast<size_t>(H) * Dh * Dh;
   ColSums cs;
-  cs.seg[0] = ColSum{part, static_cast<size_t>(D), static_cast<size_t>(D), P, db_a, nullptr};
-  cs.seg[1] = ColSum{part + PD, static_cast<size_t>(D), static_cast<size_t>(D), P, db_x, nullptr};
-  cs.seg[2] = ColSum{part + 2 * PD, static_cast<size_t>(D), static_cast<size_t>(D), P, dLambda,
-                     Lambda};
-  cs.seg[3] = ColSum{pcw, 4 * static_cast<size_t>(D), 4 * static_cast<size_t>(D), P, dconv_w,
+  const int GP = 4, GS = 4;  // (16 interleaved sums for the 256-partial vectors measured slower)
+  cs.seg[0] = ColSum{part, static_cast<size_t>(D), static_cast<size_t>(D), P, GP, db_a, nullptr};
+  cs.seg[1] = ColSum{part + PD, static_cast<size_t>(D), static_cast<size_t>(D), P, GP, db_x,
                      nullptr};
-  cs.seg[4] = ColSum{pw, 2 * nW, nW, L.S, dW_a, nullptr};
-  cs.seg[5] = ColSum{pw + nW, 2 * nW, nW, L.S, dW_x, nullptr};
-  const size_t nmax = std::max(nW, 4 * static_cast<size_t>(D));
-  colsum<<<dim3(static_cast<unsigned>((nmax + 63) / 64), kMaxSeg), 256, 0, s>>>(cs);
+  cs.seg[2] = ColSum{part + 2 * PD, static_cast<size_t>(D), static_cast<size_t>(D), P, GP,
+                     dLambda, Lambda};
+  cs.seg[3] = ColSum{pcw, 4 * static_cast<size_t>(D), 4 * static_cast<size_t>(D), P, GP, dconv_w,
+                     nullptr};
+  cs.seg[4] = ColSum{pw, 2 * nW, nW, L.S, GS, dW_a, nullptr};
+  cs.seg[5] = ColSum{pw + nW, 2 * nW, nW, L.S, GS, dW_x, nullptr};
+  size_t nblk = 0;
+  for (int i = 0; i < kMaxSeg; ++i)
+    nblk = std::max(nblk, (cs.seg[i].n + 256 / cs.seg[i].G - 1) / (256 / cs.seg[i].G));
+  colsum<<<dim3(static_cast<unsigned>(nblk), kMaxSeg), 256, 0, s>>>(cs);
   return hipGetLastError();
 }
 

@@ -87,6 +87,8 @@ def check(got, ref, tol, names=NAMES):
     ("bf16", 1, 64, 256, 1),     # exactly one chunk
     ("f32", 2, 130, 96, 3),      # fp32, Dh 32
     ("f32", 1, 65, 256, 1),      # fp32, Dh 256
+    ("bf16", 2, 70, 33, 3),      # odd D: one channel per lane in the lane kernels, Dh 11
+    ("f32", 1, 40, 15, 5),       # odd D, fp32, Dh 3
 ])
 def test_backward_small_shapes(dtype, B, T, D, H):
     inp = case(dtype, B, T, D, H, seed=B * 100 + T)
