@@ -56,6 +56,8 @@ _lib.rglru_scan_preacts.argtypes = [_vp] * 7 + [_i] * 5 + [_vp, _sz, _vp, _i, _i
 _lib.rglru_scan_preacts.restype = _i
 _lib.rglru_decode_step.argtypes = [_vp] * 10 + [_i] * 4 + [_vp]
 _lib.rglru_decode_step.restype = _i
+_lib.rglru_prefill_state.argtypes = [_vp, _vp] + [_i] * 4 + [_vp]
+_lib.rglru_prefill_state.restype = _i
 _lib.rglru_backward_workspace_size.argtypes = [_i] * 5
 _lib.rglru_backward_workspace_size.restype = _sz
 _lib.rglru_backward.argtypes = [_vp] * 19 + [_i] * 5 + [_vp, _sz, _vp]
@@ -191,6 +193,22 @@ def rglru_decode_step(x_t, conv_state, h, y_t, conv_w, W_a, b_a, W_x, b_x, Lambd
                                   _ptr(b_x, f32, "b_x"), _ptr(Lambda, f32, "Lambda"), N, D, H,
                                   _dt(io), _stream(stream)),
            "rglru_decode_step")
+
+
+def rglru_prefill_state(x, conv_state, stream=None):
+    """conv_state [B,3,D] (x's dtype) = the last three inputs of each sequence of x [B,T,D]."""
+    io = x.dtype
+    B, T, D = x.shape
+    _check(_lib.rglru_prefill_state(_ptr(x, io, "x"), _ptr(conv_state, io, "conv_state"), B, T, D,
+                                    _dt(io), _stream(stream)), "rglru_prefill_state")
+
+
+def prefill_state(x, stream=None):
+    """A new conv-state tensor [B,3,D] for continuing x [B,T,D] with decode steps."""
+    B, T, D = x.shape
+    cs = torch.empty((B, 3, D), dtype=x.dtype, device=x.device)
+    rglru_prefill_state(x, cs, stream)
+    return cs
 
 
 def rglru_backward_workspace_size(B, T, D, H, dtype) -> int:

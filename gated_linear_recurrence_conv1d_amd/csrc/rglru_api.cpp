@@ -305,6 +305,21 @@ rglru_status rglru_decode_step(const void *x_t, void *conv_state, float *h, void
                                          Lambda, N, D, H, io, static_cast<hipStream_t>(stream)));
 }
 
+rglru_status rglru_prefill_state(const void *x, void *conv_state, int B, int T, int D,
+                                 rglru_dtype dt, void *stream) {
+  if (B < 1 || T < 1 || D < 1) return RGLRU_ERR_INVALID_ARG;
+  if (dt != RGLRU_F32 && dt != RGLRU_BF16) return RGLRU_ERR_UNSUPPORTED;
+  if (!x || !conv_state) return RGLRU_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(conv_state, 16)) return RGLRU_ERR_INVALID_ARG;
+  const size_t eb = elem_bytes(dt);
+  if (overlaps(x, static_cast<size_t>(B) * T * D * eb, conv_state, static_cast<size_t>(B) * 3 * D * eb))
+    return RGLRU_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return hip_status(rglru::launch_prefill_state(x, conv_state, B, T, D,
+                                                dt == RGLRU_BF16 ? kBF16 : kF32,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 size_t rglru_backward_workspace_size(int B, int T, int D, int H, rglru_dtype dt) {
   if (check_shape(B, T, D, H, dt) != RGLRU_OK) return 0;
   return rglru::backward_layout(B, T, D, H, dt == RGLRU_BF16 ? kBF16 : kF32).total;

@@ -210,6 +210,57 @@ __global__ __launch_bounds__(256) void decode_valu(
   Elem<T>::store(y_t, off, hn);
 }
 
+// Prefill -> decode hand-off: conv_state[b][j] = x[b][T - 3 + j] (oldest first), zero where
+// T - 3 + j < 0 -- the conv's view of the inputs before the next step, exactly as the forward saw
+// them (zero padding before t = 0). 16-byte pieces when D allows, else elements.
+template <typename T, int V>
+__global__ __launch_bounds__(256) void prefill_state(const T *__restrict__ x, T *__restrict__ cs,
+                                                     int B, int Tn, int D) {
+  const int DV = D / V;
+  const size_t n = static_cast<size_t>(B) * 3 * DV;
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int dv = static_cast<int>(i % DV);
+  const size_t bj = i / DV;
+  const int j = static_cast<int>(bj % 3);
+  const int b = static_cast<int>(bj / 3);
+  const int t = Tn - 3 + j;
+  typedef u32x4_t P;
+  const size_t dst = (bj * D + static_cast<size_t>(dv) * V);
+  if constexpr (V * sizeof(T) == 16) {
+    P v = {0u, 0u, 0u, 0u};
+    if (t >= 0) v = *reinterpret_cast<const P *>(x + (static_cast<size_t>(b) * Tn + t) * D + dv * V);
+    *reinterpret_cast<P *>(cs + dst) = v;
+  } else {
+    cs[dst] = t >= 0 ? x[(static_cast<size_t>(b) * Tn + t) * D + dv] : T(0);
+  }
+}
+
+hipError_t launch_prefill_state(const void *x, void *conv_state, int B, int T, int D, int io,
+                                hipStream_t s) {
+  const size_t eb = io == kBF16 ? 2 : 4;
+  const bool vec = (D * eb) % 16 == 0;
+  const int V = vec ? static_cast<int>(16 / eb) : 1;
+  const size_t n = static_cast<size_t>(B) * 3 * (D / V);
+  const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+  if (io == kBF16) {
+    if (vec)
+      prefill_state<bf16_t, 8><<<blocks, 256, 0, s>>>(static_cast<const bf16_t *>(x),
+                                                       static_cast<bf16_t *>(conv_state), B, T, D);
+    else
+      prefill_state<bf16_t, 1><<<blocks, 256, 0, s>>>(static_cast<const bf16_t *>(x),
+                                                       static_cast<bf16_t *>(conv_state), B, T, D);
+  } else {
+    if (vec)
+      prefill_state<float, 4><<<blocks, 256, 0, s>>>(static_cast<const float *>(x),
+                                                     static_cast<float *>(conv_state), B, T, D);
+    else
+      prefill_state<float, 1><<<blocks, 256, 0, s>>>(static_cast<const float *>(x),
+                                                     static_cast<float *>(conv_state), B, T, D);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const void *x_t, void *conv_state, float *h, void *y_t,
                          const void *conv_w, const void *W_a, const float *b_a, const void *W_x,
                          const float *b_x, const float *Lambda, int N, int D, int H, int io,

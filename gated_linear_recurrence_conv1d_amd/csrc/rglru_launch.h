@@ -30,6 +30,10 @@ hipError_t launch_scan_chunked(const void *x, const void *pre, const void *conv_
                                int T, int D, int L, float2 *sums, float *carry, int io,
                                hipStream_t s);
 
+// conv_state[b] = the last three inputs of sequence b (zeros before t = 0).
+hipError_t launch_prefill_state(const void *x, void *conv_state, int B, int T, int D, int io,
+                                hipStream_t s);
+
 // One decode step for N rows, in place on conv_state and h.
 hipError_t launch_decode(const void *x_t, void *conv_state, float *h, void *y_t,
                          const void *conv_w, const void *W_a, const float *b_a, const void *W_x,

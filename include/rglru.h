@@ -148,6 +148,19 @@ rglru_status rglru_decode_step(const void *x_t, void *conv_state, float *h, void
                                const void *W_x, const float *b_x, const float *Lambda, int N,
                                int D, int H, rglru_dtype dt, void *stream);
 
+/* Prefill -> decode hand-off. After rglru_forward over x (which returns the final state h_T), this
+ * writes the conv state that rglru_decode_step continues from: conv_state[b][j] = x[b][T-3+j]
+ * for j = 0..2 (oldest first), zero where T-3+j < 0 -- the inputs the conv sees before the next
+ * step, with the forward's zero padding before t = 0. With h = h_T, decode steps on the
+ * following tokens then continue the sequence exactly as a forward over the concatenation would
+ * (the fixed-size state that makes decoding fast: alby13 blog, "Core Components of Griffin -- 1.
+ * RG-LRU" and "Griffin's Strengths").
+ *  x           [B][T][D] dtype       the prefilled inputs
+ *  conv_state  [B][3][D] dtype, out  must not overlap x
+ * Returns RGLRU_OK or an error code. */
+rglru_status rglru_prefill_state(const void *x, void *conv_state, int B, int T, int D,
+                                 rglru_dtype dt, void *stream);
+
 /* Bytes of device workspace rglru_backward needs for this shape (0 when the shape is invalid).
  * About 4 B (bf16) or 8 B (fp32) of pre-activations, the same again of gate gradients and 4 B of
  * conv-output gradient per element of x, plus chunk summaries and partial sums. */

@@ -188,3 +188,14 @@ def test_backward_workspace_size():
 ])
 def test_backward_argument_checks(kw, status):
     assert bwd(**kw) == status
+
+
+def test_prefill_state_argument_checks():
+    x, cs = 0x100000000, 0x200000000
+    ok_shape = (2, 64, 512, rg.RGLRU_BF16)
+    assert lib.rglru_prefill_state(None, cs, *ok_shape, None) == rg.RGLRU_ERR_INVALID_ARG
+    assert lib.rglru_prefill_state(x, None, *ok_shape, None) == rg.RGLRU_ERR_INVALID_ARG
+    assert lib.rglru_prefill_state(x, x + 4096, *ok_shape, None) == rg.RGLRU_ERR_INVALID_ARG  # overlap
+    assert lib.rglru_prefill_state(x + 8, cs, *ok_shape, None) == rg.RGLRU_ERR_INVALID_ARG    # align
+    assert lib.rglru_prefill_state(x, cs, 0, 64, 512, rg.RGLRU_BF16, None) == rg.RGLRU_ERR_INVALID_ARG
+    assert lib.rglru_prefill_state(x, cs, 2, 64, 512, 9, None) == rg.RGLRU_ERR_UNSUPPORTED

@@ -309,13 +309,39 @@ def test_decode_fp32_and_resume_of_forward():
     g1 = dict(g)
     g1["x"] = g["x"][:, :t1].contiguous()
     _, h1 = gpu_forward(g1)
-    cs = g["x"][:, t1 - 3:t1].contiguous().clone()
+    cs = rg.prefill_state(g1["x"])  # the prefill -> decode hand-off
+    assert torch.equal(cs, g["x"][:, t1 - 3:t1])
     h = h1.clone()
     for t in range(t1, T):
         yt = rg.decode_step(g["x"][:, t].contiguous(), cs, h, g["conv_w"], g["W_a"], g["b_a"],
                             g["W_x"], g["b_x"], g["Lam"])
         torch.cuda.synchronize()
         assert err(host(yt), yr[:, t]) < TOL["f32"]
+
+
+@pytest.mark.parametrize("dtype,B,T,D,H,t1", [("bf16", 2, 200, 512, 2, 130), ("bf16", 3, 70, 96, 2, 2),
+                                             ("bf16", 1, 9, 256, 1, 1), ("f32", 2, 50, 24, 2, 5)])
+def test_prefill_then_decode_continues_the_sequence(dtype, B, T, D, H, t1):
+    """Forward over x[:, :t1] (the automatic plan: fused for bf16 Dh 256), hand-off with
+    rglru_prefill_state (zeros before t = 0 when t1 < 3), then decode steps over x[:, t1:] give
+    the oracle's forward over the whole sequence."""
+    inp = case(dtype, B, T, D, H, seed=T + t1)
+    g = to_device(inp)
+    yr, hr = oracle_forward(inp)
+    g1 = dict(g)
+    g1["x"] = g["x"][:, :t1].contiguous()
+    _, h = gpu_forward(g1)
+    cs = rg.prefill_state(g1["x"])
+    expect = torch.zeros_like(cs)
+    k = min(3, t1)
+    expect[:, 3 - k:] = g["x"][:, t1 - k:t1]
+    assert torch.equal(cs, expect)
+    for t in range(t1, T):
+        yt = rg.decode_step(g["x"][:, t].contiguous(), cs, h, g["conv_w"], g["W_a"], g["b_a"],
+                            g["W_x"], g["b_x"], g["Lam"])
+        torch.cuda.synchronize()
+        assert err(host(yt), yr[:, t]) < TOL[dtype], t
+    assert err(h.cpu().numpy(), hr) < TOL[dtype]
 
 
 # ---------------------------------------------------------------------------------------------
