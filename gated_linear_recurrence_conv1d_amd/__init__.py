@@ -58,6 +58,8 @@ _lib.rglru_decode_step.argtypes = [_vp] * 10 + [_i] * 4 + [_vp]
 _lib.rglru_decode_step.restype = _i
 _lib.rglru_prefill_state.argtypes = [_vp, _vp] + [_i] * 4 + [_vp]
 _lib.rglru_prefill_state.restype = _i
+_lib.rglru_local_mqa.argtypes = [_vp] * 4 + [_i] * 5 + [ctypes.c_float, _i, _vp]
+_lib.rglru_local_mqa.restype = _i
 _lib.rglru_backward_workspace_size.argtypes = [_i] * 5
 _lib.rglru_backward_workspace_size.restype = _sz
 _lib.rglru_backward.argtypes = [_vp] * 19 + [_i] * 5 + [_vp, _sz, _vp]
@@ -209,6 +211,22 @@ def prefill_state(x, stream=None):
     cs = torch.empty((B, 3, D), dtype=x.dtype, device=x.device)
     rglru_prefill_state(x, cs, stream)
     return cs
+
+
+def rglru_local_mqa(q, k, v, o, window, scale=0.0, stream=None):
+    """q, o [B,T,Hq,dh]; k, v [B,T,dh]; bf16."""
+    B, T, Hq, dh = q.shape
+    bf = torch.bfloat16
+    _check(_lib.rglru_local_mqa(_ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
+                                _ptr(o, bf, "o"), B, T, Hq, dh, int(window), float(scale),
+                                RGLRU_BF16, _stream(stream)), "rglru_local_mqa")
+
+
+def local_mqa(q, k, v, window, scale=0.0, stream=None):
+    """Returns o [B,T,Hq,dh] (bf16)."""
+    o = torch.empty_like(q)
+    rglru_local_mqa(q, k, v, o, window, scale, stream)
+    return o
 
 
 def rglru_backward_workspace_size(B, T, D, H, dtype) -> int:

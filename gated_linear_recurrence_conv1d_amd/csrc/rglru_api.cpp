@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "rglru.h"
 #include "rglru_launch.h"
@@ -318,6 +319,27 @@ rglru_status rglru_prefill_state(const void *x, void *conv_state, int B, int T, 
   return hip_status(rglru::launch_prefill_state(x, conv_state, B, T, D,
                                                 dt == RGLRU_BF16 ? kBF16 : kF32,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+rglru_status rglru_local_mqa(const void *q, const void *k, const void *v, void *o, int B, int T,
+                             int Hq, int dh, int window, float scale, rglru_dtype dt,
+                             void *stream) {
+  if (B < 1 || T < 1 || Hq < 1 || dh < 1 || window < 1) return RGLRU_ERR_INVALID_ARG;
+  if (dt != RGLRU_BF16 || !rglru::local_mqa_supported(dh)) return RGLRU_ERR_UNSUPPORTED;
+  if (B > 65535 || Hq > 65535) return RGLRU_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o) return RGLRU_ERR_INVALID_ARG;
+  const void *vec16[] = {q, k, v, o};
+  for (const void *p : vec16)
+    if (!aligned(p, 16)) return RGLRU_ERR_INVALID_ARG;
+  if (!(scale == scale) || scale < 0.0f) return RGLRU_ERR_INVALID_ARG;  // NaN or negative
+  const size_t qbytes = static_cast<size_t>(B) * T * Hq * dh * 2;
+  const size_t kbytes = static_cast<size_t>(B) * T * dh * 2;
+  if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kbytes) || overlaps(o, qbytes, v, kbytes))
+    return RGLRU_ERR_INVALID_ARG;
+  if (scale == 0.0f) scale = 1.0f / std::sqrt(static_cast<float>(dh));
+  (void)hipGetLastError();
+  return hip_status(rglru::launch_local_mqa(q, k, v, o, B, T, Hq, dh, window, scale,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 size_t rglru_backward_workspace_size(int B, int T, int D, int H, rglru_dtype dt) {

@@ -65,6 +65,11 @@ hipError_t launch_resident_preacts(const void *x, const void *conv_w, const void
 hipError_t launch_resident_dxc(const void *dp, const void *wti, float *dxc, int B, int T, int D,
                                int H, hipStream_t s);
 
+// Local sliding-window multi-query attention, forward (bf16, dh in {64, 128, 256}).
+bool local_mqa_supported(int dh);
+hipError_t launch_local_mqa(const void *q, const void *k, const void *v, void *o, int B, int T,
+                            int Hq, int dh, int window, float scale, hipStream_t s);
+
 // Backward (gradients of every input and parameter). Time is cut into chunks of kBwdChunk steps
 // for the reverse scan. BwdLayout gives the workspace carve (byte offsets, 256-byte aligned) and
 // the row split of the dW contraction; launch_backward assumes a workspace of layout.total bytes.

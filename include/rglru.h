@@ -161,6 +161,25 @@ rglru_status rglru_decode_step(const void *x_t, void *conv_state, float *h, void
 rglru_status rglru_prefill_state(const void *x, void *conv_state, int B, int T, int D,
                                  rglru_dtype dt, void *stream);
 
+/* Local (sliding-window) multi-query attention, forward: Griffin's other temporal-mixing block,
+ * whose query heads share one key/value head and whose positions attend only within a fixed
+ * window of recent positions, typically 1024 (alby13 blog "Beyond Transformer Architecture: Griffin
+ * and Google RecurrentGemma", section "Core Components of Griffin -- 2. Local Sliding-Window MQA";
+ * Soham De's Griffin thread, tweet on adding a local attention block every two recurrent blocks).
+ *   o[b][t][h] = sum_u softmax_u(scale * <q[b][t][h], k[b][u]>) v[b][u],
+ *   u in [max(0, t - window + 1), t]   (the window holds `window` positions including t).
+ *  q  [B][T][Hq][dh] bf16    query heads
+ *  k  [B][T][dh] bf16        the shared key head
+ *  v  [B][T][dh] bf16        the shared value head
+ *  o  [B][T][Hq][dh] bf16, out, must not overlap q, k or v
+ *  window >= 1; scale > 0, or 0 for 1/sqrt(dh)
+ * Softmax and both contractions accumulate in fp32 (MFMA); probabilities enter the second
+ * contraction as bf16 hi + lo (about 16 bits). Supported: dt = RGLRU_BF16, dh in {64, 128, 256} (else
+ * RGLRU_ERR_UNSUPPORTED). No workspace. */
+rglru_status rglru_local_mqa(const void *q, const void *k, const void *v, void *o, int B, int T,
+                             int Hq, int dh, int window, float scale, rglru_dtype dt,
+                             void *stream);
+
 /* Bytes of device workspace rglru_backward needs for this shape (0 when the shape is invalid).
  * About 4 B (bf16) or 8 B (fp32) of pre-activations, the same again of gate gradients and 4 B of
  * conv-output gradient per element of x, plus chunk summaries and partial sums. */

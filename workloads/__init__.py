@@ -135,6 +135,16 @@ def make_cotangents(inp: dict, seed: int = 1) -> dict:
     return dict(dy=dy, dh_T=dh_T)
 
 
+def make_attention_inputs(B: int, T: int, Hq: int, dh: int, seed: int = 0) -> dict:
+    """Seeded inputs of local multi-query attention: q [B,T,Hq,dh], k and v [B,T,dh], each ~N(0,1)
+    drawn in float32 in that order and rounded to bf16 (returned as float32 arrays)."""
+    rng = np.random.default_rng(seed)
+    q = round_to_dtype(rng.standard_normal((B, T, Hq, dh), dtype=np.float32), "bf16")
+    k = round_to_dtype(rng.standard_normal((B, T, dh), dtype=np.float32), "bf16")
+    v = round_to_dtype(rng.standard_normal((B, T, dh), dtype=np.float32), "bf16")
+    return dict(q=q, k=k, v=v)
+
+
 def to_device(inp: dict, device="cuda"):
     """torch tensors on `device` for the GPU side: I/O-dtype tensors for x, conv_w, W_a, W_x and
     conv_state (exact, since the values are already representable), float32 for the rest."""
