@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "RG-LRU fwd tokens·channels/s + % HBM peak, B=8 T=2048 D=2560 bf16"
 KERNEL_SOURCES = ["rglru_device.h", "rglru_mfma.h", "rglru_gates.hip", "rglru_scan.hip",
                   "rglru_fused.hip"]
@@ -294,6 +295,39 @@ def backward_leg(torch, rg, w, g, y, warmup=200, reps=100):
                                  "traffic = measured HBM bytes of all its kernels per call"}}
 
 
+def mqa_leg(torch, rg, warmup=20, reps=50):
+    """Local sliding-window multi-query attention (rglru_local_mqa) on the Griffin-2B-shaped
+    attention layer: B=8, T=2048, 10 query heads of 256 sharing one key/value head, window 1024,
+    bf16, seeded N(0,1) inputs. Roofline: MFMA (bf16 dense peak) against the algorithmic flops
+    4 * B * Hq * dh * (number of visible (query, key) pairs); the kernel issues 1.5x that in MFMA
+    work (the probabilities enter the second contraction as bf16 hi + lo)."""
+    from workloads import make_attention_inputs
+    B, T, Hq, dh, W = 8, 2048, 10, 256, 1024
+    inp = make_attention_inputs(B, T, Hq, dh, seed=0)
+    q = torch.from_numpy(inp["q"]).to("cuda", torch.bfloat16)
+    k = torch.from_numpy(inp["k"]).to("cuda", torch.bfloat16)
+    v = torch.from_numpy(inp["v"]).to("cuda", torch.bfloat16)
+    o = torch.empty_like(q)
+    for _ in range(warmup):
+        rg.rglru_local_mqa(q, k, v, o, W)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        rg.rglru_local_mqa(q, k, v, o, W)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    pairs = sum(min(t + 1, W) for t in range(T))
+    flops = 4.0 * B * Hq * dh * pairs
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": f"local_mqa_b{B}_t{T}_hq{Hq}_dh{dh}_w{W}_bf16", "ms": round(ms, 4),
+            "value": B * T * Hq / (ms * 1e-3), "unit": "query rows/s", "reps": reps,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "algorithmic_flops": flops}}
+
+
 def cpu_baseline(w, inp, min_seconds=2.0):
     """The fp64 oracle, as it stands, on the host cores (OpenMP over (sequence, head)): whole
     forwards of the full workload, repeated until min_seconds of wall time have passed (a few
@@ -322,6 +356,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
+    ap.add_argument("--no-mqa", action="store_true", help="skip the local-attention leg")
     ap.add_argument("--bwd-warmup", type=int, default=200)
     ap.add_argument("--bwd-reps", type=int, default=100)
     ap.add_argument("--backward-traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -472,6 +507,8 @@ def main():
         line["backward"] = backward_leg(torch, rg, w, g, ys[0], args.bwd_warmup, args.bwd_reps)
     if not args.no_decode:
         line["decode"] = decode_leg(torch, rg)
+    if not args.no_mqa:
+        line["local_mqa"] = mqa_leg(torch, rg)
     if args.copy_calibration:
         src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
