@@ -327,6 +327,9 @@ rglru_status rglru_local_mqa(const void *q, const void *k, const void *v, void *
   if (B < 1 || T < 1 || Hq < 1 || dh < 1 || window < 1) return RGLRU_ERR_INVALID_ARG;
   if (dt != RGLRU_BF16 || !rglru::local_mqa_supported(dh)) return RGLRU_ERR_UNSUPPORTED;
   if (B > 65535 || Hq > 65535) return RGLRU_ERR_UNSUPPORTED;
+  // one sequence's k (and v) must fit a 32-bit buffer range, with room past it for the kernel's
+  // no-op loads
+  if (static_cast<size_t>(T) * dh * 2 > (size_t{1} << 30)) return RGLRU_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o) return RGLRU_ERR_INVALID_ARG;
   const void *vec16[] = {q, k, v, o};
   for (const void *p : vec16)

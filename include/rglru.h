@@ -174,8 +174,8 @@ rglru_status rglru_prefill_state(const void *x, void *conv_state, int B, int T, 
  *  o  [B][T][Hq][dh] bf16, out, must not overlap q, k or v
  *  window >= 1; scale > 0, or 0 for 1/sqrt(dh)
  * Softmax and both contractions accumulate in fp32 (MFMA); probabilities enter the second
- * contraction as bf16 hi + lo (about 16 bits). Supported: dt = RGLRU_BF16, dh in {64, 128, 256} (else
- * RGLRU_ERR_UNSUPPORTED). No workspace. */
+ * contraction as bf16 hi + lo (about 16 bits). Supported: dt = RGLRU_BF16, dh in {64, 128, 256},
+ * T * dh * 2 <= 2^30 bytes per sequence of k (else RGLRU_ERR_UNSUPPORTED). No workspace. */
 rglru_status rglru_local_mqa(const void *q, const void *k, const void *v, void *o, int B, int T,
                              int Hq, int dh, int window, float scale, rglru_dtype dt,
                              void *stream);

@@ -130,6 +130,26 @@ def test_decode_argument_checks():
     assert dec(dt=5) == rg.RGLRU_ERR_UNSUPPORTED
 
 
+def test_local_mqa_argument_checks():
+    def mqa(**kw):
+        a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, B=2, T=64, Hq=2,
+                 dh=128, window=16, scale=0.0, dt=rg.RGLRU_BF16)
+        a.update(kw)
+        return lib.rglru_local_mqa(a["q"], a["k"], a["v"], a["o"], a["B"], a["T"], a["Hq"],
+                                   a["dh"], a["window"], a["scale"], a["dt"], None)
+    assert mqa(B=0) == rg.RGLRU_ERR_INVALID_ARG
+    assert mqa(window=0) == rg.RGLRU_ERR_INVALID_ARG
+    assert mqa(v=None) == rg.RGLRU_ERR_INVALID_ARG
+    assert mqa(dh=96) == rg.RGLRU_ERR_UNSUPPORTED
+    assert mqa(dt=rg.RGLRU_F32) == rg.RGLRU_ERR_UNSUPPORTED
+    assert mqa(T=(1 << 21) + 1, dh=256) == rg.RGLRU_ERR_UNSUPPORTED  # k of one sequence > 1 GiB
+    assert mqa(k=FAKE + 0x100008) == rg.RGLRU_ERR_INVALID_ARG        # misaligned
+    assert mqa(scale=-1.0) == rg.RGLRU_ERR_INVALID_ARG
+    assert mqa(scale=float("nan")) == rg.RGLRU_ERR_INVALID_ARG
+    assert mqa(o=FAKE + 0x200000 + 4096) == rg.RGLRU_ERR_INVALID_ARG  # o overlaps v
+    assert mqa(o=FAKE) == rg.RGLRU_ERR_INVALID_ARG                    # o is q
+
+
 def test_gate_and_scan_stage_checks():
     assert lib.rglru_gate_preacts(FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000,
                                   FAKE + 0x4000, FAKE + 0x5000, None, 2, 64, 512, 2,
