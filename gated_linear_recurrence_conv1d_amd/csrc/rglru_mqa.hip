@@ -243,10 +243,14 @@ __global__ __launch_bounds__(Mqa<DH>::kThreads, 1) void local_mqa_fwd(
     const int Ks0 = kb * M::kKB + 32 * side;
     const bool full = Ks0 + 31 <= qw && Ks0 > qw + 31 - W && Ks0 + 31 < T;
     if (!full) {
+      // lane terms re-derived from the thread index here (this path is rare; kept live, they
+      // would be spilled, and a reload waits for the loads in flight)
+      const int tx = static_cast<int>(__builtin_amdgcn_workitem_id_x());
+      const int rel = qw + (tx & 31) - Ks0 - 4 * ((tx >> 5) & 1);  // row - (key of j = 0)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int key = Ks0 + 8 * (j >> 2) + 4 * half + (j & 3);
-        const bool ok = key <= qr && key > qr - W && key < T;
+        const int dk = 8 * (j >> 2) + (j & 3);  // key - (key of j = 0)
+        const bool ok = dk <= rel && dk > rel - W && Ks0 + 4 * ((tx >> 5) & 1) + dk < T;
         sacc[j] = ok ? sacc[j] : -__builtin_inff();
       }
     }
