@@ -936,6 +936,10 @@ BwdLayout backward_layout(int B, int T, int D, int H, int io) {
   L.nC = (T + kBwdChunk - 1) / kBwdChunk;
   const long long rows = static_cast<long long>(B) * T;
   L.mfma_dxc = io == kBF16 && (Dh == 32 || Dh == 64 || Dh == 128 || Dh == 256);
+  L.fused = io == kBF16 && static_cast<long long>(T) * D * 4 < (1LL << 31) &&
+            fused_backward_supported(Dh);
+  // partial sums of dpa, dpx, r dz: per chunk, or per tile of the fused pass
+  L.nCp = L.fused ? (T + kFusedBwdRows - 1) / kFusedBwdRows : L.nC;
   L.mfma_dw = io == kBF16 && (Dh == 128 || Dh == 256);
   // Row splits of the dW contraction. MFMA: one 256 x Dh tile per workgroup and one workgroup
   // per CU (its LDS), so about as many workgroups as the 256 CUs of the chip, never more (a
@@ -957,16 +961,18 @@ BwdLayout backward_layout(int B, int T, int D, int H, int io) {
     off += (bytes + 255) / 256 * 256;
     return r;
   };
-  L.o_pre = take(n * pairb);
+  L.o_pre = take(L.fused ? 0 : n * pairb);
   L.o_dpre = take(n * pairb);
   L.o_dlo = take(io == kBF16 ? n * 4 : 0);
   L.o_dxc = take(n * sizeof(float));
-  L.o_sums = take(P * D * sizeof(float2));
-  L.o_carry = take(P * D * sizeof(float));
-  L.o_part = take(3 * P * D * sizeof(float));
+  L.o_sums = take(L.fused ? 0 : P * D * sizeof(float2));
+  L.o_carry = take(L.fused ? 0 : P * D * sizeof(float));
+  L.o_part = take(3 * static_cast<size_t>(B) * L.nCp * D * sizeof(float));
   L.o_pcw = take(4 * P * D * sizeof(float));
   L.o_pw = take(static_cast<size_t>(L.S) * H * 2 * Dh * Dh * sizeof(float));
   L.o_wti = take(L.mfma_dxc ? static_cast<size_t>(H) * Dh * 2 * Dh * sizeof(bf16_t) : 0);
+  L.o_ctrl = take(L.fused ? (2 + static_cast<size_t>(H)) * sizeof(unsigned) : 0);
+  L.o_lb = take(L.fused ? fused_backward_slots(B, T, D) * sizeof(unsigned long long) : 0);
   L.total = off;
   return L;
 }
@@ -991,31 +997,45 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
   float *part = reinterpret_cast<float *>(ws + L.o_part);
   float *pcw = reinterpret_cast<float *>(ws + L.o_pcw);
   float *pw = reinterpret_cast<float *>(ws + L.o_pw);
-  // pre-activations recomputed with the conv output split into bf16 hi + lo: the gradients
-  // amplify pre-activation errors (through r (1 - r) and 1/m), so the backward does not reuse
-  // the forward's bf16-operand rounding
   const bool resident = io == kBF16 && static_cast<long long>(Tn) * D * 4 < (1LL << 31);
-  hipError_t e = resident && resident_preacts_supported(Dh)
-                     ? launch_resident_preacts(x, conv_w, W_a, b_a, W_x, b_x, pre, B, Tn, D, H, s)
-                     : launch_gates(x, conv_w, W_a, b_a, W_x, b_x, pre, B, Tn, D, H, io, s, true);
-  if (e != hipSuccess) return e;
   const size_t lanes = static_cast<size_t>(B) * D;
   const unsigned lblocks = static_cast<unsigned>((lanes + kBwdThreads - 1) / kBwdThreads);
   // lane kernels: two adjacent channels per lane when D is even
   const bool pair = D % 2 == 0;
   const dim3 lgrid(pair ? (lblocks + 1) / 2 : lblocks, L.nC);
-  if (pair) {
-    bwd_summary<T, 2><<<lgrid, kBwdThreads, 0, s>>>(pre, dy, Lambda, sums, B, Tn, D, L.nC);
-  } else {
-    bwd_summary<T, 1><<<lgrid, kBwdThreads, 0, s>>>(pre, dy, Lambda, sums, B, Tn, D, L.nC);
+  hipError_t e = hipSuccess;
+  if constexpr (sizeof(T) == 2) {
+    if (L.fused) {
+      // passes 1-3 as one tile pass (partial sums per tile of kFusedBwdRows steps)
+      e = launch_fused_backward(x, y, dy, h0, dh_T, conv_w, W_a, b_a, W_x, b_x, Lambda,
+                                reinterpret_cast<uint32_t *>(dpre),
+                                reinterpret_cast<uint32_t *>(dlo), dxc, part, dh0, B, Tn, D, H,
+                                reinterpret_cast<unsigned *>(ws + L.o_ctrl),
+                                reinterpret_cast<unsigned long long *>(ws + L.o_lb), s);
+      if (e != hipSuccess) return e;
+    }
   }
-  bwd_carry<<<lblocks, kBwdThreads, 0, s>>>(sums, dh_T, carry, dh0, B, D, L.nC);
-  if (pair) {
-    bwd_emit<T, 2><<<lgrid, kBwdThreads, 0, s>>>(x, pre, y, dy, h0, conv_w, Lambda, carry, dpre,
-                                                 dlo, dxc, part, B, Tn, D, L.nC);
-  } else {
-    bwd_emit<T, 1><<<lgrid, kBwdThreads, 0, s>>>(x, pre, y, dy, h0, conv_w, Lambda, carry, dpre,
-                                                 dlo, dxc, part, B, Tn, D, L.nC);
+  if (!L.fused) {
+    // pre-activations recomputed with the conv output split into bf16 hi + lo: the gradients
+    // amplify pre-activation errors (through r (1 - r) and 1/m), so the backward does not reuse
+    // the forward's bf16-operand rounding
+    e = resident && resident_preacts_supported(Dh)
+            ? launch_resident_preacts(x, conv_w, W_a, b_a, W_x, b_x, pre, B, Tn, D, H, s)
+            : launch_gates(x, conv_w, W_a, b_a, W_x, b_x, pre, B, Tn, D, H, io, s, true);
+    if (e != hipSuccess) return e;
+    if (pair) {
+      bwd_summary<T, 2><<<lgrid, kBwdThreads, 0, s>>>(pre, dy, Lambda, sums, B, Tn, D, L.nC);
+    } else {
+      bwd_summary<T, 1><<<lgrid, kBwdThreads, 0, s>>>(pre, dy, Lambda, sums, B, Tn, D, L.nC);
+    }
+    bwd_carry<<<lblocks, kBwdThreads, 0, s>>>(sums, dh_T, carry, dh0, B, D, L.nC);
+    if (pair) {
+      bwd_emit<T, 2><<<lgrid, kBwdThreads, 0, s>>>(x, pre, y, dy, h0, conv_w, Lambda, carry, dpre,
+                                                   dlo, dxc, part, B, Tn, D, L.nC);
+    } else {
+      bwd_emit<T, 1><<<lgrid, kBwdThreads, 0, s>>>(x, pre, y, dy, h0, conv_w, Lambda, carry, dpre,
+                                                   dlo, dxc, part, B, Tn, D, L.nC);
+    }
   }
   if constexpr (sizeof(T) == 2) {
     if (L.mfma_dxc) {
@@ -1062,14 +1082,15 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
   }
   // fixed-order sums of the partials
   const int P = B * L.nC;
-  const size_t PD = static_cast<size_t>(P) * D;
+  const int Pp = B * L.nCp;  // partials of dpa, dpx, r dz
+  const size_t PD = static_cast<size_t>(Pp) * D;
   const size_t nW = static_cast<size_t>(H) * Dh * Dh;
   ColSums cs;
   const int GP = 4, GS = 4;  // (16 interleaved sums for the 256-partial vectors measured slower)
-  cs.seg[0] = ColSum{part, static_cast<size_t>(D), static_cast<size_t>(D), P, GP, db_a, nullptr};
-  cs.seg[1] = ColSum{part + PD, static_cast<size_t>(D), static_cast<size_t>(D), P, GP, db_x,
+  cs.seg[0] = ColSum{part, static_cast<size_t>(D), static_cast<size_t>(D), Pp, GP, db_a, nullptr};
+  cs.seg[1] = ColSum{part + PD, static_cast<size_t>(D), static_cast<size_t>(D), Pp, GP, db_x,
                      nullptr};
-  cs.seg[2] = ColSum{part + 2 * PD, static_cast<size_t>(D), static_cast<size_t>(D), P, GP,
+  cs.seg[2] = ColSum{part + 2 * PD, static_cast<size_t>(D), static_cast<size_t>(D), Pp, GP,
                      dLambda, Lambda};
   cs.seg[3] = ColSum{pcw, 4 * static_cast<size_t>(D), 4 * static_cast<size_t>(D), P, GP, dconv_w,
                      nullptr};

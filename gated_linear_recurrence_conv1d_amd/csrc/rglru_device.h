@@ -96,6 +96,31 @@ template <> struct PrePair<bf16_t> {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Words of a tile-to-tile look-back (a carried state crossing 64-step tiles of one sequence):
+// two fp32 in one 64-bit word, stored and loaded as single relaxed agent-scope atomics (each word
+// is self-contained, so no release/acquire fences are needed). kEmpty marks a word not yet
+// written (a NaN pattern no pack2 produces: pack2 canonicalises NaN in its low half); waits are
+// bounded by kMaxSpin polls, after which the waiting tile writes NaN instead of hanging.
+constexpr unsigned long long kEmpty = ~0ull;
+constexpr unsigned kMaxSpin = 1u << 26;
+__device__ __forceinline__ unsigned long long pack2(float lo, float hi) {
+  if (lo != lo) lo = __builtin_nanf("");
+  return static_cast<unsigned long long>(__float_as_uint(lo)) |
+         (static_cast<unsigned long long>(__float_as_uint(hi)) << 32);
+}
+__device__ __forceinline__ float lo_f(unsigned long long v) {
+  return __uint_as_float(static_cast<uint32_t>(v));
+}
+__device__ __forceinline__ float hi_f(unsigned long long v) {
+  return __uint_as_float(static_cast<uint32_t>(v >> 32));
+}
+__device__ __forceinline__ unsigned long long ld_relaxed(const unsigned long long *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(unsigned long long *p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Per-channel constant kd = -c * softplus(-Lambda), so that log a = kd * r. softplus is taken
 // as max(z,0) + log1p(exp(-|z|)); computed once per lane with the accurate library functions.
 __device__ __forceinline__ float decay_coeff(float lambda) {

@@ -39,9 +39,7 @@
 
 namespace rglru {
 
-constexpr unsigned long long kEmpty = ~0ull;
 constexpr int kFusedRows = 64;
-constexpr unsigned kMaxSpin = 1u << 26;  // bounded wait: a lost predecessor yields NaN, not a hang
 constexpr unsigned kWaitVm0 = 0x0F70;     // s_waitcnt operand: vmcnt(0) only
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -65,23 +63,6 @@ template <int DH> struct Fused {
   static constexpr int kXRows = kLoads * kRowsPerLoad;  // staged rows (tile + 3-row halo)
 };
 
-__device__ __forceinline__ unsigned long long pack2(float lo, float hi) {
-  if (lo != lo) lo = __builtin_nanf("");
-  return static_cast<unsigned long long>(__float_as_uint(lo)) |
-         (static_cast<unsigned long long>(__float_as_uint(hi)) << 32);
-}
-__device__ __forceinline__ float lo_f(unsigned long long v) {
-  return __uint_as_float(static_cast<uint32_t>(v));
-}
-__device__ __forceinline__ float hi_f(unsigned long long v) {
-  return __uint_as_float(static_cast<uint32_t>(v >> 32));
-}
-__device__ __forceinline__ unsigned long long ld_relaxed(const unsigned long long *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_relaxed(unsigned long long *p, unsigned long long v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 __device__ __forceinline__ bf16x8_t f32x8_to_bf16x8(const float *p) {
   const float4 v0 = *reinterpret_cast<const float4 *>(p);
@@ -102,6 +83,13 @@ __global__ void fused_reset(unsigned long long *slots, size_t n, unsigned *ctrl,
     slots[i] = kEmpty;
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < nctrl; i += blockDim.x) ctrl[i] = 0u;
+}
+
+hipError_t launch_lookback_reset(unsigned long long *slots, size_t n, unsigned *ctrl, int nctrl,
+                                 hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 2048));
+  fused_reset<<<std::max(1u, blocks), 256, 0, s>>>(slots, n, ctrl, nctrl);
+  return hipGetLastError();
 }
 
 struct TileCtx {

@@ -65,6 +65,23 @@ hipError_t launch_resident_preacts(const void *x, const void *conv_w, const void
 hipError_t launch_resident_dxc(const void *dp, const void *wti, float *dxc, int B, int T, int D,
                                int H, hipStream_t s);
 
+// Reset of a look-back area: n slots to the empty pattern and nctrl control words to 0.
+hipError_t launch_lookback_reset(unsigned long long *slots, size_t n, unsigned *ctrl, int nctrl,
+                                 hipStream_t s);
+
+// The backward's per-element part in one pass over kFusedBwdRows-step tiles, latest first (bf16, Dh in
+// {128, 256}, T * D * 4 < 2^31): pre-activations recomputed on MFMA, the adjoint carried from
+// tile to tile, and dpre / dlo / dxc / the per-tile partial sums / dh0 as the separate kernels
+// produce them. ctrl: 2 + H words, slots: fused_backward_slots(B, T, D) words (both reset here).
+bool fused_backward_supported(int Dh);
+size_t fused_backward_slots(int B, int T, int D);
+hipError_t launch_fused_backward(const void *x, const void *y, const void *dy, const float *h0,
+                                 const float *dh_T, const void *conv_w, const void *W_a,
+                                 const float *b_a, const void *W_x, const float *b_x,
+                                 const float *Lambda, uint32_t *dpre, uint32_t *dlo, float *dxc,
+                                 float *part, float *dh0, int B, int T, int D, int H,
+                                 unsigned *ctrl, unsigned long long *slots, hipStream_t s);
+
 // Local sliding-window multi-query attention, forward (bf16, dh in {64, 128, 256}).
 bool local_mqa_supported(int dh);
 hipError_t launch_local_mqa(const void *q, const void *k, const void *v, void *o, int B, int T,
@@ -75,12 +92,16 @@ hipError_t launch_local_mqa(const void *q, const void *k, const void *v, void *o
 // the row split of the dW contraction; launch_backward assumes a workspace of layout.total bytes.
 constexpr int kBwdChunk = 64;
 constexpr int kBwdCUs = 256;  // CUs the dW split is sized for (MI355X)
+constexpr int kFusedBwdRows = 32;  // tile of the fused per-element pass
 struct BwdLayout {
   int nC;                     // chunks per sequence
+  int nCp;                    // partial-sum rows per sequence (chunks, or fused-pass tiles)
   int S;                      // row splits of the dW contraction
   int rows_per_split;         // rows of the flattened (b, t) index per split
   bool mfma_dxc, mfma_dw;     // which contractions run on MFMA
-  size_t o_pre, o_dpre, o_dlo, o_dxc, o_sums, o_carry, o_part, o_pcw, o_pw, o_wti, total;
+  bool fused;                 // the per-element part as one tile pass (no pre, sums, carry)
+  size_t o_pre, o_dpre, o_dlo, o_dxc, o_sums, o_carry, o_part, o_pcw, o_pw, o_wti, o_ctrl, o_lb,
+      total;
 };
 BwdLayout backward_layout(int B, int T, int D, int H, int io);
 hipError_t launch_backward(const void *x, const void *conv_w, const void *W_a, const float *b_a,

@@ -182,7 +182,8 @@ def bwd(**kw):
 def test_backward_workspace_size():
     B, T, D, H = 8, 2048, 2560, 10
     n = B * T * D
-    # pre-activation pairs, gate-gradient pairs, conv-output gradients
+    # gate-gradient pairs (hi and lo) and conv-output gradients; the unfused plan adds the
+    # pre-activation pairs
     assert rg.rglru_backward_workspace_size(B, T, D, H, "bf16") >= n * (4 + 4 + 4)
     assert rg.rglru_backward_workspace_size(B, T, D, H, "f32") >= n * (8 + 8 + 4)
     assert rg.rglru_backward_workspace_size(B, T, D, 7, "bf16") == 0
