@@ -30,11 +30,11 @@ METRIC = "RG-LRU fwd tokens·channels/s + % HBM peak, B=8 T=2048 D=2560 bf16"
 KERNEL_SOURCES = ["rglru_device.h", "rglru_mfma.h", "rglru_gates.hip", "rglru_scan.hip",
                   "rglru_fused.hip"]
 BACKWARD_SOURCES = ["rglru_device.h", "rglru_mfma.h", "rglru_backward.hip", "rglru_bwd_tiles.hip",
-                    "rglru_gates.hip"]
+                    "rglru_bwd_fused.hip", "rglru_gates.hip"]
 # kernels of one rglru_backward call (name prefixes in rocprofv3 output)
-BACKWARD_KERNELS = ["tile_preacts", "gates_mfma<256, true>", "bwd_summary", "bwd_carry", "bwd_emit",
-                    "wt_prep", "tile_dxc", "dxc_mfma", "dxc_valu", "conv_bwd", "dw_mfma", "dw_valu",
-                    "colsum"]
+BACKWARD_KERNELS = ["tile_bwd", "tile_preacts", "gates_mfma<256, true>", "bwd_summary", "bwd_carry",
+                    "bwd_emit", "wt_prep", "tile_dxc", "dxc_mfma", "dxc_valu", "conv_bwd", "dw_mfma",
+                    "dw_valu", "colsum"]
 
 
 def is_backward_kernel(name: str) -> bool:

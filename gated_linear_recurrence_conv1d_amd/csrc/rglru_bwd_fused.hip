@@ -28,6 +28,8 @@
 // bitwise from run to run. Maps are published before any wait, so a tile's wait ends as soon as
 // the tiles after it have finished their first pass; it is bounded all the same (a lost word
 // gives NaN and bumps a counter, never a hang).
+#include <algorithm>
+
 #include "rglru_launch.h"
 #include "rglru_mfma.h"
 
@@ -131,6 +133,7 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     w23c = as_bf16x2(__builtin_amdgcn_perm(cw[3], cw[2], csel));
   }
   const float kd = decay_coeff(Lambda[dc]);
+
   // conv of staged rows q .. q+3 (time t - 3 .. t for tile row q), as pair words: both channels
   // of the pair, or channel c alone
   auto conv2 = [&](const uint32_t (&xv)[4], float &o0, float &o1) {
@@ -349,8 +352,9 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
         const float m = __builtin_amdgcn_sqrtf(-e * (2.0f + e));
         const float delta = bf16_to_f32(dyt[row * DH]) + gk;
         const float hp = t > 0 ? bf16_to_f32(yt[row * DH]) : hinit;
-        const float dm = delta * ig * xc;
-        const float di = delta * m * xc;
+        const float dx_ = delta * xc, dmg = delta * m;
+        const float dm = dx_ * ig;
+        const float di = dmg * xc;
         float dz = delta * hp * a;
         if (m > 0.0f) dz -= dm * (a * a) * __builtin_amdgcn_rcpf(m);
         const float dpa = kd * dz * (rr * (1.0f - rr));
@@ -363,7 +367,7 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
         const uint32_t hpk = pack_bf16x2(dpa, dpx);
         dpres[o] = hpk;
         dlos[o] = pack_bf16x2(dpa - bf16lo(hpk), dpx - bf16hi(hpk));
-        dxcs[o] = delta * m * ig;
+        dxcs[o] = dmg * ig;
       }
     }
     psum[(0 * F::kSeg + sg) * DH + c] = s_pa;
@@ -385,6 +389,16 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
   }
 }
 
+// Look-back words to the empty pattern and the control words (give-up count, tickets) to 0
+// before each launch.
+__global__ void tile_bwd_reset(unsigned long long *slots, size_t n, unsigned *ctrl, int nctrl) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    slots[i] = kEmpty;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nctrl; i += blockDim.x) ctrl[i] = 0u;
+}
+
 bool fused_backward_supported(int Dh) { return Dh == 128 || Dh == 256; }
 
 size_t fused_backward_slots(int B, int T, int D) {
@@ -399,8 +413,11 @@ hipError_t launch_fused_backward(const void *x, const void *y, const void *dy, c
                                  unsigned *ctrl, unsigned long long *slots, hipStream_t s) {
   const int nTT = (T + kRows - 1) / kRows;
   unsigned long long *agg = slots, *incl = slots + fused_backward_slots(B, T, D) / 2;
-  hipError_t e = launch_lookback_reset(slots, fused_backward_slots(B, T, D), ctrl, 2 + H, s);
-  if (e != hipSuccess) return e;
+  {
+    const size_t n = fused_backward_slots(B, T, D);
+    const unsigned blocks = static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 2048));
+    tile_bwd_reset<<<std::max(1u, blocks), 256, 0, s>>>(slots, n, ctrl, 2 + H);
+  }
   // one workgroup per CU (the LDS of a tile), the same number for every head
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess)

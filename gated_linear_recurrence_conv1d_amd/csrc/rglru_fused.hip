@@ -85,13 +85,6 @@ __global__ void fused_reset(unsigned long long *slots, size_t n, unsigned *ctrl,
     for (int i = threadIdx.x; i < nctrl; i += blockDim.x) ctrl[i] = 0u;
 }
 
-hipError_t launch_lookback_reset(unsigned long long *slots, size_t n, unsigned *ctrl, int nctrl,
-                                 hipStream_t s) {
-  const unsigned blocks = static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 2048));
-  fused_reset<<<std::max(1u, blocks), 256, 0, s>>>(slots, n, ctrl, nctrl);
-  return hipGetLastError();
-}
-
 struct TileCtx {
   int j, tt, b, t0;
 };

@@ -65,10 +65,6 @@ hipError_t launch_resident_preacts(const void *x, const void *conv_w, const void
 hipError_t launch_resident_dxc(const void *dp, const void *wti, float *dxc, int B, int T, int D,
                                int H, hipStream_t s);
 
-// Reset of a look-back area: n slots to the empty pattern and nctrl control words to 0.
-hipError_t launch_lookback_reset(unsigned long long *slots, size_t n, unsigned *ctrl, int nctrl,
-                                 hipStream_t s);
-
 // The backward's per-element part in one pass over kFusedBwdRows-step tiles, latest first (bf16, Dh in
 // {128, 256}, T * D * 4 < 2^31): pre-activations recomputed on MFMA, the adjoint carried from
 // tile to tile, and dpre / dlo / dxc / the per-tile partial sums / dh0 as the separate kernels
