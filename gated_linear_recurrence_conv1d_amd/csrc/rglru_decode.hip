@@ -8,12 +8,16 @@
 // Every element of conv_state, h and y_t belongs to exactly one workgroup, which reads it before
 // it writes it, so the in-place update needs no synchronisation beyond the workgroup's own.
 //
-//  * decode_mfma<DH>: bf16 I/O, DH in {32, 64, 128, 256}. A 32-row tile of one head: conv in fp32
-//    into LDS (fp32 copy for the gate math, bf16 copy as the MFMA A operand), the gate
-//    projections on v_mfma_f32_32x32x16_bf16 with the weights streamed from L2 two k-steps
-//    ahead, then the nonlinearity and state update straight from the accumulators. Every load
-//    that can be issued early is (the states it updates, all conv-state rows of a thread), since
-//    a decode step is one pass over memory with little compute to hide latency behind.
+//  * decode_mfma<DH>: bf16 I/O, DH in {32, 64}. A 32-row tile of one head: conv in fp32 into
+//    LDS (fp32 copy for the gate math, bf16 copy as the MFMA A operand), the gate projections on
+//    v_mfma_f32_32x32x16_bf16 with the weights streamed from L2 two k-steps ahead, then the
+//    nonlinearity and state update straight from the accumulators. Every load that can be issued
+//    early is (the states it updates, all conv-state rows of a thread), since a decode step is
+//    one pass over memory with little compute to hide latency behind.
+//  * decode_mfma64<DH>: bf16 I/O, DH in {128, 256}. The same on a 64-row tile, one wave per
+//    32-channel group covering both 32-row halves, so each weight fragment streamed from L2 feeds
+//    two MFMAs: the weights cross L2 once per 64 rows instead of per 32, which is what bounds the
+//    MFMA phase (every workgroup streams its head's 2 Dh^2 weights at the same time).
 //  * decode_valu<T>: any Dh <= 256, fp32 or bf16, one workgroup per (row, head).
 #include "rglru_launch.h"
 #include "rglru_mfma.h"
@@ -166,6 +170,132 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma(
   }
 }
 
+// 64-row tile of one head: Dh/32 waves, wave w owns channel group w (32 channels) for rows
+// 0..31 and 32..63 (accumulators [half][gate]); weights streamed from L2 kPF k-steps ahead.
+template <int DH>
+__global__ __launch_bounds__(2 * DH, 2) void decode_mfma64(
+    const bf16_t *__restrict__ x_t, bf16_t *__restrict__ cs, float *__restrict__ h,
+    bf16_t *__restrict__ y_t, const bf16_t *__restrict__ conv_w, const bf16_t *__restrict__ W_a,
+    const float *__restrict__ b_a, const bf16_t *__restrict__ W_x,
+    const float *__restrict__ b_x, const float *__restrict__ Lambda, int N, int D) {
+  static_assert(DH == 128 || DH == 256, "64-row decode tile needs Dh in {128, 256}");
+  constexpr int kRows = 64, kLda = DH + 8, kKS = DH / 16, kThr = 2 * DH, kPF = 4;
+  __shared__ __attribute__((aligned(16))) bf16_t lds_a[kRows * kLda];
+  __shared__ float lds_xc[kRows * DH];
+  const int n0 = blockIdx.x * kRows;
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int lrow = lane & 31;
+  const int khalf = (lane >> 5) * 8;
+  const int cl = w * 32 + lrow;  // this lane's channel within the head
+  const int d = g * DH + cl;
+  // tile row of accumulator j in this lane (v_mfma_f32_32x32x16_bf16 layout), half 0
+  auto acc_row = [&](int j) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); };
+
+  // The fp32 states this wave will update are loaded first: they do not depend on the conv.
+  float hv[2][16];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int n = min(n0 + rt * 32 + acc_row(j), N - 1);  // clamped; stores masked
+      hv[rt][j] = h[static_cast<size_t>(n) * D + d];
+    }
+
+  // Conv and conv-state shift: thread = (channel pair p, rows r0 .. r0+RPG-1); all loads are
+  // issued before any store (rows past N read row N-1 and store nothing).
+  {
+    constexpr int P = DH / 2;
+    constexpr int RPG = kRows * P / kThr;
+    const int p = tid % P;
+    const int r0 = (tid / P) * RPG;
+    const int d0 = g * DH + 2 * p;
+    float w0[4], w1[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t wv = *reinterpret_cast<const uint32_t *>(conv_w + static_cast<size_t>(j) * D + d0);
+      w0[j] = bf16lo(wv);
+      w1[j] = bf16hi(wv);
+    }
+    uint32_t c0[RPG], c1[RPG], c2[RPG], xv[RPG];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const int n = min(n0 + r0 + i, N - 1);
+      const uint32_t *c = reinterpret_cast<const uint32_t *>(cs + static_cast<size_t>(n) * 3 * D + d0);
+      c0[i] = c[0];
+      c1[i] = c[D / 2];
+      c2[i] = c[D];
+      xv[i] = *reinterpret_cast<const uint32_t *>(x_t + static_cast<size_t>(n) * D + d0);
+    }
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const int r = r0 + i;
+      const int n = n0 + r;
+      const float y0 = fmaf(w0[3], bf16lo(xv[i]),
+                            fmaf(w0[2], bf16lo(c2[i]), fmaf(w0[1], bf16lo(c1[i]), w0[0] * bf16lo(c0[i]))));
+      const float y1 = fmaf(w1[3], bf16hi(xv[i]),
+                            fmaf(w1[2], bf16hi(c2[i]), fmaf(w1[1], bf16hi(c1[i]), w1[0] * bf16hi(c0[i]))));
+      if (n < N) {
+        uint32_t *c = reinterpret_cast<uint32_t *>(cs + static_cast<size_t>(n) * 3 * D + d0);
+        c[0] = c1[i];
+        c[D / 2] = c2[i];
+        c[D] = xv[i];
+      }
+      *reinterpret_cast<uint32_t *>(lds_a + r * kLda + 2 * p) = pack_bf16x2(y0, y1);
+      lds_xc[r * DH + 2 * p] = y0;
+      lds_xc[r * DH + 2 * p + 1] = y1;
+    }
+  }
+  __syncthreads();
+
+  f32x16_t acc[2][2];  // [row half][gate]
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    acc[rt][0] = f32x16_t{};
+    acc[rt][1] = f32x16_t{};
+  }
+  const size_t wrow = (static_cast<size_t>(g) * DH + cl) * DH + khalf;  // B operand: W row cl
+  bf16x8_t bw[kPF][2];
+#pragma unroll
+  for (int i = 0; i < kPF && i < kKS; ++i) {
+    bw[i][0] = load_bf16x8(W_a + wrow + i * 16);
+    bw[i][1] = load_bf16x8(W_x + wrow + i * 16);
+  }
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const bf16x8_t af = load_bf16x8(lds_a + (rt * 32 + lrow) * kLda + ks * 16 + khalf);
+      acc[rt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bw[ks % kPF][0], acc[rt][0], 0, 0, 0);
+      acc[rt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bw[ks % kPF][1], acc[rt][1], 0, 0, 0);
+    }
+    if (ks + kPF < kKS) {
+      bw[ks % kPF][0] = load_bf16x8(W_a + wrow + (ks + kPF) * 16);
+      bw[ks % kPF][1] = load_bf16x8(W_x + wrow + (ks + kPF) * 16);
+    }
+  }
+
+  const float ba = b_a[d], bx = b_x[d];
+  const float kd = decay_coeff(Lambda[d]);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int row = rt * 32 + acc_row(j);
+      const int n = n0 + row;
+      if (n < N) {
+        float a, u;
+        gate(acc[rt][0][j] + ba, acc[rt][1][j] + bx, lds_xc[row * DH + cl], kd, a, u);
+        const size_t off = static_cast<size_t>(n) * D + d;
+        const float hn = fmaf(a, hv[rt][j], u);
+        h[off] = hn;
+        y_t[off] = f32_to_bf16(hn);
+      }
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void decode_valu(
     const T *__restrict__ x_t, T *__restrict__ cs, float *__restrict__ h, T *__restrict__ y_t,
@@ -267,7 +397,8 @@ hipError_t launch_decode(const void *x_t, void *conv_state, float *h, void *y_t,
                          hipStream_t s) {
   const int Dh = D / H;
   if (io == kBF16 && (Dh == 32 || Dh == 64 || Dh == 128 || Dh == 256)) {
-    dim3 grid((N + 31) / 32, H);  // DecodeTile<>::kRows rows per workgroup
+    dim3 grid((N + 31) / 32, H);    // DecodeTile<>::kRows rows per workgroup
+    dim3 grid64((N + 63) / 64, H);  // decode_mfma64: 64 rows per workgroup
     const bf16_t *xx = static_cast<const bf16_t *>(x_t);
     bf16_t *cc = static_cast<bf16_t *>(conv_state);
     bf16_t *yy = static_cast<bf16_t *>(y_t);
@@ -282,8 +413,12 @@ hipError_t launch_decode(const void *x_t, void *conv_state, float *h, void *y_t,
     switch (Dh) {
       RGLRU_DECODE_CASE(32)
       RGLRU_DECODE_CASE(64)
-      RGLRU_DECODE_CASE(128)
-      RGLRU_DECODE_CASE(256)
+      case 128:
+        decode_mfma64<128><<<grid64, 256, 0, s>>>(xx, cc, h, yy, cw, wa, b_a, wx, b_x, Lambda, N, D);
+        break;
+      case 256:
+        decode_mfma64<256><<<grid64, 512, 0, s>>>(xx, cc, h, yy, cw, wa, b_a, wx, b_x, Lambda, N, D);
+        break;
       default: return hipErrorInvalidValue;
     }
 #undef RGLRU_DECODE_CASE

@@ -274,7 +274,8 @@ def decode_inputs(N, T, D, H, seed=0):
     return inp, to_device(inp)
 
 
-@pytest.mark.parametrize("N,D,H", [(70, 512, 2), (5, 256, 4), (3, 96, 2), (64, 128, 4)])
+@pytest.mark.parametrize("N,D,H", [(70, 512, 2), (100, 512, 4), (5, 256, 4), (3, 96, 2),
+                                   (64, 128, 4)])
 def test_decode_steps_match_oracle(N, D, H):
     """Several in-place steps: y_t and h within the bf16 bound, conv_state bit-exact."""
     inp, g = decode_inputs(N, 5, D, H)
