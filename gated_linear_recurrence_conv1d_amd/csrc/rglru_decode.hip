@@ -191,6 +191,8 @@ __global__ __launch_bounds__(2 * DH, 2) void decode_mfma64(
   const int khalf = (lane >> 5) * 8;
   const int cl = w * 32 + lrow;  // this lane's channel within the head
   const int d = g * DH + cl;
+  const float ba = b_a[d], bx = b_x[d];  // (loaded ahead of every store)
+  const float kd = decay_coeff(Lambda[d]);
   // tile row of accumulator j in this lane (v_mfma_f32_32x32x16_bf16 layout), half 0
   auto acc_row = [&](int j) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); };
 
@@ -204,14 +206,16 @@ __global__ __launch_bounds__(2 * DH, 2) void decode_mfma64(
       hv[rt][j] = h[static_cast<size_t>(n) * D + d];
     }
 
-  // Conv and conv-state shift: thread = (channel pair p, rows r0 .. r0+RPG-1); all loads are
-  // issued before any store (rows past N read row N-1 and store nothing).
+  // Conv: thread = (channel pair p, rows r0 .. r0+RPG-1). The shifted conv state is stored only
+  // after the MFMAs: vector memory operations complete in issue order, so stores issued here
+  // would make every wait for a weight fragment in the MFMA loop wait for them as well.
+  constexpr int P = DH / 2;
+  constexpr int RPG = kRows * P / kThr;
+  const int p = tid % P;
+  const int r0 = (tid / P) * RPG;
+  const int d0 = g * DH + 2 * p;
+  uint32_t c1[RPG], c2[RPG], xv[RPG];
   {
-    constexpr int P = DH / 2;
-    constexpr int RPG = kRows * P / kThr;
-    const int p = tid % P;
-    const int r0 = (tid / P) * RPG;
-    const int d0 = g * DH + 2 * p;
     float w0[4], w1[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(2 * DH, 2) void decode_mfma64(
       w0[j] = bf16lo(wv);
       w1[j] = bf16hi(wv);
     }
-    uint32_t c0[RPG], c1[RPG], c2[RPG], xv[RPG];
+    uint32_t c0[RPG];
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
       const int n = min(n0 + r0 + i, N - 1);
@@ -232,17 +236,10 @@ __global__ __launch_bounds__(2 * DH, 2) void decode_mfma64(
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
       const int r = r0 + i;
-      const int n = n0 + r;
       const float y0 = fmaf(w0[3], bf16lo(xv[i]),
                             fmaf(w0[2], bf16lo(c2[i]), fmaf(w0[1], bf16lo(c1[i]), w0[0] * bf16lo(c0[i]))));
       const float y1 = fmaf(w1[3], bf16hi(xv[i]),
                             fmaf(w1[2], bf16hi(c2[i]), fmaf(w1[1], bf16hi(c1[i]), w1[0] * bf16hi(c0[i]))));
-      if (n < N) {
-        uint32_t *c = reinterpret_cast<uint32_t *>(cs + static_cast<size_t>(n) * 3 * D + d0);
-        c[0] = c1[i];
-        c[D / 2] = c2[i];
-        c[D] = xv[i];
-      }
       *reinterpret_cast<uint32_t *>(lds_a + r * kLda + 2 * p) = pack_bf16x2(y0, y1);
       lds_xc[r * DH + 2 * p] = y0;
       lds_xc[r * DH + 2 * p + 1] = y1;
@@ -277,8 +274,17 @@ __global__ __launch_bounds__(2 * DH, 2) void decode_mfma64(
     }
   }
 
-  const float ba = b_a[d], bx = b_x[d];
-  const float kd = decay_coeff(Lambda[d]);
+  // conv-state shift (rows past N store nothing)
+#pragma unroll
+  for (int i = 0; i < RPG; ++i) {
+    const int n = n0 + r0 + i;
+    if (n < N) {
+      uint32_t *c = reinterpret_cast<uint32_t *>(cs + static_cast<size_t>(n) * 3 * D + d0);
+      c[0] = c1[i];
+      c[D / 2] = c2[i];
+      c[D] = xv[i];
+    }
+  }
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
