@@ -36,7 +36,6 @@
 namespace rglru {
 
 namespace {
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr int kRawWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit data, no swizzle
 constexpr uint32_t kLoPair = 0x05040100u, kHiPair = 0x07060302u;  // low / high 16-bit halves
@@ -175,18 +174,15 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     for (int i = w; i < F::kLoads; i += F::kNW) {  // wave-uniform
       if (i < F::kXLoads) {
         const unsigned row_off = static_cast<unsigned>((t0 - 3 + i * F::kRowsPerLoad) * 2 * D);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            sx, (lds_void_t *)(xr[bf] + i * F::kRowsPerLoad * DH), 16, row_off + lane_off, 0, 0, 0);
+        dma_16b(sx, row_off + lane_off, lds_addr(xr[bf] + i * F::kRowsPerLoad * DH));
       } else if (i < F::kXLoads + F::kRLoads) {
         const int q = i - F::kXLoads;
         const unsigned row_off = static_cast<unsigned>((t0 + q * F::kRowsPerLoad) * 2 * D);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            sdy, (lds_void_t *)(dyr[bf] + q * F::kRowsPerLoad * DH), 16, row_off + lane_off, 0, 0, 0);
+        dma_16b(sdy, row_off + lane_off, lds_addr(dyr[bf] + q * F::kRowsPerLoad * DH));
       } else {
         const int q = i - F::kXLoads - F::kRLoads;
         const unsigned row_off = static_cast<unsigned>((t0 - 1 + q * F::kRowsPerLoad) * 2 * D);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            sy, (lds_void_t *)(yr[bf] + q * F::kRowsPerLoad * DH), 16, row_off + lane_off, 0, 0, 0);
+        dma_16b(sy, row_off + lane_off, lds_addr(yr[bf] + q * F::kRowsPerLoad * DH));
       }
     }
   };
@@ -198,12 +194,20 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     if (j0 < ntiles) stage(j0, 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): own staging loads landed
   }
+  // Barriers inside the loop order LDS only (lds_barrier): the staging loads are waited for
+  // explicitly (vmcnt(0) in pass 2, before the next tile's first barrier), and no global memory
+  // is exchanged between the waves, so no barrier needs to wait for the y stores or the staging
+  // loads in flight.
   int cur = 0;
   for (;;) {
-    __syncthreads();  // this tile's rows staged; the previous tile's LDS reads done
+    lds_barrier();  // this tile's rows staged; the previous tile's LDS reads done
     const int j = __builtin_amdgcn_readfirstlane(s_tile[cur]);
     if (j >= ntiles) break;
-    if (tid == 0) s_tile[cur ^ 1] = static_cast<int>(atomicAdd(ticket, 1u));
+    // The next ticket: its round trip overlaps the conv; written to LDS after it (vector memory
+    // completes in issue order, so waiting for the ticket also waits for the previous tile's
+    // gradient stores: the later the wait, the less of it is left).
+    unsigned claim = 0;
+    if (tid == 0) claim = atomicAdd(ticket, 1u);
     const int b = j % B, tt = nTT - 1 - j / B, t0 = tt * kRows;
     const bf16_t *xs = xr[cur];
     // ---- conv -> hi / lo bf16
@@ -220,7 +224,8 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
       *reinterpret_cast<uint32_t *>(xa + (kRows + row) * F::kLda + 2 * cp) =
           pack_bf16x2(o0 - bf16lo(hv), o1 - bf16hi(hv));
     }
-    __syncthreads();  // xa ready; the next ticket visible
+    if (tid == 0) s_tile[cur ^ 1] = static_cast<int>(claim);
+    lds_barrier();  // xa ready; the next ticket visible
     {
       const int jn = __builtin_amdgcn_readfirstlane(s_tile[cur ^ 1]);
       if (jn < ntiles) stage(jn, cur ^ 1);  // its last readers finished before the loop top
@@ -236,14 +241,14 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
         acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wa[ks], acc[0], 0, 0, 0);
         acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wx[ks], acc[1], 0, 0, 0);
       }
-    __syncthreads();  // every wave is done with xa
+    lds_barrier();  // every wave is done with xa
     // ---- pre-activations (with the biases) as fp16 pairs over the conv tile: row r, channel cl
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
       const int r = 8 * (jj >> 2) + 4 * half + (jj & 3);
       preL[r * DH + cl] = pack_f16x2(acc[0][jj] + ba, acc[1][jj] + bx);
     }
-    __syncthreads();  // pre ready
+    lds_barrier();  // pre ready
     // ---- lane phase, pass 1: this segment's map g_start = A g_end + U, walking it backward.
     // Rows at or past T (only in the last tile) are the identity (a = 1, dy = 0).
     const bf16_t *dyt = dyr[cur] + c;  // row r: dy at t0 + r
@@ -259,7 +264,7 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
       A *= a;
     }
     sc[sg * DH + c] = make_float2(A, U);
-    __syncthreads();  // segment maps ready
+    lds_barrier();  // segment maps ready
     // ---- the tile's map, g at its end from the next tile in time, g at its start published
     if (sg == 0) {
       float At = 1.0f, Ut = 0.0f;
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
         dh0[bd] = gstart;
       gin[c] = gend;
     }
-    __syncthreads();  // g at the tile's end ready
+    lds_barrier();  // g at the tile's end ready
     // ---- pass 2: from g at this segment's end, backward over its rows: gradients and sums
     float gk = gin[c];
     for (int s = F::kSeg - 1; s > sg; --s) {
@@ -373,7 +378,7 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     psum[(0 * F::kSeg + sg) * DH + c] = s_pa;
     psum[(1 * F::kSeg + sg) * DH + c] = s_px;
     psum[(2 * F::kSeg + sg) * DH + c] = s_rdz;
-    __syncthreads();  // partial sums ready
+    lds_barrier();  // partial sums ready
     if (sg == 0) {
       const size_t PD = static_cast<size_t>(B) * nTT * D;
       const size_t pidx = (static_cast<size_t>(b) * nTT + tt) * D + dc;

@@ -121,6 +121,39 @@ __device__ __forceinline__ void st_relaxed(unsigned long long *p, unsigned long 
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// One 16-byte-per-lane buffer load straight into LDS (the wave's 64 lanes fill 1 KB from byte
+// lds_base on), written as inline asm: for the builtin form the compiler cannot tell which LDS
+// bytes the load writes, so it makes later LDS reads -- and every __syncthreads -- wait for all of
+// the wave's outstanding vector memory operations. Kernels that use it order the loads
+// themselves (s_waitcnt vmcnt, then a barrier, before any wave reads the rows; a barrier before
+// a buffer is refilled). M0 (the LDS base) is restored afterwards.
+__device__ __forceinline__ void dma_16b(__amdgpu_buffer_rsrc_t rsrc, unsigned voff,
+                                        unsigned lds_base) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(lds_base), "s"(rsrc));
+}
+
+// LDS byte address of a __shared__ pointer (the low half of its generic address), wave-uniform.
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>(p)));
+}
+
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads it does not wait for the
+// wave's outstanding vector memory loads and stores, so they stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Per-channel constant kd = -c * softplus(-Lambda), so that log a = kd * r. softplus is taken
 // as max(z,0) + log1p(exp(-|z|)); computed once per lane with the accurate library functions.
 __device__ __forceinline__ float decay_coeff(float lambda) {

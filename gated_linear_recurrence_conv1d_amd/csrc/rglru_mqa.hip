@@ -48,32 +48,6 @@ namespace {
 constexpr int kRawWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit data, no swizzle
 constexpr unsigned kNoRows = 0x7F000000u;  // a byte offset past every sequence's K and V
 
-// One 16-byte-per-lane buffer load straight into LDS (the wave's 64 lanes fill 1 KB from byte
-// lds_base on), written as inline asm: for the builtin form the compiler cannot tell which LDS
-// bytes the load writes and makes every later LDS read wait for it. The kernel orders these
-// loads itself (s_waitcnt vmcnt, then a barrier, before any wave reads the rows; a barrier before
-// a buffer is refilled). M0 (the LDS base) is restored afterwards.
-__device__ __forceinline__ void dma_16b(__amdgpu_buffer_rsrc_t rsrc, unsigned voff,
-                                        unsigned lds_base) {
-  unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
-      "s_nop 0\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(lds_base), "s"(rsrc));
-}
-
-// Workgroup barrier that orders LDS accesses only: unlike __syncthreads it does not wait for the
-// wave's outstanding vector memory loads, so LDS loads of a later block stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 }  // namespace
 
 template <int DH> struct Mqa {
