@@ -13,9 +13,11 @@
 // Both: one workgroup owns one head for its whole life and takes that head's 64-row tiles
 // (time-major within a sequence, sequences in turn) in a static round robin; wave w owns the
 // head's output channels in groups of 32 (two groups per wave at Dh = 256, one wave per SIMD)
-// and keeps their weight rows -- the MFMA B operand, 256 registers at Dh = 256 -- in registers. The rows of tile k+1 are copied to LDS with direct
-// buffer-to-LDS loads while tile k is in the MFMAs, so the tile loop waits on HBM only when a
-// tile's compute is shorter than its loads.
+// and keeps their weight rows -- the MFMA B operand, 256 registers at Dh = 256 -- in registers.
+// The rows of tile k+1 are copied to LDS with direct buffer-to-LDS loads while tile k is in the
+// MFMAs, so the tile loop waits on HBM only when a tile's compute is shorter than its loads.
+// Vector memory operations complete in issue order, so each tile waits for its loads before
+// issuing its stores, and the barriers order LDS only: no wait ever covers a tile's stores.
 #include "rglru_launch.h"
 #include "rglru_mfma.h"
 
@@ -23,7 +25,6 @@ namespace rglru {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr int kWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit data, no swizzle
 constexpr uint32_t kLoPair = 0x05040100u, kHiPair = 0x07060302u;  // low / high halves
@@ -109,15 +110,16 @@ __global__ __launch_bounds__(PreTile<DH>::kThreads, 2) void tile_preacts(
         kWord3);
     for (int i = w; i < F::kLoads; i += F::kNW) {
       const unsigned row_off = static_cast<unsigned>((t0 - 3 + i * F::kRowsPerLoad) * 2 * D);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(seq, (lds_void *)(xr + i * F::kRowsPerLoad * DH), 16,
-                                               row_off + lane_off, 0, 0, 0);
+      dma_16b(seq, row_off + lane_off, lds_addr(xr + i * F::kRowsPerLoad * DH));
     }
   };
   int j = blockIdx.x / H;
   if (j < ntiles) stage(j);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): own staging loads landed
+  // The barriers order LDS only: the staging loads are waited for explicitly (before the
+  // stores), so no barrier waits for the previous tile's stores.
   for (; j < ntiles; j += per) {
-    __syncthreads();  // staged rows visible; xa free
+    lds_barrier();  // staged rows visible; xa free
     // ---- conv (fp32 dot products of bf16 pairs) -> hi / lo bf16
 #pragma unroll 4
     for (int r = 0; r < PRPG; ++r) {
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(PreTile<DH>::kThreads, 2) void tile_preacts(
       *reinterpret_cast<uint32_t *>(xa + (kRows + row) * F::kLda + 2 * pc) =
           pack_bf16x2(o0 - bf16lo(hv), o1 - bf16hi(hv));
     }
-    __syncthreads();  // xa ready; xr free
+    lds_barrier();  // xa ready; xr free
     const int jn = j + per;
     if (jn < ntiles) stage(jn);
     // ---- [64 x DH] x [DH x 2 DH]: A = hi + lo
@@ -195,7 +197,11 @@ __global__ __launch_bounds__(PreTile<DH>::kThreads, 2) void tile_preacts(
 // dxc[b][t][g*DH + i] += sum_k dp[b][t][g*DH .. as 2 DH bf16][k] wti[g][i][k] for the tiles of
 // head g, as above. dp rows (bf16 pairs, dpa low) are staged one row per load instruction into
 // rows padded by 16 bytes, so the A-operand reads of 32 rows fall on distinct banks; two tile
-// buffers, tile k+1 loading while tile k is in the MFMAs.
+// buffers, tile k+1 loading while tile k is in the MFMAs. Per tile: [barrier] stage tile k+1,
+// load the dxc values to update, MFMAs, one wait (vmcnt(0): staging and dxc loads), stores.
+// Vector memory completes in issue order, so the wait sits before this tile's stores -- a wait
+// after them (or a __syncthreads, which waits for every outstanding operation) would take their
+// whole round trip on every tile -- and the barrier orders LDS only.
 template <int DH> struct DxcTile {
   static_assert(DH == 128 || DH == 256, "resident dxc tile needs Dh in {128, 256}");
   static constexpr int kGPW = 1;          // 32-channel groups per wave
@@ -239,8 +245,7 @@ __global__ __launch_bounds__(DxcTile<DH>::kThreads, 2) void tile_dxc(
     if (slane) {
       for (int r = w; r < kRows; r += F::kNW) {
         const unsigned off = static_cast<unsigned>(((t0 + r) * D + g * DH) * 4 + lane * 16);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            seq, (lds_void *)(la + (buf * kRows + r) * F::kLd), 16, off, 0, 0, 0);
+        dma_16b(seq, off, lds_addr(la + (buf * kRows + r) * F::kLd));
       }
     }
   };
@@ -250,9 +255,11 @@ __global__ __launch_bounds__(DxcTile<DH>::kThreads, 2) void tile_dxc(
   for (int it = 0; j < ntiles; j += per, ++it) {
     // this tile's rows are in buffer it & 1; the other buffer's readers (the previous tile's
     // MFMAs) are past this barrier
-    __syncthreads();
-    // the dxc values this lane updates, loaded first (they do not depend on the MFMAs and land
-    // while they run), then the next tile's rows
+    lds_barrier();
+    // the next tile's rows, then the dxc values this lane updates (neither depends on the MFMAs;
+    // both land while they run)
+    const int jn = j + per;
+    if (jn < ntiles) stage(jn, (it + 1) & 1);
     const int b = j % B, t0 = (j / B) * kRows;
     unsigned Dv = static_cast<unsigned>(D);
     asm volatile("" : "+s"(Dv));
@@ -272,8 +279,6 @@ __global__ __launch_bounds__(DxcTile<DH>::kThreads, 2) void tile_dxc(
           const int r = rt * 32 + 8 * (jj >> 2) + (jj & 3);
           old[gi][rt][jj] = (full || t0 + r + 4 * half < T) ? *at(gi, r) : 0.0f;
         }
-    const int jn = j + per;
-    if (jn < ntiles) stage(jn, (it + 1) & 1);
     const bf16_t *lt = la + (it & 1) * kRows * F::kLd;
     f32x16_t acc[F::kGPW][2];
 #pragma unroll
@@ -287,6 +292,7 @@ __global__ __launch_bounds__(DxcTile<DH>::kThreads, 2) void tile_dxc(
         for (int gi = 0; gi < F::kGPW; ++gi)
           acc[gi][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wr[gi][ks], acc[gi][rt], 0, 0, 0);
       }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile's staging and the dxc values
 #pragma unroll
     for (int gi = 0; gi < F::kGPW; ++gi)
 #pragma unroll
@@ -296,7 +302,6 @@ __global__ __launch_bounds__(DxcTile<DH>::kThreads, 2) void tile_dxc(
           const int r = rt * 32 + 8 * (jj >> 2) + (jj & 3);
           if (full || t0 + r + 4 * half < T) *at(gi, r) = old[gi][rt][jj] + acc[gi][rt][jj];
         }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // next tile's staging landed
   }
 }
 
