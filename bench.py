@@ -385,7 +385,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards over batch and heads without communication; see DESIGN.md)",
+              "(the path shards over batch and heads without communication)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -436,7 +436,7 @@ def main():
     state_bytes = (8 if g["h0"] is not None else 4) * B * D  # h0 (if any) in, h_T out
     kernels = {}
     if plan == "fused":
-        # one launch does the whole path: x in, y out, parameters, state (Measurement)
+        # one launch does the whole path: x in, y out, parameters, state
         kernels["fused"] = {"ms": ms, "bytes": n * 2 * eb + param_bytes + state_bytes,
                             "note": "events bracket the look-back reset and the fused kernel"}
 
