@@ -106,6 +106,7 @@ def test_tiny_fp32_config(plan, chunk):
     ("bf16", 2, 300, 512, 2, "chunked", 64),
     ("bf16", 2, 300, 512, 2, "fused", 0),
     ("bf16", 3, 129, 256, 4, "fused", 0),       # Dh = 64, ragged last tile
+    ("bf16", 2, 150, 512, 4, "fused", 0),       # Dh = 128, ragged last tile
     ("bf16", 2, 1000, 256, 2, "fused", 0),      # Dh = 128, 16 tiles per sequence
     ("bf16", 1, 640, 64, 2, "fused", 0),        # Dh = 32, exact multiple of the tile
     ("bf16", 4, 63, 512, 2, "fused", 0),        # a single partial tile
