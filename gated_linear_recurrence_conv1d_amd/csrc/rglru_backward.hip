@@ -1019,9 +1019,7 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
     // pre-activations recomputed with the conv output split into bf16 hi + lo: the gradients
     // amplify pre-activation errors (through r (1 - r) and 1/m), so the backward does not reuse
     // the forward's bf16-operand rounding
-    e = resident && resident_preacts_supported(Dh)
-            ? launch_resident_preacts(x, conv_w, W_a, b_a, W_x, b_x, pre, B, Tn, D, H, s)
-            : launch_gates(x, conv_w, W_a, b_a, W_x, b_x, pre, B, Tn, D, H, io, s, true);
+    e = launch_gates(x, conv_w, W_a, b_a, W_x, b_x, pre, B, Tn, D, H, io, s, true);
     if (e != hipSuccess) return e;
     if (pair) {
       bwd_summary<T, 2><<<lgrid, kBwdThreads, 0, s>>>(pre, dy, Lambda, sums, B, Tn, D, L.nC);

@@ -46,8 +46,10 @@ template <int DH> struct PreTile {
 };
 
 // pre[b][t][g*DH + o] = fp16 pair (pa, px) for the tiles j = blockIdx.x / H, + per, ... of head
-// g = blockIdx.x % H (tile j: sequence j % B, rows (j / B) * 64 ...).
-template <int DH>
+// g = blockIdx.x % H (tile j: sequence j % B, rows (j / B) * 64 ...). SPLIT: the conv output
+// enters as bf16 hi + lo (the backward's recompute); otherwise as one bf16 operand, the rounding
+// of the forward plans.
+template <int DH, bool SPLIT>
 __global__ __launch_bounds__(PreTile<DH>::kThreads, 2) void tile_preacts(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ conv_w,
     const bf16_t *__restrict__ W_a, const float *__restrict__ b_a,
@@ -55,7 +57,8 @@ __global__ __launch_bounds__(PreTile<DH>::kThreads, 2) void tile_preacts(
     int B, int T, int D, int H, int per) {
   typedef PreTile<DH> F;
   constexpr int PP = DH / 2;
-  __shared__ __attribute__((aligned(16))) bf16_t xa[2 * kRows * F::kLda];  // [hi, lo] conv output
+  constexpr int kParts = SPLIT ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) bf16_t xa[kParts * kRows * F::kLda];  // [hi, lo] conv out
   __shared__ __attribute__((aligned(16))) bf16_t xr[F::kXRows * DH];       // staged x rows
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -139,13 +142,14 @@ __global__ __launch_bounds__(PreTile<DH>::kThreads, 2) void tile_preacts(
           false);
       const uint32_t hv = pack_bf16x2(o0, o1);
       *reinterpret_cast<uint32_t *>(xa + row * F::kLda + 2 * pc) = hv;
-      *reinterpret_cast<uint32_t *>(xa + (kRows + row) * F::kLda + 2 * pc) =
-          pack_bf16x2(o0 - bf16lo(hv), o1 - bf16hi(hv));
+      if constexpr (SPLIT)
+        *reinterpret_cast<uint32_t *>(xa + (kRows + row) * F::kLda + 2 * pc) =
+            pack_bf16x2(o0 - bf16lo(hv), o1 - bf16hi(hv));
     }
     lds_barrier();  // xa ready; xr free
     const int jn = j + per;
     if (jn < ntiles) stage(jn);
-    // ---- [64 x DH] x [DH x 2 DH]: A = hi + lo
+    // ---- [64 x DH] x [DH x 2 DH]: A = hi (+ lo)
     f32x16_t acc[F::kGPW][2][2];  // [group][row tile][gate]
 #pragma unroll
     for (int gi = 0; gi < F::kGPW; ++gi)
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(PreTile<DH>::kThreads, 2) void tile_preacts(
 #pragma unroll
     for (int ks = 0; ks < F::kKS; ++ks)
 #pragma unroll
-      for (int part = 0; part < 2; ++part)
+      for (int part = 0; part < kParts; ++part)
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
           const bf16x8_t af =
@@ -320,7 +324,8 @@ bool resident_dxc_supported(int Dh) { return Dh == 128 || Dh == 256; }
 
 hipError_t launch_resident_preacts(const void *x, const void *conv_w, const void *W_a,
                                    const float *b_a, const void *W_x, const float *b_x,
-                                   void *pre, int B, int T, int D, int H, hipStream_t s) {
+                                   void *pre, int B, int T, int D, int H, hipStream_t s,
+                                   bool split) {
   // one workgroup per CU (the LDS of a tile), the same number for every head
   const int per = std::max(1, cu_count() / H);
   const bf16_t *xx = static_cast<const bf16_t *>(x);
@@ -331,8 +336,12 @@ hipError_t launch_resident_preacts(const void *x, const void *conv_w, const void
   switch (D / H) {
 #define RGLRU_PRE_CASE(DHV)                                                                       \
   case DHV:                                                                                       \
-    tile_preacts<DHV><<<H * per, PreTile<DHV>::kThreads, 0, s>>>(xx, cw, wa, b_a, wx, b_x, pp, B, \
-                                                                 T, D, H, per);                   \
+    if (split)                                                                                    \
+      tile_preacts<DHV, true><<<H * per, PreTile<DHV>::kThreads, 0, s>>>(xx, cw, wa, b_a, wx, b_x, \
+                                                                         pp, B, T, D, H, per);    \
+    else                                                                                          \
+      tile_preacts<DHV, false><<<H * per, PreTile<DHV>::kThreads, 0, s>>>(                        \
+          xx, cw, wa, b_a, wx, b_x, pp, B, T, D, H, per);                                         \
     break;
     RGLRU_PRE_CASE(32)
     RGLRU_PRE_CASE(64)

@@ -5,10 +5,12 @@
 // recurrent block simple; the gates are state-free, alby13 blog, "Core Components of Griffin --
 // 1. RG-LRU", which is what lets them run as one batched contraction ahead of the scan).
 //
-// Two kernels:
+// bf16 I/O with Dh in {32, 64, 128, 256} goes to tile_preacts (rglru_bwd_tiles.hip: persistent
+// workgroups, one head each, weights resident in registers) whenever one sequence fits 32-bit
+// buffer offsets; otherwise to one of two kernels here:
 //  * gates_mfma<DH>: bf16 I/O, DH in {32, 64, 128, 256}. Conv in fp32 into an LDS tile (rounded
 //    to bf16 for the MFMA A operand), then the 64 x 2DH tile on v_mfma_f32_32x32x16_bf16 with
-//    fp32 accumulation; fp16 (pa, px) pairs out.
+//    fp32 accumulation, the weights streamed from L2 per tile; fp16 (pa, px) pairs out.
 //  * gates_valu<T>: any Dh <= 256, fp32 or bf16 I/O, plain fp32 FMAs (used for fp32 I/O, where
 //    the 1e-4 accuracy target leaves no room for bf16 operands, and for odd head sizes).
 #include "rglru_launch.h"
@@ -150,6 +152,9 @@ hipError_t launch_gates(const void *x, const void *conv_w, const void *W_a, cons
                         const void *W_x, const float *b_x, void *pre, int B, int T, int D, int H,
                         int io, hipStream_t s, bool split) {
   const int Dh = D / H;
+  if (io == kBF16 && resident_preacts_supported(Dh) &&
+      static_cast<long long>(T) * D * 4 < (1LL << 31))
+    return launch_resident_preacts(x, conv_w, W_a, b_a, W_x, b_x, pre, B, T, D, H, s, split);
   if (io == kBF16 && (Dh == 32 || Dh == 64 || Dh == 128 || Dh == 256)) {
     dim3 grid((T + kTileRows - 1) / kTileRows, H, B);
     const bf16_t *xx = static_cast<const bf16_t *>(x);

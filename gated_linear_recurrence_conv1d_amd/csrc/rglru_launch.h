@@ -53,15 +53,17 @@ hipError_t launch_fused(const void *x, const void *conv_w, const void *W_a, cons
                         void *y, float *h_T, int B, int T, int D, int H, void *ctrl_ws,
                         hipStream_t s);
 
-// The backward's weight contractions as persistent workgroups with resident weights (bf16):
-// gate pre-activations with the conv output split into bf16 hi + lo (Dh in {32, 64, 128, 256}),
-// and dxc += dp [W_a ; W_x] from the interleaved transposed weights wti (Dh in {128, 256}).
+// The weight contractions as persistent workgroups with resident weights (bf16): gate
+// pre-activations (Dh in {32, 64, 128, 256}; split: the conv output as bf16 hi + lo, as the
+// backward recomputes them, else as bf16, as the forward plans round it), and the backward's
+// dxc += dp [W_a ; W_x] from the interleaved transposed weights wti (Dh in {128, 256}).
 // Both need T * D * 4 < 2^31 (32-bit buffer offsets within one sequence).
 bool resident_preacts_supported(int Dh);
 bool resident_dxc_supported(int Dh);
 hipError_t launch_resident_preacts(const void *x, const void *conv_w, const void *W_a,
                                    const float *b_a, const void *W_x, const float *b_x,
-                                   void *pre, int B, int T, int D, int H, hipStream_t s);
+                                   void *pre, int B, int T, int D, int H, hipStream_t s,
+                                   bool split);
 hipError_t launch_resident_dxc(const void *dp, const void *wti, float *dxc, int B, int T, int D,
                                int H, hipStream_t s);
 
