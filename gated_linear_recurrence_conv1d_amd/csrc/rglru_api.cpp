@@ -15,9 +15,13 @@ using rglru::kBF16;
 using rglru::kF32;
 
 constexpr size_t kAlign = 256;         // workspace carve alignment
+// The scan lanes wait on HBM latency, so the chunked plan wants many lanes in flight: chunks of
+// about 64 steps (measured best from 2 to 32 sequences of 2560 channels), shorter when that
+// still leaves fewer than ~8 waves per SIMD; the direct plan once B * D alone gives 2 waves.
 constexpr int kMinChunk = 16;          // smallest chunk the size query provisions for
-constexpr long long kTargetLanes = 2LL * 64 * 1024;  // ~2 waves per SIMD on 256 CUs x 4 SIMDs
-constexpr long long kDirectLanes = 64LL * 1024;      // >= 1 wave per SIMD: scan every channel whole
+constexpr int kMaxAutoChunk = 64;      // longest chunk the automatic plan picks
+constexpr long long kTargetLanes = 8LL * 64 * 1024;  // ~8 waves per SIMD on 256 CUs x 4 SIMDs
+constexpr long long kDirectLanes = 128LL * 1024;     // >= 2 waves per SIMD: scan channels whole
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -47,7 +51,7 @@ int auto_chunk(int B, int T, int D) {
   if (lanes >= kDirectLanes) return T;
   const long long want = (kTargetLanes + lanes - 1) / lanes;
   long long L = (T + want - 1) / want;
-  L = std::max<long long>(L, kMinChunk);
+  L = std::max<long long>(std::min<long long>(L, kMaxAutoChunk), kMinChunk);
   return L >= T ? T : static_cast<int>(L);
 }
 

@@ -56,14 +56,20 @@ def test_auto_plan_choices():
     assert rg.rglru_forward_plan_info(8, 2048, 2560, 10, "bf16") == ("fused", 64)
     assert rg.rglru_forward_plan_info(1, 65536, 2560, 10, "bf16") == ("fused", 64)
     # otherwise the split plans, chosen by how many channels there are to spread over lanes
-    assert rg.rglru_forward_plan_info(16, 4096, 4800, 100, "bf16") == ("direct", 4096)  # Dh 48
+    # (direct from B * D >= 128K lanes; chunks of at most 64 steps, shorter while the chunked
+    # lanes B * D * n_chunks stay below 512K)
+    assert rg.rglru_forward_plan_info(32, 4096, 4800, 100, "bf16") == ("direct", 4096)  # Dh 48
+    assert rg.rglru_forward_plan_info(16, 4096, 4800, 100, "bf16") == ("chunked", 64)
     plan, L = rg.rglru_forward_plan_info(8, 2048, 2400, 50, "bf16")
-    assert plan == "chunked" and 16 <= L < 2048
-    assert (8 * 2400) * ((2048 + L - 1) // L) >= 2 * 65536
+    assert plan == "chunked" and 16 <= L <= 64
+    assert (8 * 2400) * ((2048 + L - 1) // L) >= 8 * 65536
     plan, L = rg.rglru_forward_plan_info(1, 256, 256, 16, "f32")
     assert plan == "chunked" and L == 16
+    plan, L = rg.rglru_forward_plan_info(1, 4096, 2560, 10, "f32")
+    assert plan == "chunked" and 16 <= L < 64 and 2560 * ((4096 + L - 1) // L) >= 8 * 65536
     assert rg.rglru_forward_plan_info(1, 10, 256, 16, "f32") == ("direct", 10)
-    assert rg.rglru_forward_plan_info(16, 4096, 4096, 16, "f32") == ("direct", 4096)
+    assert rg.rglru_forward_plan_info(32, 4096, 4096, 16, "f32") == ("direct", 4096)
+    assert rg.rglru_forward_plan_info(16, 4096, 4096, 16, "f32") == ("chunked", 64)
 
 
 FAKE = 0x10000  # never dereferenced: every call below fails its checks before any launch
