@@ -7,12 +7,13 @@
 //
 // bf16 I/O with Dh in {32, 64, 128, 256} goes to tile_preacts (rglru_bwd_tiles.hip: persistent
 // workgroups, one head each, weights resident in registers) whenever one sequence fits 32-bit
-// buffer offsets; otherwise to one of two kernels here:
+// buffer offsets; otherwise to one of the kernels here:
 //  * gates_mfma<DH>: bf16 I/O, DH in {32, 64, 128, 256}. Conv in fp32 into an LDS tile (rounded
 //    to bf16 for the MFMA A operand), then the 64 x 2DH tile on v_mfma_f32_32x32x16_bf16 with
 //    fp32 accumulation, the weights streamed from L2 per tile; fp16 (pa, px) pairs out.
-//  * gates_valu<T>: any Dh <= 256, fp32 or bf16 I/O, plain fp32 FMAs (used for fp32 I/O, where
-//    the 1e-4 accuracy target leaves no room for bf16 operands, and for odd head sizes).
+//  * gates_tiled<T> (Dh % 4 == 0) and gates_valu<T> (any Dh <= 256): fp32 or bf16 I/O, plain
+//    fp32 FMAs (used for fp32 I/O, where the 1e-4 accuracy target leaves no room for bf16
+//    operands, and for other head sizes); the same sums in the same order, tiled or not.
 #include "rglru_launch.h"
 #include "rglru_mfma.h"
 
@@ -148,6 +149,108 @@ __global__ __launch_bounds__(256) void gates_valu(
 }
 
 // ----------------------------------------------------------------------------------------------
+// gates_tiled<T>: the fp32-FMA contraction register-tiled, for Dh % 4 == 0 (Dh <= 256). A
+// workgroup owns 64 rows of one head and 128 of its output channels: the conv output of the rows
+// sits in LDS as fp32; wave w takes rows 16w .. 16w+15 and lane l the outputs l and l + 64, both
+// gates, so each weight row is read by one lane as runs of 4 consecutive k (one 16-byte load for
+// fp32), and each conv value is one LDS broadcast shared by the 64 lanes and reused for 4 FMAs.
+// Every output is accumulated in ascending k from zero, as gates_valu does, so the two kernels
+// agree bit for bit.
+constexpr int kTiledRows = 64;
+constexpr int kTiledOut = 128;
+
+template <typename T> __device__ __forceinline__ float4 load4(const T *p);
+template <> __device__ __forceinline__ float4 load4<float>(const float *p) {
+  return *reinterpret_cast<const float4 *>(p);
+}
+template <> __device__ __forceinline__ float4 load4<bf16_t>(const bf16_t *p) {
+  const uint2 v = *reinterpret_cast<const uint2 *>(p);
+  return make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gates_tiled(
+    const T *__restrict__ x, const T *__restrict__ conv_w, const T *__restrict__ W_a,
+    const float *__restrict__ b_a, const T *__restrict__ W_x, const float *__restrict__ b_x,
+    typename PrePair<T>::type *__restrict__ pre, int Tn, int D, int Dh) {
+  __shared__ float4 xc4[kTiledRows * 256 / 4];  // [row][Dh] fp32 conv output
+  float *xc = reinterpret_cast<float *>(xc4);
+  const int nob = (Dh + kTiledOut - 1) / kTiledOut;
+  const int t0 = blockIdx.x * kTiledRows;
+  const int g = blockIdx.y / nob;
+  const int ob = blockIdx.y % nob;
+  const int b = blockIdx.z;
+  const T *xb = x + static_cast<size_t>(b) * Tn * D;
+  for (int e = threadIdx.x; e < kTiledRows * Dh; e += blockDim.x) {
+    const int r = e / Dh, i = e % Dh;
+    const int d = g * Dh + i;
+    const int t = t0 + r;
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kConvW; ++j) {
+      const int s = t - (kConvW - 1) + j;
+      if (s >= 0 && s < Tn)
+        acc = fmaf(Elem<T>::load(conv_w, static_cast<size_t>(j) * D + d),
+                   Elem<T>::load(xb, static_cast<size_t>(s) * D + d), acc);
+    }
+    xc[e] = acc;
+  }
+  __syncthreads();
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int o0 = ob * kTiledOut + lane;
+  const int o1 = o0 + 64;
+  // rows of out-of-range outputs are clamped to a valid one (loaded, never stored)
+  const size_t wr0 = (static_cast<size_t>(g) * Dh + min(o0, Dh - 1)) * Dh;
+  const size_t wr1 = (static_cast<size_t>(g) * Dh + min(o1, Dh - 1)) * Dh;
+  const int rbase = w * 16;
+  float acc[16][2][2];  // [row][output][gate]
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r][0][0] = acc[r][0][1] = acc[r][1][0] = acc[r][1][1] = 0.0f;
+  float4 wn[4] = {load4<T>(W_a + wr0), load4<T>(W_x + wr0), load4<T>(W_a + wr1),
+                  load4<T>(W_x + wr1)};
+  for (int k = 0; k < Dh; k += 4) {
+    const float4 wc[4] = {wn[0], wn[1], wn[2], wn[3]};
+    if (k + 4 < Dh) {
+      wn[0] = load4<T>(W_a + wr0 + k + 4);
+      wn[1] = load4<T>(W_x + wr0 + k + 4);
+      wn[2] = load4<T>(W_a + wr1 + k + 4);
+      wn[3] = load4<T>(W_x + wr1 + k + 4);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float4 v = xc4[((rbase + r) * Dh + k) >> 2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float4 a = wc[2 * q], xw = wc[2 * q + 1];
+        acc[r][q][0] = fmaf(a.x, v.x, acc[r][q][0]);
+        acc[r][q][1] = fmaf(xw.x, v.x, acc[r][q][1]);
+        acc[r][q][0] = fmaf(a.y, v.y, acc[r][q][0]);
+        acc[r][q][1] = fmaf(xw.y, v.y, acc[r][q][1]);
+        acc[r][q][0] = fmaf(a.z, v.z, acc[r][q][0]);
+        acc[r][q][1] = fmaf(xw.z, v.z, acc[r][q][1]);
+        acc[r][q][0] = fmaf(a.w, v.w, acc[r][q][0]);
+        acc[r][q][1] = fmaf(xw.w, v.w, acc[r][q][1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int o = q ? o1 : o0;
+    if (o >= Dh) continue;
+    const int d = g * Dh + o;
+    const float ba = b_a[d], bx = b_x[d];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = t0 + rbase + r;
+      if (t < Tn)
+        pre[(static_cast<size_t>(b) * Tn + t) * D + d] =
+            PrePair<T>::pack(acc[r][q][0] + ba, acc[r][q][1] + bx);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------------------
 hipError_t launch_gates(const void *x, const void *conv_w, const void *W_a, const float *b_a,
                         const void *W_x, const float *b_x, void *pre, int B, int T, int D, int H,
                         int io, hipStream_t s, bool split) {
@@ -177,6 +280,21 @@ hipError_t launch_gates(const void *x, const void *conv_w, const void *W_a, cons
       default: return hipErrorInvalidValue;
     }
 #undef RGLRU_GATES_CASE
+    return hipGetLastError();
+  }
+  if (Dh % 4 == 0 && Dh <= 256 &&
+      static_cast<long long>(H) * ((Dh + kTiledOut - 1) / kTiledOut) <= 65535) {
+    dim3 tgrid((T + kTiledRows - 1) / kTiledRows, H * ((Dh + kTiledOut - 1) / kTiledOut), B);
+    if (io == kBF16)
+      gates_tiled<bf16_t><<<tgrid, 256, 0, s>>>(
+          static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(conv_w),
+          static_cast<const bf16_t *>(W_a), b_a, static_cast<const bf16_t *>(W_x), b_x,
+          static_cast<uint32_t *>(pre), T, D, Dh);
+    else
+      gates_tiled<float><<<tgrid, 256, 0, s>>>(
+          static_cast<const float *>(x), static_cast<const float *>(conv_w),
+          static_cast<const float *>(W_a), b_a, static_cast<const float *>(W_x), b_x,
+          static_cast<float2 *>(pre), T, D, Dh);
     return hipGetLastError();
   }
   dim3 grid((T + kValuRows - 1) / kValuRows, H, B);
