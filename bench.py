@@ -31,8 +31,9 @@ KERNEL_SOURCES = ["rglru_device.h", "rglru_mfma.h", "rglru_gates.hip", "rglru_sc
                   "rglru_fused.hip"]
 BACKWARD_SOURCES = ["rglru_device.h", "rglru_mfma.h", "rglru_backward.hip", "rglru_bwd_tiles.hip",
                     "rglru_bwd_fused.hip", "rglru_gates.hip"]
-# kernels of one rglru_backward call (name prefixes in rocprofv3 output)
-BACKWARD_KERNELS = ["tile_bwd", "tile_preacts", "gates_mfma<256, true>", "bwd_summary", "bwd_carry",
+# kernels of one rglru_backward call (name prefixes in rocprofv3 output; the split-operand gate
+# kernels only: the forward plans run the same kernels with a single bf16 operand)
+BACKWARD_KERNELS = ["tile_bwd", "tile_preacts<256, true>", "gates_mfma<256, true>", "bwd_summary", "bwd_carry",
                     "bwd_emit", "wt_prep", "tile_dxc", "dxc_mfma", "dxc_valu", "conv_bwd", "dw_mfma",
                     "dw_valu", "colsum"]
 

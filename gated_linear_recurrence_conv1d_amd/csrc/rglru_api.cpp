@@ -16,7 +16,7 @@ using rglru::kF32;
 
 constexpr size_t kAlign = 256;         // workspace carve alignment
 // The scan lanes wait on HBM latency, so the chunked plan wants many lanes in flight: chunks of
-// about 64 steps (measured best from 2 to 32 sequences of 2560 channels), shorter when that
+// about 64 steps (measured best from 1 to 64 sequences of 2560 channels), shorter when that
 // still leaves fewer than ~8 waves per SIMD; the direct plan once B * D alone gives 2 waves.
 constexpr int kMinChunk = 16;          // smallest chunk the size query provisions for
 constexpr int kMaxAutoChunk = 64;      // longest chunk the automatic plan picks

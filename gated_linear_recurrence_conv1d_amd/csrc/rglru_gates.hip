@@ -153,11 +153,13 @@ __global__ __launch_bounds__(256) void gates_valu(
 // workgroup owns 64 rows of one head and 128 of its output channels: the conv output of the rows
 // sits in LDS as fp32; wave w takes rows 16w .. 16w+15 and lane l the outputs l and l + 64, both
 // gates, so each weight row is read by one lane as runs of 4 consecutive k (one 16-byte load for
-// fp32), and each conv value is one LDS broadcast shared by the 64 lanes and reused for 4 FMAs.
+// fp32; two such runs per chunk when Dh % 8 == 0), and each conv value is one LDS broadcast
+// shared by the 64 lanes and reused for 4 FMAs.
 // Every output is accumulated in ascending k from zero, as gates_valu does, so the two kernels
 // agree bit for bit.
 constexpr int kTiledRows = 64;
 constexpr int kTiledOut = 128;
+constexpr int kTiledK = 8;  // k per weight-row run (two 16-byte loads for fp32) when Dh allows
 
 template <typename T> __device__ __forceinline__ float4 load4(const T *p);
 template <> __device__ __forceinline__ float4 load4<float>(const float *p) {
@@ -168,7 +170,7 @@ template <> __device__ __forceinline__ float4 load4<bf16_t>(const bf16_t *p) {
   return make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
 }
 
-template <typename T>
+template <typename T, int KC>
 __global__ __launch_bounds__(256) void gates_tiled(
     const T *__restrict__ x, const T *__restrict__ conv_w, const T *__restrict__ W_a,
     const float *__restrict__ b_a, const T *__restrict__ W_x, const float *__restrict__ b_x,
@@ -207,22 +209,38 @@ __global__ __launch_bounds__(256) void gates_tiled(
   float acc[16][2][2];  // [row][output][gate]
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r][0][0] = acc[r][0][1] = acc[r][1][0] = acc[r][1][1] = 0.0f;
-  float4 wn[4] = {load4<T>(W_a + wr0), load4<T>(W_x + wr0), load4<T>(W_a + wr1),
-                  load4<T>(W_x + wr1)};
-  for (int k = 0; k < Dh; k += 4) {
-    const float4 wc[4] = {wn[0], wn[1], wn[2], wn[3]};
-    if (k + 4 < Dh) {
-      wn[0] = load4<T>(W_a + wr0 + k + 4);
-      wn[1] = load4<T>(W_x + wr0 + k + 4);
-      wn[2] = load4<T>(W_a + wr1 + k + 4);
-      wn[3] = load4<T>(W_x + wr1 + k + 4);
+  constexpr int NV = KC / 4;  // runs of 4 k per weight row and chunk
+  float4 wn[NV][4];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    wn[u][0] = load4<T>(W_a + wr0 + 4 * u);
+    wn[u][1] = load4<T>(W_x + wr0 + 4 * u);
+    wn[u][2] = load4<T>(W_a + wr1 + 4 * u);
+    wn[u][3] = load4<T>(W_x + wr1 + 4 * u);
+  }
+  for (int k = 0; k < Dh; k += KC) {
+    float4 wc[NV][4];
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) wc[u][c] = wn[u][c];
+    if (k + KC < Dh) {
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        wn[u][0] = load4<T>(W_a + wr0 + k + KC + 4 * u);
+        wn[u][1] = load4<T>(W_x + wr0 + k + KC + 4 * u);
+        wn[u][2] = load4<T>(W_a + wr1 + k + KC + 4 * u);
+        wn[u][3] = load4<T>(W_x + wr1 + k + KC + 4 * u);
+      }
     }
 #pragma unroll
+    for (int u = 0; u < NV; ++u)
+#pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float4 v = xc4[((rbase + r) * Dh + k) >> 2];
+      const float4 v = xc4[((rbase + r) * Dh + k + 4 * u) >> 2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const float4 a = wc[2 * q], xw = wc[2 * q + 1];
+        const float4 a = wc[u][2 * q], xw = wc[u][2 * q + 1];
         acc[r][q][0] = fmaf(a.x, v.x, acc[r][q][0]);
         acc[r][q][1] = fmaf(xw.x, v.x, acc[r][q][1]);
         acc[r][q][0] = fmaf(a.y, v.y, acc[r][q][0]);
@@ -285,16 +303,18 @@ hipError_t launch_gates(const void *x, const void *conv_w, const void *W_a, cons
   if (Dh % 4 == 0 && Dh <= 256 &&
       static_cast<long long>(H) * ((Dh + kTiledOut - 1) / kTiledOut) <= 65535) {
     dim3 tgrid((T + kTiledRows - 1) / kTiledRows, H * ((Dh + kTiledOut - 1) / kTiledOut), B);
-    if (io == kBF16)
-      gates_tiled<bf16_t><<<tgrid, 256, 0, s>>>(
-          static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(conv_w),
-          static_cast<const bf16_t *>(W_a), b_a, static_cast<const bf16_t *>(W_x), b_x,
-          static_cast<uint32_t *>(pre), T, D, Dh);
-    else
-      gates_tiled<float><<<tgrid, 256, 0, s>>>(
-          static_cast<const float *>(x), static_cast<const float *>(conv_w),
-          static_cast<const float *>(W_a), b_a, static_cast<const float *>(W_x), b_x,
-          static_cast<float2 *>(pre), T, D, Dh);
+#define RGLRU_TILED(TT, KCV, PT)                                                                  \
+  gates_tiled<TT, KCV><<<tgrid, 256, 0, s>>>(                                                     \
+      static_cast<const TT *>(x), static_cast<const TT *>(conv_w), static_cast<const TT *>(W_a),  \
+      b_a, static_cast<const TT *>(W_x), b_x, static_cast<PT *>(pre), T, D, Dh)
+    if (io == kBF16) {
+      if (Dh % kTiledK == 0) RGLRU_TILED(bf16_t, kTiledK, uint32_t);
+      else RGLRU_TILED(bf16_t, 4, uint32_t);
+    } else {
+      if (Dh % kTiledK == 0) RGLRU_TILED(float, kTiledK, float2);
+      else RGLRU_TILED(float, 4, float2);
+    }
+#undef RGLRU_TILED
     return hipGetLastError();
   }
   dim3 grid((T + kValuRows - 1) / kValuRows, H, B);
