@@ -65,11 +65,15 @@ def case(dtype, B, T, D, H, seed=0, bias=0.25, h0=True, ac=None):
 # ---------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype,D,H", [("bf16", 512, 2), ("bf16", 256, 2), ("bf16", 256, 4),
                                        ("bf16", 128, 4), ("bf16", 96, 2), ("f32", 256, 16),
-                                       ("f32", 96, 2)])
+                                       ("f32", 96, 2),
+                                       ("f32", 512, 2),    # Dh 256: two full output blocks
+                                       ("f32", 400, 2),    # Dh 200: second block partial
+                                       ("bf16", 264, 2),   # Dh 132: runs of 4 k, partial block
+                                       ("f32", 90, 2)])    # Dh 45: the per-output kernel
 def test_gate_preacts_match_oracle(dtype, D, H):
-    """The gate projection alone (MFMA for bf16 with Dh in {32, 64, 128, 256}, vector ALU
-    otherwise) against the oracle's pre-activations; 150 rows = two full 64-row tiles and a
-    ragged tail."""
+    """The gate projection alone (MFMA for bf16 with Dh in {32, 64, 128, 256}, register-tiled
+    vector-ALU FMAs for other Dh % 4 == 0 in blocks of 128 outputs, per-output FMAs otherwise)
+    against the oracle's pre-activations; 150 rows = two full 64-row tiles and a ragged tail."""
     inp = case(dtype, 2, 150, D, H)
     g = to_device(inp)
     pre = rg.pre_buffer(g["x"])
