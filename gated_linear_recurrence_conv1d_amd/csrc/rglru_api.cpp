@@ -45,14 +45,19 @@ rglru_status check_shape(int B, int T, int D, int H, rglru_dtype dt) {
   return RGLRU_OK;
 }
 
-// Chunk length of the automatic plan; returns T when the direct plan is chosen.
-int auto_chunk(int B, int T, int D) {
+// Chunk length of the chunked plan when the caller leaves it open.
+int chunk_for(int B, int T, int D) {
   const long long lanes = static_cast<long long>(B) * D;
-  if (lanes >= kDirectLanes) return T;
   const long long want = (kTargetLanes + lanes - 1) / lanes;
   long long L = (T + want - 1) / want;
   L = std::max<long long>(std::min<long long>(L, kMaxAutoChunk), kMinChunk);
   return L >= T ? T : static_cast<int>(L);
+}
+
+// Chunk length of the automatic plan; returns T when the direct plan is chosen.
+int auto_chunk(int B, int T, int D) {
+  if (static_cast<long long>(B) * D >= kDirectLanes) return T;
+  return chunk_for(B, T, D);
 }
 
 size_t pre_bytes(int B, int T, int D, rglru_dtype dt) {
@@ -84,7 +89,7 @@ bool resolve_plan(int B, int T, int D, rglru_plan plan, int chunk_len, bool &dir
     direct = true;
   } else if (plan == RGLRU_PLAN_CHUNKED) {
     if (chunk_len < 0) return false;
-    L = chunk_len == 0 ? auto_chunk(B, T, D) : std::min(chunk_len, T);
+    L = chunk_len == 0 ? chunk_for(B, T, D) : std::min(chunk_len, T);
     direct = false;
   } else {
     return false;
