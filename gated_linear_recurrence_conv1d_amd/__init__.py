@@ -44,6 +44,10 @@ _lib.rglru_forward_workspace_size.argtypes = [_i] * 5
 _lib.rglru_forward_workspace_size.restype = _sz
 _lib.rglru_scan_workspace_size.argtypes = [_i] * 5
 _lib.rglru_scan_workspace_size.restype = _sz
+_lib.rglru_forward_workspace_size_planned.argtypes = [_i] * 7
+_lib.rglru_forward_workspace_size_planned.restype = _sz
+_lib.rglru_lookback_failures.argtypes = [_vp, _sz, ctypes.POINTER(ctypes.c_uint), _vp]
+_lib.rglru_lookback_failures.restype = _i
 _lib.rglru_forward_plan_info.argtypes = [_i] * 5 + [ctypes.POINTER(_i), ctypes.POINTER(_i)]
 _lib.rglru_forward_plan_info.restype = _i
 _lib.rglru_forward.argtypes = [_vp] * 10 + [_i] * 5 + [_vp, _sz, _vp]
@@ -99,6 +103,33 @@ def _ptr(t, io_dtype=None, name=""):
     return t.data_ptr()
 
 
+def _shape(t, shape, name):
+    """Raise ValueError unless tensor t (if given) has exactly this shape. Every buffer's size is
+    checked here, before any call: the C ABI takes sizes only through B, T, D, H, N, so a tensor
+    of another size would be read or written out of its bounds on the device."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _dims(x, W_a):
+    if x.dim() != 3:
+        raise ValueError(f"x: expected [B, T, D], got shape {tuple(x.shape)}")
+    B, T, D = x.shape
+    if W_a.dim() != 3 or W_a.shape[0] < 1 or D % W_a.shape[0]:
+        raise ValueError(f"W_a: expected [H, D/H, D/H] with D = {D}, got {tuple(W_a.shape)}")
+    return B, T, D, W_a.shape[0]
+
+
+def _check_params(D, H, conv_w, W_a, b_a, W_x, b_x, Lam):
+    Dh = D // H
+    _shape(conv_w, (4, D), "conv_w")
+    _shape(W_a, (H, Dh, Dh), "W_a")
+    _shape(W_x, (H, Dh, Dh), "W_x")
+    _shape(b_a, (D,), "b_a")
+    _shape(b_x, (D,), "b_x")
+    _shape(Lam, (D,), "Lambda")
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -120,6 +151,22 @@ def rglru_scan_workspace_size(B, T, D, H, dtype) -> int:
     return int(_lib.rglru_scan_workspace_size(B, T, D, H, _dt(dtype)))
 
 
+def rglru_forward_workspace_size_planned(B, T, D, H, dtype, plan="auto", chunk_len=0) -> int:
+    return int(_lib.rglru_forward_workspace_size_planned(B, T, D, H, _dt(dtype), _PLANS[plan],
+                                                         int(chunk_len)))
+
+
+def rglru_lookback_failures(workspace, stream=None) -> int:
+    """Look-back waits of the last forward / backward call on `workspace` that gave up (0 after
+    a normal call). Waits for the stream."""
+    n = ctypes.c_uint(0)
+    _check(_lib.rglru_lookback_failures(_ptr(workspace, None, "workspace"),
+                                        workspace.numel() * workspace.element_size(),
+                                        ctypes.byref(n), _stream(stream)),
+           "rglru_lookback_failures")
+    return int(n.value)
+
+
 def rglru_forward_plan_info(B, T, D, H, dtype):
     plan, chunk = _i(), _i()
     _check(_lib.rglru_forward_plan_info(B, T, D, H, _dt(dtype), ctypes.byref(plan),
@@ -130,8 +177,11 @@ def rglru_forward_plan_info(B, T, D, H, dtype):
 
 def _fwd_args(x, conv_w, W_a, b_a, W_x, b_x, Lam, h0, y, h_T):
     io = x.dtype
-    B, T, D = x.shape
-    H = W_a.shape[0]
+    B, T, D, H = _dims(x, W_a)
+    _check_params(D, H, conv_w, W_a, b_a, W_x, b_x, Lam)
+    _shape(h0, (B, D), "h0")
+    _shape(y, (B, T, D), "y")
+    _shape(h_T, (B, D), "h_T")
     f32 = torch.float32
     ptrs = [_ptr(x, io, "x"), _ptr(conv_w, io, "conv_w"), _ptr(W_a, io, "W_a"),
             _ptr(b_a, f32, "b_a"), _ptr(W_x, io, "W_x"), _ptr(b_x, f32, "b_x"),
@@ -159,8 +209,9 @@ def rglru_forward_planned(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, h_T, wor
 def rglru_gate_preacts(x, conv_w, W_a, b_a, W_x, b_x, pre, stream=None):
     """pre: int32 [B,T,D] (fp16 pairs) for bf16 x, float32 [B,T,D,2] for fp32 x."""
     io = x.dtype
-    B, T, D = x.shape
-    H = W_a.shape[0]
+    B, T, D, H = _dims(x, W_a)
+    _check_params(D, H, conv_w, W_a, b_a, W_x, b_x, None)
+    _check_pre(pre, x)
     f32 = torch.float32
     _check(_lib.rglru_gate_preacts(_ptr(x, io, "x"), _ptr(conv_w, io, "conv_w"),
                                    _ptr(W_a, io, "W_a"), _ptr(b_a, f32, "b_a"),
@@ -169,10 +220,32 @@ def rglru_gate_preacts(x, conv_w, W_a, b_a, W_x, b_x, pre, stream=None):
            "rglru_gate_preacts")
 
 
+def _check_pre(pre, x):
+    B, T, D = x.shape
+    if x.dtype == torch.bfloat16:
+        _shape(pre, (B, T, D), "pre")
+        if pre.dtype != torch.int32:
+            raise ValueError("pre: expected int32 (fp16 pairs) for bf16 x")
+    else:
+        _shape(pre, (B, T, D, 2), "pre")
+        if pre.dtype != torch.float32:
+            raise ValueError("pre: expected float32 pairs for fp32 x")
+
+
 def rglru_scan_preacts(x, pre, conv_w, Lambda, h0, y, h_T, H, workspace=None, plan="auto",
                        chunk_len=0, stream=None):
     io = x.dtype
+    if x.dim() != 3:
+        raise ValueError(f"x: expected [B, T, D], got shape {tuple(x.shape)}")
     B, T, D = x.shape
+    if H < 1 or D % H:
+        raise ValueError(f"H = {H} must divide D = {D}")
+    _check_pre(pre, x)
+    _shape(conv_w, (4, D), "conv_w")
+    _shape(Lambda, (D,), "Lambda")
+    _shape(h0, (B, D), "h0")
+    _shape(y, (B, T, D), "y")
+    _shape(h_T, (B, D), "h_T")
     f32 = torch.float32
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.rglru_scan_preacts(_ptr(x, io, "x"), _ptr(pre, None, "pre"),
@@ -185,8 +258,16 @@ def rglru_scan_preacts(x, pre, conv_w, Lambda, h0, y, h_T, H, workspace=None, pl
 
 def rglru_decode_step(x_t, conv_state, h, y_t, conv_w, W_a, b_a, W_x, b_x, Lambda, stream=None):
     io = x_t.dtype
+    if x_t.dim() != 2:
+        raise ValueError(f"x_t: expected [N, D], got shape {tuple(x_t.shape)}")
     N, D = x_t.shape
+    if W_a.dim() != 3 or W_a.shape[0] < 1 or D % W_a.shape[0]:
+        raise ValueError(f"W_a: expected [H, D/H, D/H] with D = {D}, got {tuple(W_a.shape)}")
     H = W_a.shape[0]
+    _check_params(D, H, conv_w, W_a, b_a, W_x, b_x, Lambda)
+    _shape(conv_state, (N, 3, D), "conv_state")
+    _shape(h, (N, D), "h")
+    _shape(y_t, (N, D), "y_t")
     f32 = torch.float32
     _check(_lib.rglru_decode_step(_ptr(x_t, io, "x_t"), _ptr(conv_state, io, "conv_state"),
                                   _ptr(h, f32, "h"), _ptr(y_t, io, "y_t"),
@@ -200,7 +281,10 @@ def rglru_decode_step(x_t, conv_state, h, y_t, conv_w, W_a, b_a, W_x, b_x, Lambd
 def rglru_prefill_state(x, conv_state, stream=None):
     """conv_state [B,3,D] (x's dtype) = the last three inputs of each sequence of x [B,T,D]."""
     io = x.dtype
+    if x.dim() != 3:
+        raise ValueError(f"x: expected [B, T, D], got shape {tuple(x.shape)}")
     B, T, D = x.shape
+    _shape(conv_state, (B, 3, D), "conv_state")
     _check(_lib.rglru_prefill_state(_ptr(x, io, "x"), _ptr(conv_state, io, "conv_state"), B, T, D,
                                     _dt(io), _stream(stream)), "rglru_prefill_state")
 
@@ -215,7 +299,12 @@ def prefill_state(x, stream=None):
 
 def rglru_local_mqa(q, k, v, o, window, scale=0.0, stream=None):
     """q, o [B,T,Hq,dh]; k, v [B,T,dh]; bf16."""
+    if q.dim() != 4:
+        raise ValueError(f"q: expected [B, T, Hq, dh], got shape {tuple(q.shape)}")
     B, T, Hq, dh = q.shape
+    _shape(k, (B, T, dh), "k")
+    _shape(v, (B, T, dh), "v")
+    _shape(o, (B, T, Hq, dh), "o")
     bf = torch.bfloat16
     _check(_lib.rglru_local_mqa(_ptr(q, bf, "q"), _ptr(k, bf, "k"), _ptr(v, bf, "v"),
                                 _ptr(o, bf, "o"), B, T, Hq, dh, int(window), float(scale),
@@ -236,8 +325,15 @@ def rglru_backward_workspace_size(B, T, D, H, dtype) -> int:
 def rglru_backward(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, dy, dh_T, dx, dconv_w, dW_a,
                    db_a, dW_x, db_x, dLambda, dh0, workspace, stream=None):
     io = x.dtype
-    B, T, D = x.shape
-    H = W_a.shape[0]
+    B, T, D, H = _dims(x, W_a)
+    Dh = D // H
+    _check_params(D, H, conv_w, W_a, b_a, W_x, b_x, Lambda)
+    for t, shape, name in ((h0, (B, D), "h0"), (y, (B, T, D), "y"), (dy, (B, T, D), "dy"),
+                           (dh_T, (B, D), "dh_T"), (dx, (B, T, D), "dx"),
+                           (dconv_w, (4, D), "dconv_w"), (dW_a, (H, Dh, Dh), "dW_a"),
+                           (db_a, (D,), "db_a"), (dW_x, (H, Dh, Dh), "dW_x"), (db_x, (D,), "db_x"),
+                           (dLambda, (D,), "dLambda"), (dh0, (B, D), "dh0")):
+        _shape(t, shape, name)
     f32 = torch.float32
     ptrs = [_ptr(x, io, "x"), _ptr(conv_w, io, "conv_w"), _ptr(W_a, io, "W_a"),
             _ptr(b_a, f32, "b_a"), _ptr(W_x, io, "W_x"), _ptr(b_x, f32, "b_x"),
@@ -268,10 +364,10 @@ def forward(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0=None, plan="auto", chunk_l
     y = torch.empty_like(x)
     h_T = torch.empty((B, D), dtype=torch.float32, device=x.device)
     if workspace is None:
-        n = rglru_forward_workspace_size(B, T, D, H, x.dtype)
-        if plan == "chunked" and chunk_len:
-            # small explicit chunks may need more summary space than the default provisions
-            n += 12 * B * D * ((T + chunk_len - 1) // chunk_len) + 1024
+        n = rglru_forward_workspace_size_planned(B, T, D, H, x.dtype, plan, chunk_len)
+        if n == 0:
+            raise RglruError(RGLRU_ERR_UNSUPPORTED if plan == "fused" else RGLRU_ERR_INVALID_ARG,
+                             "rglru_forward_workspace_size_planned")
         workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
     rglru_forward_planned(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, h_T, workspace, plan,
                           chunk_len, stream)

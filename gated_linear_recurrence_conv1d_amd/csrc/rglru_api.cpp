@@ -119,6 +119,14 @@ size_t fused_bytes(int B, int T, int D, int H) {
          2 * rglru::fused_slots(B, T, H, D / H) * sizeof(unsigned long long);
 }
 
+// Workspace of one resolved forward plan. The split plans: control words, pre-activations, then
+// (chunked) the scan's chunk summaries; the fused plan: control words, then look-back words.
+size_t split_or_fused_bytes(int B, int T, int D, int H, rglru_dtype dt, Kind kind, int L) {
+  if (kind == kFused) return align_up(fused_bytes(B, T, D, H));
+  return rglru::kCtrlBytes + align_up(pre_bytes(B, T, D, dt)) +
+         (kind == kDirect ? 0 : scan_carve(B, D, (T + L - 1) / L).total);
+}
+
 rglru_status hip_status(hipError_t e) { return e == hipSuccess ? RGLRU_OK : RGLRU_ERR_HIP; }
 
 }  // namespace
@@ -143,8 +151,33 @@ size_t rglru_scan_workspace_size(int B, int T, int D, int H, rglru_dtype dt) {
 
 size_t rglru_forward_workspace_size(int B, int T, int D, int H, rglru_dtype dt) {
   if (check_shape(B, T, D, H, dt) != RGLRU_OK) return 0;
-  const size_t split = align_up(pre_bytes(B, T, D, dt)) + rglru_scan_workspace_size(B, T, D, H, dt);
+  const size_t split = rglru::kCtrlBytes + align_up(pre_bytes(B, T, D, dt)) +
+                       rglru_scan_workspace_size(B, T, D, H, dt);
   return std::max(split, align_up(fused_bytes(B, T, D, H)));
+}
+
+size_t rglru_forward_workspace_size_planned(int B, int T, int D, int H, rglru_dtype dt,
+                                            rglru_plan plan, int chunk_len) {
+  if (check_shape(B, T, D, H, dt) != RGLRU_OK) return 0;
+  Kind kind;
+  int L;
+  if (resolve_forward(B, T, D, H, dt, plan, chunk_len, kind, L) != RGLRU_OK) return 0;
+  return split_or_fused_bytes(B, T, D, H, dt, kind, L);
+}
+
+rglru_status rglru_lookback_failures(const void *workspace, size_t workspace_bytes,
+                                     unsigned *count, void *stream) {
+  if (!workspace || !count || workspace_bytes < rglru::kCtrlBytes) return RGLRU_ERR_INVALID_ARG;
+  if (!aligned(workspace, 16)) return RGLRU_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned v = 0;
+  (void)hipGetLastError();
+  if (hipMemcpyAsync(&v, static_cast<const unsigned *>(workspace) + 1, sizeof(unsigned),
+                     hipMemcpyDeviceToHost, s) != hipSuccess)
+    return RGLRU_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return RGLRU_ERR_HIP;
+  *count = v;
+  return RGLRU_OK;
 }
 
 rglru_status rglru_forward_plan_info(int B, int T, int D, int H, rglru_dtype dt, int *plan,
@@ -239,8 +272,8 @@ rglru_status rglru_forward_planned(const void *x, const void *conv_w, const void
                                           T, D, H, workspace, static_cast<hipStream_t>(stream)));
   }
   const bool direct = kind == kDirect;
-  const size_t pre_area = align_up(pre_bytes(B, T, D, dt));
-  const size_t need = pre_area + (direct ? 0 : scan_carve(B, D, (T + L - 1) / L).total);
+  const size_t pre_area = rglru::kCtrlBytes + align_up(pre_bytes(B, T, D, dt));
+  const size_t need = split_or_fused_bytes(B, T, D, H, dt, kind, L);
   if (!workspace || workspace_bytes < need) return RGLRU_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return RGLRU_ERR_INVALID_ARG;
   if (overlaps(workspace, need, y, io_bytes) || overlaps(workspace, need, x, io_bytes))
@@ -249,10 +282,14 @@ rglru_status rglru_forward_planned(const void *x, const void *conv_w, const void
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int io = dt == RGLRU_BF16 ? kBF16 : kF32;
   char *ws = static_cast<char *>(workspace);
+  char *pre = ws + rglru::kCtrlBytes;
   (void)hipGetLastError();  // start from a clean error state
-  hipError_t e = rglru::launch_gates(x, conv_w, W_a, b_a, W_x, b_x, ws, B, T, D, H, io, s);
+  // the split plans never wait: their look-back failure count is zero
+  hipError_t e = rglru::launch_clear_words(reinterpret_cast<unsigned *>(ws), 2, s);
+  if (e == hipSuccess)
+    e = rglru::launch_gates(x, conv_w, W_a, b_a, W_x, b_x, pre, B, T, D, H, io, s);
   if (e != hipSuccess) return RGLRU_ERR_HIP;
-  return rglru_scan_preacts(x, ws, conv_w, Lambda, h0, y, h_T, B, T, D, H, dt, ws + pre_area,
+  return rglru_scan_preacts(x, pre, conv_w, Lambda, h0, y, h_T, B, T, D, H, dt, ws + pre_area,
                             workspace_bytes - pre_area, stream, direct ? RGLRU_PLAN_DIRECT
                                                                        : RGLRU_PLAN_CHUNKED,
                             L);

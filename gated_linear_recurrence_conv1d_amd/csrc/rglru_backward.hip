@@ -1,7 +1,8 @@
 // rglru_backward.hip -- gradients of the Conv1D(width 4) -> RG-LRU forward.
 //
-// The forward (Griffin paper page on docshare.wps.com, section "Model Architecture"; the gate
-// that can discard the input and keep the history, Soham De's Griffin thread, tweet on adding a
+// The forward (the RG-LRU named by the Griffin paper page on docshare.wps.com, abstract and
+// Introduction, with the equations the forward's header writes out; the gate that can discard
+// the input and keep the history, Soham De's Griffin thread, tweet on adding a
 // Recurrent Gate to LRU; the temporal Conv1D in front, same thread, tweet on keeping the recurrent
 // block simple) is differentiated with the chain rule. The pages name training as the place the
 // method was memory bound (same thread, the tweet on the Pallas kernel and HBM accesses), which
@@ -961,6 +962,9 @@ BwdLayout backward_layout(int B, int T, int D, int H, int io) {
     off += (bytes + 255) / 256 * 256;
     return r;
   };
+  // control words first, in every path: [1] counts look-back waits that gave up (read back by
+  // rglru_lookback_failures), [2 + g] the tile tickets of the fused pass
+  L.o_ctrl = take(kCtrlBytes);
   L.o_pre = take(L.fused ? 0 : n * pairb);
   L.o_dpre = take(n * pairb);
   L.o_dlo = take(io == kBF16 ? n * 4 : 0);
@@ -971,7 +975,6 @@ BwdLayout backward_layout(int B, int T, int D, int H, int io) {
   L.o_pcw = take(4 * P * D * sizeof(float));
   L.o_pw = take(static_cast<size_t>(L.S) * H * 2 * Dh * Dh * sizeof(float));
   L.o_wti = take(L.mfma_dxc ? static_cast<size_t>(H) * Dh * 2 * Dh * sizeof(bf16_t) : 0);
-  L.o_ctrl = take(L.fused ? (2 + static_cast<size_t>(H)) * sizeof(unsigned) : 0);
   L.o_lb = take(L.fused ? fused_backward_slots(B, T, D) * sizeof(unsigned long long) : 0);
   L.total = off;
   return L;
@@ -1004,6 +1007,11 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
   const bool pair = D % 2 == 0;
   const dim3 lgrid(pair ? (lblocks + 1) / 2 : lblocks, L.nC);
   hipError_t e = hipSuccess;
+  if (!L.fused) {
+    // no waits on this path: the failure count is zero
+    e = launch_clear_words(reinterpret_cast<unsigned *>(ws + L.o_ctrl), 2, s);
+    if (e != hipSuccess) return e;
+  }
   if constexpr (sizeof(T) == 2) {
     if (L.fused) {
       // passes 1-3 as one tile pass (partial sums per tile of kFusedBwdRows steps)

@@ -1,8 +1,9 @@
 // rglru_device.h -- device-side element types and the RG-LRU gate math for gfx950.
 //
-// The gate math follows the RG-LRU (Griffin paper page on docshare.wps.com, section "Model
-// Architecture"; the recurrence gate that can drop the input and keep the history is the one of
-// Soham De's Griffin thread, tweet on adding a Recurrent Gate to LRU):
+// The gate math follows the RG-LRU as this library defines it (the Griffin paper page on
+// docshare.wps.com names the layer in its abstract and Introduction but prints no equations; the
+// recurrence gate that can drop the input and keep the history is the one of Soham De's Griffin
+// thread, tweet on adding a Recurrent Gate to LRU):
 //   r = sigmoid(pa), i = sigmoid(px), log a = -8 r softplus(-Lambda),
 //   a = exp(log a), m = sqrt(1 - a^2), u = m * i * xc, h <- a h + u.
 // In fp32, 1 - a*a cancels catastrophically when a is near 1 (a^8 = 0.9999 and r = 0.01 give

@@ -85,6 +85,15 @@ __global__ void fused_reset(unsigned long long *slots, size_t n, unsigned *ctrl,
     for (int i = threadIdx.x; i < nctrl; i += blockDim.x) ctrl[i] = 0u;
 }
 
+__global__ void clear_words(unsigned *p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+hipError_t launch_clear_words(unsigned *p, int n, hipStream_t s) {
+  clear_words<<<1, 64, 0, s>>>(p, n);
+  return hipGetLastError();
+}
+
 struct TileCtx {
   int j, tt, b, t0;
 };

@@ -40,6 +40,13 @@ hipError_t launch_decode(const void *x_t, void *conv_state, float *h, void *y_t,
                          const float *b_x, const float *Lambda, int N, int D, int H, int io,
                          hipStream_t s);
 
+// Every forward and backward workspace starts with kCtrlBytes of control words: word 1 counts
+// the look-back waits that gave up (zero after any call that completed normally), the words
+// after it are the fused passes' tile tickets. Calls whose plan has no waits clear word 1 with
+// launch_clear_words.
+constexpr size_t kCtrlBytes = 256;
+hipError_t launch_clear_words(unsigned *p, int n, hipStream_t s);
+
 // Single-pass fused forward (bf16 I/O, Dh in {32, 64, 128, 256}, T * D < 2^31 so that offsets
 // within one sequence fit in 32 bits): conv + MFMA gates + gate
 // nonlinearity + scan with a decoupled look-back across 64-step time tiles. ctrl_ws:

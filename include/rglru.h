@@ -13,8 +13,9 @@
  * keeping the recurrent block simple and on adding a Recurrent Gate to LRU); gates that do not
  * read the recurrent state and a fixed-size state (alby13 blog "Beyond Transformer Architecture:
  * Griffin and Google RecurrentGemma", section "Core Components of Griffin -- 1. RG-LRU"); the
- * diagonal recurrence (Soham De's thread, tweet on S4D/LRU); the RG-LRU layer itself (Griffin
- * paper page on docshare.wps.com: abstract, Introduction, section "Model Architecture").
+ * diagonal recurrence (Soham De's thread, tweet on S4D/LRU); the RG-LRU layer itself is named by
+ * the Griffin paper page on docshare.wps.com (abstract and Introduction). The pages print no
+ * equations: the ones above are the RG-LRU's as this library defines it, c = 8.
  *
  * Conventions for every entry point:
  *  - Pointers named x, y, conv_w, W_a, W_x, conv_state, workspace, b_a, b_x, Lambda, h0, h_T, h
@@ -75,6 +76,25 @@ const char *rglru_status_string(rglru_status s);
  * the shape is invalid. */
 size_t rglru_forward_workspace_size(int B, int T, int D, int H, rglru_dtype dt);
 
+/* Bytes of device workspace rglru_forward_planned needs with this plan and chunk length (the
+ * smallest workspace that call accepts; rglru_forward_workspace_size covers every plan with
+ * chunks of 16 steps or more). Returns 0 when the shape, plan or chunk length is invalid or the
+ * plan is unsupported for the shape. */
+size_t rglru_forward_workspace_size_planned(int B, int T, int D, int H, rglru_dtype dt,
+                                            rglru_plan plan, int chunk_len);
+
+/* Every rglru_forward / rglru_forward_planned / rglru_backward workspace begins with a control
+ * block; its failure count is the number of look-back waits of the last such call on this
+ * workspace that gave up. The FUSED forward and the backward's tile pass link time tiles by
+ * bounded waits on words other tiles publish; a wait that exceeds its bound (which only a broken
+ * ordering invariant can cause) stops, writes NaN for its channel and bumps the count, so a
+ * defect shows as NaN and a nonzero count, never as a hang. Plans without waits set the count to
+ * zero. This call waits for `stream` (the copy is ordered after the work queued on it), then
+ * writes the count to *count (host memory). workspace_bytes must be at least 256.
+ * Returns RGLRU_OK, RGLRU_ERR_INVALID_ARG or RGLRU_ERR_HIP. */
+rglru_status rglru_lookback_failures(const void *workspace, size_t workspace_bytes,
+                                     unsigned *count, void *stream);
+
 /* The plan and chunk length RGLRU_PLAN_AUTO picks for this shape (host-side query, no launch).
  * Writes *plan (RGLRU_PLAN_DIRECT, _CHUNKED or _FUSED) and *chunk_len (T for DIRECT, the tile
  * length 64 for FUSED). */
@@ -134,7 +154,11 @@ rglru_status rglru_scan_preacts(const void *x, const void *pre, const void *conv
                                 size_t workspace_bytes, void *stream, rglru_plan plan,
                                 int chunk_len);
 
-/* One decode step for N independent sequences, in place.
+/* One decode step for N independent sequences, in place: the same conv, gates and recurrence for
+ * T = 1, continuing from a fixed-size per-sequence state -- the last three inputs and the fp32 h
+ * -- which is what makes the recurrent model's decoding fast and its memory constant (alby13
+ * blog "Beyond Transformer Architecture: Griffin and Google RecurrentGemma", sections "Core
+ * Components of Griffin -- 1. RG-LRU" and "Griffin's Strengths").
  *  x_t         [N][D] dtype                new token per row
  *  conv_state  [N][3][D] dtype, in/out     last three inputs, oldest first; becomes
  *                                          (cs[1], cs[2], x_t)
@@ -190,7 +214,8 @@ size_t rglru_backward_workspace_size(int B, int T, int D, int H, rglru_dtype dt)
  * and the scan); the pages print no backward -- they place the method's memory-bound cost in
  * training (Soham De's Griffin thread, muskviewer.com, the tweet on the Pallas kernel and HBM
  * accesses), and the forward it differentiates is the one described above. The reverse-time
- * adjoint delta_t = dy_t + a_{t+1} delta_{t+1} is scanned in chunks of 64 steps, so the pass has
+ * adjoint delta_t = dy_t + a_{t+1} delta_{t+1} is scanned in time tiles (32 steps in the bf16
+ * tile pass for Dh 128 / 256, chunks of 64 steps otherwise) linked across tiles, so the pass has
  * parallelism over time as well as over (b, d).
  *  x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0   the forward's inputs (h0 NULL: zeros)
  *  y       [B][T][D] dtype            the forward's output for these inputs; h[t-1] is read from

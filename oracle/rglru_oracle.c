@@ -4,7 +4,7 @@
  *
  * TEST INFRASTRUCTURE ONLY. Nothing in the product path may include, link or call this file.
  * Only tests/, __graft_entry__.smoke() and the cpu_baseline leg of bench.py use it, through
- * oracle/oracle.py. It shares no code, header, table or constant with the HIP library.
+ * oracle/__init__.py. It shares no code, header, table or constant with the HIP library.
  *
  * Sources (the pages are web pages about Griffin / RecurrentGemma):
  *  - "Soham De's Griffin thread" (muskviewer.com, sohamde_ tweet 1768346638286762045):
@@ -53,8 +53,9 @@ static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 static double softplus(double z) { return (z > 0.0 ? z : 0.0) + log1p(exp(-fabs(z))); }
 
 /* One RG-LRU step for one channel, given the conv output xc and both pre-activations.
- * Returns the new state. (Griffin paper, section Model Architecture: recurrence gate r, input
- * gate i, decay a = sigma(Lambda)^(c r) taken in log space, normaliser sqrt(1 - a^2).) */
+ * Returns the new state: the gate, decay and normaliser terms of the definition in this file's
+ * header (recurrence gate r, input gate i, decay a = sigma(Lambda)^(c r) taken in log space,
+ * normaliser sqrt(1 - a^2)). */
 static double rglru_step(double h, double xc, double pa, double px, double lambda) {
   double r = sigmoid(pa);
   double ig = sigmoid(px);

@@ -226,3 +226,94 @@ def test_prefill_state_argument_checks():
     assert lib.rglru_prefill_state(x + 8, cs, *ok_shape, None) == rg.RGLRU_ERR_INVALID_ARG    # align
     assert lib.rglru_prefill_state(x, cs, 0, 64, 512, rg.RGLRU_BF16, None) == rg.RGLRU_ERR_INVALID_ARG
     assert lib.rglru_prefill_state(x, cs, 2, 64, 512, 9, None) == rg.RGLRU_ERR_UNSUPPORTED
+
+
+def test_planned_workspace_sizes():
+    B, T, D, H = 8, 2048, 2560, 10
+    ctrl = 256
+    pre = B * T * D * 4
+    fused = rg.rglru_forward_workspace_size_planned(B, T, D, H, "bf16", "fused", 0)
+    assert fused >= ctrl + 2 * (T // 64) * B * D * 8
+    assert rg.rglru_forward_workspace_size_planned(B, T, D, H, "bf16", "auto", 0) == fused
+    direct = rg.rglru_forward_workspace_size_planned(B, T, D, H, "bf16", "direct", 0)
+    assert direct >= ctrl + pre
+    for L in (1, 7, 64, 5000):
+        nC = (T + min(L, T) - 1) // min(L, T)
+        got = rg.rglru_forward_workspace_size_planned(B, T, D, H, "bf16", "chunked", L)
+        assert got >= direct + B * nC * D * 12, L
+    # explicit chunks shorter than 16 steps need more than the plan-independent query gives
+    assert rg.rglru_forward_workspace_size_planned(B, T, D, H, "bf16", "chunked", 1) > \
+        rg.rglru_forward_workspace_size(B, T, D, H, "bf16")
+    # the plan-independent size covers every plan with chunks of >= 16 steps
+    for plan, L in (("fused", 0), ("direct", 0), ("chunked", 16), ("chunked", 0)):
+        assert rg.rglru_forward_workspace_size_planned(B, T, D, H, "bf16", plan, L) <= \
+            rg.rglru_forward_workspace_size(B, T, D, H, "bf16")
+    # invalid: unsupported fused shape, negative chunk, bad shape
+    assert rg.rglru_forward_workspace_size_planned(1, 64, 96, 2, "bf16", "fused", 0) == 0
+    assert rg.rglru_forward_workspace_size_planned(1, 64, 256, 1, "f32", "fused", 0) == 0
+    assert rg.rglru_forward_workspace_size_planned(1, 64, 256, 1, "bf16", "chunked", -1) == 0
+    assert rg.rglru_forward_workspace_size_planned(1, 64, 256, 3, "bf16", "direct", 0) == 0
+
+
+def test_lookback_failures_argument_checks():
+    n = ctypes.c_uint(7)
+    assert lib.rglru_lookback_failures(None, 1 << 20, ctypes.byref(n), None) == \
+        rg.RGLRU_ERR_INVALID_ARG
+    assert lib.rglru_lookback_failures(FAKE, 255, ctypes.byref(n), None) == \
+        rg.RGLRU_ERR_INVALID_ARG
+    assert lib.rglru_lookback_failures(FAKE, 256, None, None) == rg.RGLRU_ERR_INVALID_ARG
+    assert lib.rglru_lookback_failures(FAKE + 8, 256, ctypes.byref(n), None) == \
+        rg.RGLRU_ERR_INVALID_ARG
+    assert n.value == 7
+
+
+def test_binding_checks_every_tensor_size():
+    """The binding checks each tensor's shape against (B, T, D, H) before any call, so that a
+    wrong-sized buffer never reaches the device (host tensors: nothing is launched)."""
+    import torch
+    B, T, D, H = 2, 5, 64, 2
+    Dh = D // H
+    bf, f32 = torch.bfloat16, torch.float32
+    x = torch.zeros(B, T, D, dtype=bf)
+    p = dict(conv_w=torch.zeros(4, D, dtype=bf), W_a=torch.zeros(H, Dh, Dh, dtype=bf),
+             b_a=torch.zeros(D), W_x=torch.zeros(H, Dh, Dh, dtype=bf), b_x=torch.zeros(D),
+             Lambda=torch.zeros(D))
+    good = dict(h0=torch.zeros(B, D), y=torch.zeros(B, T, D, dtype=bf), h_T=torch.zeros(B, D))
+    bad = {"conv_w": torch.zeros(3, D, dtype=bf), "W_x": torch.zeros(H, Dh, Dh + 1, dtype=bf),
+           "b_a": torch.zeros(D - 1), "Lambda": torch.zeros(D + 1), "h0": torch.zeros(B + 1, D),
+           "y": torch.zeros(B, T - 1, D, dtype=bf), "h_T": torch.zeros(B, D // 2)}
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    for name, t in bad.items():
+        args = dict(p, **good)
+        args[name] = t
+        with pytest.raises(ValueError, match=name):
+            rg.rglru_forward(x, args["conv_w"], args["W_a"], args["b_a"], args["W_x"],
+                             args["b_x"], args["Lambda"], args["h0"], args["y"], args["h_T"], ws)
+    with pytest.raises(ValueError, match="pre"):
+        rg.rglru_gate_preacts(x, p["conv_w"], p["W_a"], p["b_a"], p["W_x"], p["b_x"],
+                              torch.zeros(B, T, D - 2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="pre"):
+        rg.rglru_scan_preacts(x, torch.zeros(B, T, D, 2), p["conv_w"], p["Lambda"], None,
+                              good["y"], None, H)
+    N = 3
+    with pytest.raises(ValueError, match="conv_state"):
+        rg.rglru_decode_step(torch.zeros(N, D, dtype=bf), torch.zeros(N, 2, D, dtype=bf),
+                             torch.zeros(N, D), torch.zeros(N, D, dtype=bf), **p)
+    with pytest.raises(ValueError, match="h"):
+        rg.rglru_decode_step(torch.zeros(N, D, dtype=bf), torch.zeros(N, 3, D, dtype=bf),
+                             torch.zeros(N + 1, D), torch.zeros(N, D, dtype=bf), **p)
+    with pytest.raises(ValueError, match="conv_state"):
+        rg.rglru_prefill_state(x, torch.zeros(B, 3, D + 1, dtype=bf))
+    with pytest.raises(ValueError, match="k"):
+        rg.rglru_local_mqa(torch.zeros(B, T, 2, 64, dtype=bf), torch.zeros(B, T + 1, 64, dtype=bf),
+                           torch.zeros(B, T, 64, dtype=bf), torch.zeros(B, T, 2, 64, dtype=bf), 4)
+    grads = dict(dx=torch.zeros(B, T, D, dtype=bf), dconv_w=torch.zeros(4, D),
+                 dW_a=torch.zeros(H, Dh, Dh), db_a=torch.zeros(D), dW_x=torch.zeros(H, Dh, Dh),
+                 db_x=torch.zeros(D), dLambda=torch.zeros(D), dh0=torch.zeros(B, D))
+    for name in grads:
+        g = dict(grads)
+        g[name] = torch.zeros(1)
+        with pytest.raises(ValueError, match=name):
+            rg.rglru_backward(x, p["conv_w"], p["W_a"], p["b_a"], p["W_x"], p["b_x"], p["Lambda"],
+                              None, good["y"], good["y"], None, g["dx"], g["dconv_w"], g["dW_a"],
+                              g["db_a"], g["dW_x"], g["db_x"], g["dLambda"], g["dh0"], ws)
