@@ -52,6 +52,10 @@ _lib.rglru_forward_plan_info.argtypes = [_i] * 5 + [ctypes.POINTER(_i), ctypes.P
 _lib.rglru_forward_plan_info.restype = _i
 _lib.rglru_forward.argtypes = [_vp] * 10 + [_i] * 5 + [_vp, _sz, _vp]
 _lib.rglru_forward.restype = _i
+_lib.rglru_forward_noalloc.argtypes = [_vp] * 10 + [_i] * 5 + [_vp]
+_lib.rglru_forward_noalloc.restype = _i
+_lib.rglru_forward_noalloc_max_bytes.argtypes = []
+_lib.rglru_forward_noalloc_max_bytes.restype = _sz
 _lib.rglru_forward_planned.argtypes = [_vp] * 10 + [_i] * 5 + [_vp, _sz, _vp, _i, _i]
 _lib.rglru_forward_planned.restype = _i
 _lib.rglru_gate_preacts.argtypes = [_vp] * 7 + [_i] * 5 + [_vp]
@@ -195,6 +199,16 @@ def rglru_forward(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, h_T, workspace, 
     _check(_lib.rglru_forward(*ptrs, *dims, _ptr(workspace, None, "workspace"),
                               workspace.numel() * workspace.element_size(), _stream(stream)),
            "rglru_forward")
+
+
+def rglru_forward_noalloc(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, h_T, stream=None):
+    """rglru_forward with the library's own fixed device workspace (no allocation)."""
+    ptrs, dims = _fwd_args(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, h_T)
+    _check(_lib.rglru_forward_noalloc(*ptrs, *dims, _stream(stream)), "rglru_forward_noalloc")
+
+
+def rglru_forward_noalloc_max_bytes() -> int:
+    return int(_lib.rglru_forward_noalloc_max_bytes())
 
 
 def rglru_forward_planned(x, conv_w, W_a, b_a, W_x, b_x, Lambda, h0, y, h_T, workspace,

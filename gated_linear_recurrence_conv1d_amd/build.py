@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "librglru.so")
 SOURCES = ["rglru_api.cpp", "rglru_gates.hip", "rglru_scan.hip", "rglru_decode.hip",
            "rglru_fused.hip", "rglru_backward.hip", "rglru_bwd_tiles.hip", "rglru_bwd_fused.hip",
-           "rglru_mqa.hip"]
+           "rglru_mqa.hip", "rglru_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

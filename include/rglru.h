@@ -131,6 +131,23 @@ rglru_status rglru_forward_planned(const void *x, const void *conv_w, const void
                                    size_t workspace_bytes, void *stream, rglru_plan plan,
                                    int chunk_len);
 
+/* rglru_forward for callers that cannot allocate device memory -- code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc: the same plans and kernels as
+ * rglru_forward (automatic plan), with no workspace argument. The workspace is a fixed array the
+ * library owns, rglru_forward_noalloc_max_bytes() = 72 MiB on each GPU it runs on (held until the
+ * process ends); its device address is looked up once per device, on that device's first call.
+ * The call allocates nothing. Shapes whose automatic plan needs more workspace than the array
+ * holds return RGLRU_ERR_UNSUPPORTED before any launch (the fused plan needs about B*T*D/4 bytes:
+ * up to 300M elements fit). All calls on one GPU share its array: calls that overlap in time on
+ * one GPU (other streams, other threads) race and must be serialised by the caller. Arguments,
+ * layouts, checks and other errors as for rglru_forward; RGLRU_ERR_HIP if the array cannot be
+ * located on the current device. */
+rglru_status rglru_forward_noalloc(const void *x, const void *conv_w, const void *W_a,
+                                   const float *b_a, const void *W_x, const float *b_x,
+                                   const float *Lambda, const float *h0, void *y, float *h_T,
+                                   int B, int T, int D, int H, rglru_dtype dt, void *stream);
+size_t rglru_forward_noalloc_max_bytes(void);
+
 /* The gate projections alone (conv + block-diagonal matmuls + biases), as the forward computes
  * them before its scan. pre [B][T][D] holds one (pa, px) pair per element: two fp16 values
  * (pa in the low half) for bf16, two fp32 values (pa first) for fp32. */
