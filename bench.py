@@ -70,23 +70,48 @@ def measured_traffic(kernel: str, workload: str, key="hbm_bytes_per_launch", sou
         return None
 
 
+# Two counter passes (rocprofv3 collects one pass per run: at most 8 SQ counters each).
+PMC_PASSES = (
+    ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES",
+     "SQ_ACTIVE_INST_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "GRBM_GUI_ACTIVE"],
+    ["SQ_INSTS_VALU_TRANS_F32", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY",
+     "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE"],
+)
+# VALU issue model (cycles of one SIMD): a full-rate wave64 operation takes 2 cycles (32 lanes per
+# cycle: 157.3 TFLOP/s fp32 = 256 CUs x 4 SIMDs x 2.4 GHz x 32 lanes x 2 flops per FMA), a
+# transcendental (exp2, rcp, sqrt, rsq, log) a quarter of that rate, 8 cycles (measured).
+VALU_CYCLES, TRANS_CYCLES, SIMDS, CLOCK_GHZ, XCDS = 2.0, 8.0, 1024, 2.4, 8
+
 PROFILE_CMDS = {
     "trace": "rocprofv3 --kernel-trace --stats -d OUT/trace -o bench --output-format csv -- "
-             "python3 REPO/bench.py --no-cpu-baseline",
+             "python3 REPO/bench.py --no-cpu-baseline --no-plan-legs",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'fused_forward|copyBuffer' -d "
              "OUT/fetch -o fetch --output-format csv -- python3 REPO/bench.py --steps 5 "
-             "--warmup 5 --no-cpu-baseline --no-decode --no-backward --copy-calibration 256",
+             "--warmup 5 --no-cpu-baseline --no-decode --no-backward --no-mqa --no-plan-legs "
+             "--copy-calibration 256",
     "write": "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'fused_forward|copyBuffer' -d "
              "OUT/write -o write --output-format csv -- python3 REPO/bench.py --steps 5 "
-             "--warmup 5 --no-cpu-baseline --no-decode --no-backward --copy-calibration 256",
+             "--warmup 5 --no-cpu-baseline --no-decode --no-backward --no-mqa --no-plan-legs "
+             "--copy-calibration 256",
     "bwd_fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "
                  "'tile_|bwd_|wt_prep|dxc_|conv_bwd|dw_|colsum|copyBuffer' -d OUT/bfetch -o fetch "
                  "--output-format csv -- python3 REPO/bench.py --steps 5 --warmup 5 "
-                 "--no-cpu-baseline --no-decode --bwd-warmup 2 --bwd-reps 3 --copy-calibration 256",
+                 "--no-cpu-baseline --no-decode --no-mqa --no-plan-legs --bwd-warmup 2 "
+                 "--bwd-reps 3 --copy-calibration 256",
     "bwd_write": "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex "
                  "'tile_|bwd_|wt_prep|dxc_|conv_bwd|dw_|colsum|copyBuffer' -d OUT/bwrite -o write "
                  "--output-format csv -- python3 REPO/bench.py --steps 5 --warmup 5 "
-                 "--no-cpu-baseline --no-decode --bwd-warmup 2 --bwd-reps 3 --copy-calibration 256",
+                 "--no-cpu-baseline --no-decode --no-mqa --no-plan-legs --bwd-warmup 2 "
+                 "--bwd-reps 3 --copy-calibration 256",
+    "leg_trace": "rocprofv3 --kernel-trace --stats -d OUT/trace_W -o bench --output-format csv -- "
+                 "python3 REPO/bench.py --workload W --steps 20 --warmup 10 --no-cpu-baseline "
+                 "--no-backward --no-decode --no-mqa --no-plan-legs",
+    "pmc1": "rocprofv3 --pmc " + " ".join(PMC_PASSES[0]) + " -d OUT/pmc1 -o run "
+            "--output-format csv -- python3 REPO/bench.py --steps 5 --warmup 2 --no-cpu-baseline "
+            "--no-backward --no-decode --no-mqa --no-plan-legs",
+    "pmc2": "rocprofv3 --pmc " + " ".join(PMC_PASSES[1]) + " -d OUT/pmc2 -o run "
+            "--output-format csv -- python3 REPO/bench.py --steps 5 --warmup 2 --no-cpu-baseline "
+            "--no-backward --no-decode --no-mqa --no-plan-legs",
 }
 
 
@@ -175,7 +200,113 @@ def backward_traffic_summary(fetch_csv, write_csv, workload, copy_mib=256):
     print(open(path).read(), end="")
 
 
-def trace_summary(stats_csv, workload, bench_line_path=None):
+def counter_summary(p1_csv, p2_csv, workload):
+    """Per-launch instruction and busy counts of every kernel of the bench's forward (fused plan
+    and the split plan's stages) from the two counter passes of PMC_PASSES, with the derived
+    rates. The first dispatch of each kernel (cold caches, code load) is left out."""
+    import collections
+    from workloads import WORKLOADS
+    w = [v for v in WORKLOADS.values() if v.name == workload][0]
+    n = w.B * w.T * w.D
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(list)
+    for p, path in ((1, p1_csv), (2, p2_csv)):
+        disp = collections.defaultdict(dict)
+        for r in _counter_rows(path):
+            if "rglru::" not in r["Kernel_Name"]:
+                continue  # torch's input set-up, the runtime's copies
+            k = r["Kernel_Name"].replace("void ", "").split("(")[0].replace("rglru::", "")
+            disp[(k, r["Dispatch_Id"])][r["Counter_Name"]] = float(r["Counter_Value"])
+            disp[(k, r["Dispatch_Id"])]["_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        seen = set()
+        for (k, did) in sorted(disp, key=lambda kd: int(kd[1])):
+            if k not in seen:
+                seen.add(k)
+                continue
+            for c, v in disp[(k, did)].items():
+                if c == "_ns":
+                    if p == 1:
+                        dur[k].append(v)
+                else:
+                    vals[k][f"p{p}:{c}"].append(v)
+    mean = lambda xs: sum(xs) / len(xs) if xs else float("nan")
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.txt")
+    with open(path, "w") as f:
+        f.write("# Instruction and busy counters per launch of the forward's kernels (rocprofv3).\n")
+        f.write("# Made by (REPO = this repository, OUT = a scratch directory; run from /tmp):\n")
+        f.write(f"#   {PROFILE_CMDS['pmc1']}\n#   {PROFILE_CMDS['pmc2']}\n")
+        f.write("#   python3 REPO/bench.py --counter-summary OUT/pmc1/run_counter_collection.csv "
+                "OUT/pmc2/run_counter_collection.csv\n")
+        f.write("# Means over the dispatches of each kernel after its first. Derived rates:\n"
+                "#   cycles = GRBM_GUI_ACTIVE / 8 (one count per XCD); simd_cycles = 1024 * cycles\n"
+                "#   mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / simd_cycles\n"
+                f"#   valu_issue = ({VALU_CYCLES:g} * (VALU - MFMA - TRANS) + {TRANS_CYCLES:g} * TRANS)"
+                " / simd_cycles  (the issue model of the ALU roofline)\n"
+                "#   valu_active_per_wave = SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES (share of a wave's\n"
+                "#     life spent issuing VALU; both in quad-cycles)\n"
+                "#   wait_any / wait_inst = SQ_WAIT_ANY / SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES\n"
+                "#   lds_bank_conflict = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS\n"
+                "#   per_element: over B*T*D of the workload\n")
+        f.write(f"workload: {workload}\n")
+        f.write(f"source_hash: {kernel_source_hash()}\n")
+        for k in sorted(vals, key=lambda k: -mean(dur[k])):
+            v = {c: mean(xs) for c, xs in vals[k].items()}
+            valu, mfma = v.get("p1:SQ_INSTS_VALU", 0.0), v.get("p1:SQ_INSTS_MFMA", 0.0)
+            trans = v.get("p2:SQ_INSTS_VALU_TRANS_F32", 0.0)
+            cyc = v.get("p1:GRBM_GUI_ACTIVE", float("nan")) / XCDS
+            simd_cyc = SIMDS * cyc
+            issue = VALU_CYCLES * (valu - mfma - trans) + TRANS_CYCLES * trans
+            wc1, wc2 = v.get("p1:SQ_WAVE_CYCLES", float("nan")), v.get("p2:SQ_WAVE_CYCLES",
+                                                                         float("nan"))
+            lds_act = v.get("p2:SQ_ACTIVE_INST_LDS", 0.0)
+            f.write(f"[{k}]\n")
+            f.write(f"  dispatches: {len(dur[k])}\n")
+            f.write(f"  duration_us: {mean(dur[k]) / 1e3:.2f}\n")
+            f.write(f"  clock_ghz_est: {cyc / mean(dur[k]):.3f}\n")
+            f.write(f"  waves: {v.get('p1:SQ_WAVES', 0):.0f}\n")
+            f.write(f"  valu_insts: {valu - mfma:.0f}\n")
+            f.write(f"  trans_insts: {trans:.0f}\n")
+            f.write(f"  mfma_insts: {mfma:.0f}\n")
+            f.write(f"  salu_insts: {v.get('p1:SQ_INSTS_SALU', 0):.0f}\n")
+            f.write(f"  lds_insts: {v.get('p1:SQ_INSTS_LDS', 0):.0f}\n")
+            f.write(f"  valu_per_element: {(valu - mfma) * 64 / n:.2f}\n")
+            f.write(f"  trans_per_element: {trans * 64 / n:.2f}\n")
+            f.write(f"  mfma_busy: {v.get('p1:SQ_VALU_MFMA_BUSY_CYCLES', 0) / simd_cyc:.4f}\n")
+            f.write(f"  valu_issue: {issue / simd_cyc:.4f}\n")
+            f.write(f"  valu_active_per_wave: {v.get('p1:SQ_ACTIVE_INST_VALU', 0) / wc1:.4f}\n")
+            f.write(f"  wait_any: {v.get('p2:SQ_WAIT_ANY', 0) / wc2:.4f}\n")
+            f.write(f"  wait_inst: {v.get('p2:SQ_WAIT_INST_ANY', 0) / wc2:.4f}\n")
+            f.write(f"  lds_bank_conflict: "
+                    f"{(v.get('p2:SQ_LDS_BANK_CONFLICT', 0) / lds_act) if lds_act else 0.0:.4f}\n")
+    print(open(path).read(), end="")
+
+
+def measured_counters(kernel: str, workload: str):
+    """The [kernel] block of the committed counter summary as a dict of floats, if it was taken on
+    the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    out, cur, top = {}, None, {}
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        if line.startswith("["):
+            cur = line.strip()[1:-1]
+            out[cur] = {}
+        elif ":" in line:
+            k, v = (t.strip() for t in line.split(":", 1))
+            (out[cur] if cur else top)[k] = v
+    if top.get("source_hash") != kernel_source_hash():
+        return None
+    blk = next((b for name, b in out.items() if name.startswith(kernel)), None)
+    try:
+        return {k: float(v) for k, v in blk.items()} if blk else None
+    except ValueError:
+        return None
+
+
+def trace_summary(stats_csv, workload, bench_line_path=None, key="rg2b"):
     """Condensed rocprofv3 --kernel-trace --stats summary (per-kernel calls and durations)."""
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
@@ -183,9 +314,14 @@ def trace_summary(stats_csv, workload, bench_line_path=None):
     with open(path, "w") as f:
         f.write("# rocprofv3 kernel-trace statistics of the default bench run.\n")
         f.write("# Made by (REPO = this repository, OUT = a scratch directory; run from /tmp):\n")
-        f.write(f"#   {PROFILE_CMDS['trace']}\n")
-        f.write("#   python3 REPO/bench.py --trace-summary OUT/trace/bench_kernel_stats.csv "
-                "[OUT/trace/stdout.txt]\n")
+        if key == "rg2b":
+            f.write(f"#   {PROFILE_CMDS['trace']}\n")
+            f.write("#   python3 REPO/bench.py --trace-summary OUT/trace/bench_kernel_stats.csv "
+                    "[OUT/trace/stdout.txt]\n")
+        else:
+            f.write(f"#   {PROFILE_CMDS['leg_trace'].replace('_W', '_' + key).replace(' W ', ' ' + key + ' ')}\n")
+            f.write(f"#   python3 REPO/bench.py --workload {key} --trace-summary "
+                    f"OUT/trace_{key}/bench_kernel_stats.csv [OUT/trace_{key}/stdout.txt]\n")
         f.write(f"workload: {workload}\n")
         f.write(f"source_hash: {kernel_source_hash()}\n")
         f.write(f"{'calls':>7} {'avg_us':>9} {'min_us':>9} {'max_us':>9}  kernel\n")
@@ -329,23 +465,107 @@ def mqa_leg(torch, rg, warmup=20, reps=50):
                          "algorithmic_flops": flops}}
 
 
-def cpu_baseline(w, inp, min_seconds=2.0):
-    """The fp64 oracle, as it stands, on the host cores (OpenMP over (sequence, head)): whole
-    forwards of the full workload, repeated until min_seconds of wall time have passed (a few
-    tens of core-seconds on a many-core host), reported as the mean rate."""
-    import oracle
+def plan_legs(torch, rg, names=("long", "rg9b"), warmup=10, reps=30):
+    """The long-sequence (B1 T65536) and 9B-shaped (B16 T4096 D4096) layers under the fused plan
+    and the chunked split plan, each call bracketed by events on the launch stream, with its HBM
+    roofline on the plan's algorithmic bytes, and the plan the automatic choice takes."""
+    from workloads import WORKLOADS, make_inputs, to_device
+    out = {}
+    for name in names:
+        w = WORKLOADS[name]
+        inp = make_inputs(w, seed=0)
+        g = to_device(inp)
+        del inp
+        B, T, D, H = w.B, w.T, w.D, w.H
+        io = g["x"].dtype
+        n = B * T * D
+        eb, pb = (2, 4) if io == torch.bfloat16 else (4, 8)
+        param_bytes = 2 * H * (D // H) ** 2 * eb + 4 * D * eb + 3 * 4 * D
+        state_bytes = (8 if g["h0"] is not None else 4) * B * D
+        y = torch.empty_like(g["x"])
+        hT = torch.empty((B, D), dtype=torch.float32, device=g["x"].device)
+        auto, _ = rg.rglru_forward_plan_info(B, T, D, H, io)
+        leg = {"workload": w.name, "auto_plan": auto}
+        for plan in ("fused", "chunked"):
+            nb = rg.rglru_forward_workspace_size_planned(B, T, D, H, io, plan, 0)
+            if nb == 0:
+                leg[plan] = None
+                continue
+            ws = torch.empty(nb, dtype=torch.uint8, device=g["x"].device)
 
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.forward(inp["x"], inp["conv_w"], inp["W_a"], inp["b_a"], inp["W_x"], inp["b_x"],
-                       inp["Lam"], inp["h0"])
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    return {"value": reps * w.elements / dt, "unit": "tokens·channels/s",
-            "cores": oracle.threads(), "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"{reps} full forwards of B={w.B} T={w.T} D={w.D} H={w.H}, fp64"}
+            def call():
+                rg.rglru_forward_planned(g["x"], g["conv_w"], g["W_a"], g["b_a"], g["W_x"],
+                                         g["b_x"], g["Lam"], g["h0"], y, hT, ws, plan, 0)
+
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            if plan == "fused":  # x in, y out, once
+                nbytes = n * 2 * eb + param_bytes + state_bytes
+            else:  # gates: x in, pre-activations out; scan: x and pre-activations in, y out
+                nbytes = n * (3 * eb + 2 * pb) + 2 * param_bytes + state_bytes
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            leg[plan] = {"ms": round(ms, 4), "algorithmic_bytes": nbytes, "gbs": round(gbs, 1),
+                         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                         "value": round(n / (ms * 1e-3), 1)}
+            del ws
+        timed = {p: leg[p]["ms"] for p in ("fused", "chunked") if leg.get(p)}
+        leg["fastest"] = min(timed, key=timed.get) if timed else None
+        out[name] = leg
+        del g, y, hT
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(w, inp, min_seconds=10.0, one_thread_seconds=5.0):
+    """The fp64 oracle, as it stands, on the host cores (OpenMP over (sequence, head)): whole
+    forwards of the full workload, repeated until min_seconds of wall time have passed, reported
+    as the mean rate; beside it the same oracle on one thread over a bounded sample (whole
+    forwards of the workload's first sequence alone), and the 1-thread rate of the CPU-checkable
+    fp32 configuration."""
+    import oracle
+    from workloads import WORKLOADS, make_inputs
+
+    def rate(x, conv_w, W_a, b_a, W_x, b_x, Lam, h0, elements, seconds):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.forward(x, conv_w, W_a, b_a, W_x, b_x, Lam, h0)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= seconds:
+                return reps, dt, reps * elements / dt
+
+    args = (inp["x"], inp["conv_w"], inp["W_a"], inp["b_a"], inp["W_x"], inp["b_x"], inp["Lam"],
+            inp["h0"])
+    cores = oracle.threads()
+    reps, dt, v = rate(*args, w.elements, min_seconds)
+    out = {"value": v, "unit": "tokens·channels/s", "cores": cores, "kind": "oracle",
+           "seconds": round(dt, 3),
+           "sample": f"{reps} full forwards of B={w.B} T={w.T} D={w.D} H={w.H}, fp64"}
+    try:
+        oracle.set_threads(1)
+        one = tuple(a[:1] if (a is not None and k in (0, 7)) else a for k, a in enumerate(args))
+        r1, d1, v1 = rate(*one, w.elements // w.B, one_thread_seconds)
+        t = make_inputs(WORKLOADS["tiny"], seed=0)
+        tt = WORKLOADS["tiny"]
+        r2, d2, v2 = rate(t["x"], t["conv_w"], t["W_a"], t["b_a"], t["W_x"], t["b_x"], t["Lam"],
+                          t["h0"], tt.elements, 1.0)
+        out["one_thread"] = {"value": v1, "unit": "tokens·channels/s", "cores": 1,
+                             "seconds": round(d1, 3),
+                             "sample": f"{r1} forwards of one sequence (B=1) of the same workload"}
+        out["one_thread_tiny"] = {"value": v2, "unit": "tokens·channels/s", "cores": 1,
+                                  "seconds": round(d2, 3),
+                                  "sample": f"{r2} forwards of {tt.name}"}
+    finally:
+        oracle.set_threads(cores)
+    return out
 
 
 def main():
@@ -358,6 +578,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-mqa", action="store_true", help="skip the local-attention leg")
+    ap.add_argument("--no-plan-legs", action="store_true",
+                    help="skip the long-sequence and 9B-shaped layers under the fused and chunked "
+                         "plans")
     ap.add_argument("--bwd-warmup", type=int, default=200)
     ap.add_argument("--bwd-reps", type=int, default=100)
     ap.add_argument("--backward-traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -369,20 +592,27 @@ def main():
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_fused_<workload>.txt from two rocprofv3 counter "
                          "passes and exit (no GPU needed)")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("PMC1_CSV", "PMC2_CSV"),
+                    help="write profiles/counters_<workload>.txt from the two counter passes and "
+                         "exit (no GPU needed)")
     ap.add_argument("--trace-summary", nargs="+", metavar="CSV",
                     help="write profiles/kernel_trace_fused_<workload>.txt from a rocprofv3 "
                          "kernel_stats.csv (and optionally the bench stdout) and exit")
     args = ap.parse_args()
-    if args.traffic_summary or args.trace_summary or args.backward_traffic_summary:
+    if (args.traffic_summary or args.trace_summary or args.backward_traffic_summary
+            or args.counter_summary):
         from workloads import WORKLOADS
         wname = WORKLOADS[args.workload].name
+        if args.counter_summary:
+            counter_summary(*args.counter_summary, wname)
         if args.traffic_summary:
             traffic_summary(*args.traffic_summary, wname)
         if args.backward_traffic_summary:
             backward_traffic_summary(*args.backward_traffic_summary, wname)
         if args.trace_summary:
             trace_summary(args.trace_summary[0], wname,
-                          args.trace_summary[1] if len(args.trace_summary) > 1 else None)
+                          args.trace_summary[1] if len(args.trace_summary) > 1 else None,
+                          args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -486,6 +716,31 @@ def main():
                 "traffic": traffic, "kernel": dom, "kernel_ms": round(kd["ms"], 4),
                 "algorithmic_bytes": kd["bytes"]}
 
+    # The fused kernel against its other two ceilings: the gate contraction on the matrix cores
+    # (algorithmic flops, 2 * n * 2Dh) and the vector ALU (issue cycles of the instructions the
+    # kernel executes, counted once by rocprofv3 on the current sources; null if the committed
+    # counter summary was taken on other sources).
+    extra_roofs = {}
+    if plan == "fused":
+        flops = 2.0 * n * 2 * (D // H)
+        tf = flops / (ms * 1e-3) / 1e12
+        extra_roofs["roofline_mfma"] = {"bound": "mfma", "achieved": round(tf, 1),
+                                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                        "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                        "flops": flops, "kernel": "fused"}
+        cnt = measured_counters("fused_forward", w.name)
+        alu = None
+        if cnt:
+            issue = (VALU_CYCLES * (cnt["valu_insts"] - cnt["trans_insts"])
+                     + TRANS_CYCLES * cnt["trans_insts"])
+            ach = issue / (ms * 1e-3) / 1e9
+            peak = SIMDS * CLOCK_GHZ
+            alu = {"bound": "alu", "achieved": round(ach, 1), "peak": peak,
+                   "unit": "G SIMD-cycles/s", "frac": round(ach / peak, 4),
+                   "valu_per_element": cnt["valu_per_element"],
+                   "trans_per_element": cnt["trans_per_element"], "kernel": "fused"}
+        extra_roofs["roofline_alu"] = alu
+
     line = {
         "metric": METRIC,
         "value": n / (ms * 1e-3),
@@ -499,6 +754,7 @@ def main():
                    "chunk_len": chunk, "state": "f32", "io": str(io).replace("torch.", ""),
                    "rotating_buffers": R},
         "roofline": roofline,
+        **extra_roofs,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                         for kk, vv in v.items()} for k, v in kernels.items()},
         "wall_s_timed": round(wall, 4),
@@ -510,6 +766,8 @@ def main():
         line["decode"] = decode_leg(torch, rg)
     if not args.no_mqa:
         line["local_mqa"] = mqa_leg(torch, rg)
+    if not args.no_plan_legs:
+        line["plans"] = plan_legs(torch, rg)
     if args.copy_calibration:
         src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -116,7 +116,7 @@ rglru_status resolve_forward(int B, int T, int D, int H, rglru_dtype dt, rglru_p
 
 size_t fused_bytes(int B, int T, int D, int H) {
   return rglru::fused_ctrl_bytes(H) +
-         2 * rglru::fused_slots(B, T, H, D / H) * sizeof(unsigned long long);
+         rglru::fused_slots(B, T, H, D / H) * sizeof(unsigned long long);
 }
 
 // Workspace of one resolved forward plan. The split plans: control words, pre-activations, then

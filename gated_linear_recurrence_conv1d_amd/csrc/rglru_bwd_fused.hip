@@ -396,12 +396,10 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
 
 // Look-back words to the empty pattern and the control words (give-up count, tickets) to 0
 // before each launch.
+
+// Look-back words to kEmpty, control words to 0.
 __global__ void tile_bwd_reset(unsigned long long *slots, size_t n, unsigned *ctrl, int nctrl) {
-  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
-    slots[i] = kEmpty;
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < nctrl; i += blockDim.x) ctrl[i] = 0u;
+  fill_lookback(slots, n, ctrl, nctrl);
 }
 
 bool fused_backward_supported(int Dh) { return Dh == 128 || Dh == 256; }
@@ -420,8 +418,9 @@ hipError_t launch_fused_backward(const void *x, const void *y, const void *dy, c
   unsigned long long *agg = slots, *incl = slots + fused_backward_slots(B, T, D) / 2;
   {
     const size_t n = fused_backward_slots(B, T, D);
-    const unsigned blocks = static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 2048));
-    tile_bwd_reset<<<std::max(1u, blocks), 256, 0, s>>>(slots, n, ctrl, 2 + H);
+    tile_bwd_reset<<<fill_blocks(n), 256, 0, s>>>(slots, n, ctrl, 2 + H);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   // one workgroup per CU (the LDS of a tile), the same number for every head
   int dev = 0, cus = 256;

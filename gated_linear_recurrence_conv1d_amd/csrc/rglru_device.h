@@ -104,6 +104,37 @@ constexpr float kLog2e = 1.4426950408889634f;
 // bounded by kMaxSpin polls, after which the waiting tile writes NaN instead of hanging.
 constexpr unsigned long long kEmpty = ~0ull;
 constexpr unsigned kMaxSpin = 1u << 26;
+// A word that carries either a tile's aggregate (A, U) = pack2(A, U) or, later, its inclusive
+// state h: kInclTag in the low half (a NaN payload that pack2 never produces, since it
+// canonicalises NaN to 0x7FC00000, and that differs from kEmpty's) and h in the high half.
+constexpr uint32_t kInclTag = 0x7FC00001u;
+__device__ __forceinline__ unsigned long long pack_incl(float h) {
+  return static_cast<unsigned long long>(kInclTag) |
+         (static_cast<unsigned long long>(__float_as_uint(h)) << 32);
+}
+__device__ __forceinline__ bool is_incl(unsigned long long v) {
+  return static_cast<uint32_t>(v) == kInclTag;
+}
+
+// Body of the look-back resets: n words (16-byte aligned) to kEmpty with one 16-byte store per
+// lane and step, and nctrl control words to 0 (block 0).
+__device__ __forceinline__ void fill_lookback(unsigned long long *slots, size_t n, unsigned *ctrl,
+                                              int nctrl) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  ulonglong2 *s2 = reinterpret_cast<ulonglong2 *>(slots);
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n / 2;
+       i += stride)
+    s2[i] = make_ulonglong2(kEmpty, kEmpty);
+  if (blockIdx.x == 0) {
+    if (threadIdx.x == 0 && (n & 1)) slots[n - 1] = kEmpty;
+    for (int i = threadIdx.x; i < nctrl; i += blockDim.x) ctrl[i] = 0u;
+  }
+}
+// Blocks of 256 threads for a fill of n words.
+inline unsigned fill_blocks(size_t n) {
+  const size_t b = (n / 2 + 255) / 256;
+  return static_cast<unsigned>(b < 1 ? 1 : (b > 8192 ? 8192 : b));
+}
 __device__ __forceinline__ unsigned long long pack2(float lo, float hi) {
   if (lo != lo) lo = __builtin_nanf("");
   return static_cast<unsigned long long>(__float_as_uint(lo)) |

@@ -26,9 +26,11 @@
 //      predecessor tiles of the same (sequence, head), combining aggregates until an inclusive
 //      state (or the sequence start) is found, publish this tile's inclusive state;
 //   6. fix-up h_t = P_t * carry + S_t and store y (and h_T for the last tile).
-// Each published value is one 64-bit word (two fp32) written and read with relaxed agent-scope
-// atomics, so no fences are needed; a small fill kernel resets the words to an all-ones
-// "not yet" pattern (a NaN pair the kernel never writes) and the tickets to 0 before each launch.
+// Each (tile, channel) has one 64-bit word, written and read with relaxed agent-scope atomics
+// (self-contained, so no fences are needed). It moves from "empty" (all ones, set by a small fill
+// kernel before each launch, which also zeroes the tickets) to the aggregate (A, U) to the
+// inclusive state (a NaN tag in the low half, h in the high half); one lane writes both, so a
+// reader never sees them out of order.
 // Because the look-back combines whatever predecessors have published so far, the association
 // order of the carry (not the math) depends on timing: results are reproducible to the fp32
 // rounding of the carried state, not bit for bit.
@@ -75,14 +77,10 @@ __device__ __forceinline__ bf16x8_t f32x8_to_bf16x8(const float *p) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-// Control words: [0] unused, [1] count of lanes that gave up waiting (diagnostic), [2 + p] the
-// tile ticket of (head, part) pair p.
+// Look-back words to kEmpty and control words to 0: [0] unused, [1] count of lanes that gave up
+// waiting, [2 + g] the tile ticket of head g.
 __global__ void fused_reset(unsigned long long *slots, size_t n, unsigned *ctrl, int nctrl) {
-  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
-    slots[i] = kEmpty;
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < nctrl; i += blockDim.x) ctrl[i] = 0u;
+  fill_lookback(slots, n, ctrl, nctrl);
 }
 
 __global__ void clear_words(unsigned *p, int n) {
@@ -274,7 +272,7 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
     const bf16_t *__restrict__ W_x, const float *__restrict__ b_x,
     const float *__restrict__ Lambda, const float *__restrict__ h0, bf16_t *__restrict__ y,
     float *__restrict__ h_T, int B, int T, int D, int H, int nTT, unsigned *ctrl,
-    unsigned long long *agg, unsigned long long *incl) {
+    unsigned long long *slots) {
   typedef Fused<DH> F;
   constexpr int PP = DH / 2;  // channel pairs
   // xa: the conv output in bf16, the MFMA A operand; xf: the same in fp32 for the input term;
@@ -375,16 +373,13 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
 
 
     // ---- decoupled look-back on half 0 (one channel per lane): publish this tile's aggregate
-    // and put the first predecessor's two words in flight...
+    // and put the first predecessor's word in flight...
     const size_t slot_me = (static_cast<size_t>(tc.j) * H + g) * DH + cl;  // j = tt*B + b
-    unsigned long long vi = kEmpty, va = kEmpty;
+    unsigned long long v = kEmpty;
     if (half == 0) {
-      if (tc.tt + 1 < nTT) st_relaxed(agg + slot_me, pack2(At, Ut));
-      if (tc.tt > 0) {
-        const size_t ps = ((static_cast<size_t>(tc.tt - 1) * B + tc.b) * H + g) * DH + cl;
-        vi = ld_relaxed(incl + ps);
-        va = ld_relaxed(agg + ps);
-      }
+      if (tc.tt + 1 < nTT) st_relaxed(slots + slot_me, pack2(At, Ut));
+      if (tc.tt > 0)
+        v = ld_relaxed(slots + ((static_cast<size_t>(tc.tt - 1) * B + tc.b) * H + g) * DH + cl);
     }
 
     // ... and finish the look-back: combine aggregates until an inclusive state (or the start
@@ -399,13 +394,13 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
         int jt = tc.tt - 1;
         unsigned spins = 0;
         for (;;) {
-          if (vi != kEmpty) {
-            h_in = fmaf(Aacc, lo_f(vi), Uacc);
+          if (is_incl(v)) {
+            h_in = fmaf(Aacc, hi_f(v), Uacc);
             break;
           }
-          if (va != kEmpty) {
-            Uacc = fmaf(Aacc, hi_f(va), Uacc);
-            Aacc *= lo_f(va);
+          if (v != kEmpty) {
+            Uacc = fmaf(Aacc, hi_f(v), Uacc);
+            Aacc *= lo_f(v);
             if (--jt < 0) {
               h_in = fmaf(Aacc, h0b ? *h0b : 0.0f, Uacc);
               break;
@@ -418,15 +413,12 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
             }
             __builtin_amdgcn_s_sleep(1);
           }
-          // both words in flight at once: one round trip per step
-          const size_t ps = ((static_cast<size_t>(jt) * B + tc.b) * H + g) * DH + cl;
-          vi = ld_relaxed(incl + ps);
-          va = ld_relaxed(agg + ps);
+          v = ld_relaxed(slots + ((static_cast<size_t>(jt) * B + tc.b) * H + g) * DH + cl);
         }
       }
       const float h_end = fmaf(At, h_in, Ut);
       if (tc.tt + 1 < nTT)
-        st_relaxed(incl + slot_me, pack2(h_end, 0.0f));
+        st_relaxed(slots + slot_me, pack_incl(h_end));
       else if (h_T && tc.t0 + kFusedRows == T)
         h_T[static_cast<size_t>(tc.b) * D + d] = h_end;
     }
@@ -479,7 +471,7 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
   }
 }
 
-size_t fused_ctrl_bytes(int H) { return (static_cast<size_t>(2 + 2 * H) * 4 + 255) / 256 * 256; }
+size_t fused_ctrl_bytes(int H) { return (static_cast<size_t>(2 + H) * 4 + 255) / 256 * 256; }
 
 size_t fused_slots(int B, int T, int H, int Dh) {
   const size_t nTT = (T + kFusedRows - 1) / kFusedRows;
@@ -500,11 +492,9 @@ hipError_t launch_fused(const void *x, const void *conv_w, const void *W_a, cons
   const int nTT = (T + kFusedRows - 1) / kFusedRows;
   const size_t nslot = fused_slots(B, T, H, Dh);
   unsigned *ctrl = static_cast<unsigned *>(ctrl_ws);
-  unsigned long long *agg =
+  unsigned long long *slots =
       reinterpret_cast<unsigned long long *>(static_cast<char *>(ctrl_ws) + fused_ctrl_bytes(H));
-  unsigned long long *incl = agg + nslot;
-  const unsigned rblocks = static_cast<unsigned>(std::min<size_t>((2 * nslot + 255) / 256, 4096));
-  fused_reset<<<rblocks, 256, 0, s>>>(agg, 2 * nslot, ctrl, 2 + 2 * H);
+  fused_reset<<<fill_blocks(nslot), 256, 0, s>>>(slots, nslot, ctrl, 2 + H);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int dev = 0, cus = 256;
@@ -521,7 +511,7 @@ hipError_t launch_fused(const void *x, const void *conv_w, const void *W_a, cons
   case DHV: {                                                                                   \
     const int per = std::max(1, (cus + H - 1) / H);                                             \
     fused_forward<DHV><<<H * per, Fused<DHV>::kThreads, 0, s>>>(                                \
-        xx, cw, wa, b_a, wx, b_x, Lambda, h0, yy, h_T, B, T, D, H, nTT, ctrl, agg, incl);       \
+        xx, cw, wa, b_a, wx, b_x, Lambda, h0, yy, h_T, B, T, D, H, nTT, ctrl, slots);           \
     break;                                                                                      \
   }
   switch (Dh) {

@@ -50,8 +50,8 @@ hipError_t launch_clear_words(unsigned *p, int n, hipStream_t s);
 // Single-pass fused forward (bf16 I/O, Dh in {32, 64, 128, 256}, T * D < 2^31 so that offsets
 // within one sequence fit in 32 bits): conv + MFMA gates + gate
 // nonlinearity + scan with a decoupled look-back across 64-step time tiles. ctrl_ws:
-// fused_ctrl_bytes(H) of control words followed by 2 * fused_slots() 64-bit look-back words;
-// both are reset by the launcher before the main kernel.
+// fused_ctrl_bytes(H) of control words followed by fused_slots() 64-bit look-back words (one per
+// tile and channel); both are reset by the launcher before the main kernel.
 bool fused_supported(int io, int T, int D, int Dh);
 size_t fused_ctrl_bytes(int H);
 size_t fused_slots(int B, int T, int H, int Dh);

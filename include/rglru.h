@@ -137,8 +137,8 @@ rglru_status rglru_forward_planned(const void *x, const void *conv_w, const void
  * library owns, rglru_forward_noalloc_max_bytes() = 72 MiB on each GPU it runs on (held until the
  * process ends); its device address is looked up once per device, on that device's first call.
  * The call allocates nothing. Shapes whose automatic plan needs more workspace than the array
- * holds return RGLRU_ERR_UNSUPPORTED before any launch (the fused plan needs about B*T*D/4 bytes:
- * up to 300M elements fit). All calls on one GPU share its array: calls that overlap in time on
+ * holds return RGLRU_ERR_UNSUPPORTED before any launch (the fused plan needs about B*T*D/8 bytes:
+ * up to 600M elements fit). All calls on one GPU share its array: calls that overlap in time on
  * one GPU (other streams, other threads) race and must be serialised by the caller. Arguments,
  * layouts, checks and other errors as for rglru_forward; RGLRU_ERR_HIP if the array cannot be
  * located on the current device. */

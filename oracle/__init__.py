@@ -56,6 +56,8 @@ def _load():
         lib.rglru_oracle_backward.restype = None
         lib.rglru_oracle_threads.argtypes = []
         lib.rglru_oracle_threads.restype = ctypes.c_int
+        lib.rglru_oracle_set_threads.argtypes = [i]
+        lib.rglru_oracle_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -73,6 +75,11 @@ def _ptr(a):
 def threads() -> int:
     """Number of OpenMP threads the oracle runs with."""
     return int(_load().rglru_oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Number of OpenMP threads later oracle calls use (timing control only)."""
+    _load().rglru_oracle_set_threads(int(n))
 
 
 def forward(x, conv_w, W_a, b_a, W_x, b_x, Lam, h0=None):

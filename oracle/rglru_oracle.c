@@ -76,6 +76,15 @@ static double conv_at(const double *xs, const double *conv_w, int D, int t, int 
   return acc;
 }
 
+/* Set the number of OpenMP threads later calls use (n >= 1); a timing control only. */
+void rglru_oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int rglru_oracle_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
