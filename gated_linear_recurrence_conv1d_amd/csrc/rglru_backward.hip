@@ -23,7 +23,7 @@
 //  2. bwd_carry: per (b, d) the g entering every chunk from its right, and dh0.
 //  3. bwd_emit: per (b, d, chunk) the backward walk from that carry: writes (dpa, dpx) pairs,
 //     the direct part of dxc, and per-chunk partial sums of dpa, dpx and r dz.
-//  4. dxc_mfma / dxc_valu: dxc += [dpa dpx] [W_a ; W_x] per head (bf16 MFMA or fp32 VALU).
+//  4. dxc_mfma / dxc_valu: dxc += [dpa dpx] [W_a ; W_x] per head (fp16 MFMA or fp32 VALU).
 //  5. conv_bwd: dx from dxc and conv_w; per-chunk partials of dconv_w.
 //  6. dw_mfma / dw_valu: per head and row split, partial dW = dp^T xc with xc recomputed from x.
 //  7. colsum: fixed-order sums of all partials (deterministic: no floating-point atomics).
@@ -36,56 +36,48 @@ namespace rglru {
 
 constexpr int kBwdThreads = 256;
 
-// (dpa, dpx) pair storage. fp32 I/O: one float2 (dpa first). bf16 I/O: the pair rounded to two
-// bf16 (dpa in the low half) in `hi`, and the rounding residuals, again as a bf16 pair, in `lo`:
-// hi + lo carries about 16 significant bits, which the dW contraction needs (see dw_mfma); the
-// dxc contraction reads hi alone.
+// (dpa, dpx) pair storage. fp32 I/O: one float2 (dpa first). bf16 I/O: the pair as two fp16
+// (dpa in the low half): 11 significant bits, which the dW contraction needs (bf16's 8 left single
+// elements of dW off by a few percent of the rms; see dw_mfma), in the 4 bytes of a bf16 pair.
+// The gate gradients stay far inside fp16's range (|dp| < 65504) at the configurations measured
+// here: they scale as delta * xc, the factor 1/m of dz being cancelled by r (1 - r).
 template <typename T> struct DPair;
 template <> struct DPair<float> {
   typedef float2 type;
-  __device__ __forceinline__ static void put(type *hi, type *, size_t o, float a, float x) {
-    hi[o] = make_float2(a, x);
+  __device__ __forceinline__ static void put(type *p, size_t o, float a, float x) {
+    p[o] = make_float2(a, x);
   }
   template <int CH>
-  __device__ __forceinline__ static void put(type *hi, type *lo, size_t o, const float (&a)[CH],
+  __device__ __forceinline__ static void put(type *p, size_t o, const float (&a)[CH],
                                              const float (&x)[CH]) {
     if constexpr (CH == 2)
-      *reinterpret_cast<float4 *>(hi + o) = make_float4(a[0], x[0], a[1], x[1]);
+      *reinterpret_cast<float4 *>(p + o) = make_float4(a[0], x[0], a[1], x[1]);
     else
-      put(hi, lo, o, a[0], x[0]);
+      put(p, o, a[0], x[0]);
   }
-  __device__ __forceinline__ static void get(const type *hi, const type *, size_t o, float &a,
-                                             float &x) {
-    const float2 v = hi[o];
+  __device__ __forceinline__ static void get(const type *p, size_t o, float &a, float &x) {
+    const float2 v = p[o];
     a = v.x;
     x = v.y;
   }
 };
 template <> struct DPair<bf16_t> {
   typedef uint32_t type;
-  __device__ __forceinline__ static void put(type *hi, type *lo, size_t o, float a, float x) {
-    const uint32_t h = pack_bf16x2(a, x);
-    hi[o] = h;
-    lo[o] = pack_bf16x2(a - bf16lo(h), x - bf16hi(h));  // the differences are exact in fp32
+  __device__ __forceinline__ static void put(type *p, size_t o, float a, float x) {
+    p[o] = pack_f16x2(a, x);
   }
   template <int CH>
-  __device__ __forceinline__ static void put(type *hi, type *lo, size_t o, const float (&a)[CH],
+  __device__ __forceinline__ static void put(type *p, size_t o, const float (&a)[CH],
                                              const float (&x)[CH]) {
-    if constexpr (CH == 2) {
-      const uint32_t h0 = pack_bf16x2(a[0], x[0]), h1 = pack_bf16x2(a[1], x[1]);
-      *reinterpret_cast<uint2 *>(hi + o) = make_uint2(h0, h1);
-      *reinterpret_cast<uint2 *>(lo + o) =
-          make_uint2(pack_bf16x2(a[0] - bf16lo(h0), x[0] - bf16hi(h0)),
-                     pack_bf16x2(a[1] - bf16lo(h1), x[1] - bf16hi(h1)));
-    } else {
-      put(hi, lo, o, a[0], x[0]);
-    }
+    if constexpr (CH == 2)
+      *reinterpret_cast<uint2 *>(p + o) = make_uint2(pack_f16x2(a[0], x[0]), pack_f16x2(a[1], x[1]));
+    else
+      put(p, o, a[0], x[0]);
   }
-  __device__ __forceinline__ static void get(const type *hi, const type *lo, size_t o, float &a,
-                                             float &x) {
-    const uint32_t h = hi[o], l = lo[o];
-    a = bf16lo(h) + bf16lo(l);
-    x = bf16hi(h) + bf16hi(l);
+  __device__ __forceinline__ static void get(const type *p, size_t o, float &a, float &x) {
+    const uint32_t h = p[o];
+    a = f16lo(h);
+    x = f16hi(h);
   }
 };
 
@@ -116,6 +108,18 @@ template <> struct Lanes<bf16_t, 2> {
     *reinterpret_cast<uint32_t *>(p + i) = pack_bf16x2(v[0], v[1]);
   }
 };
+template <> struct Lanes<bf16_t, 4> {
+  __device__ __forceinline__ static void load(const bf16_t *p, size_t i, float (&v)[4]) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p + i);
+    v[0] = bf16lo(u.x);
+    v[1] = bf16hi(u.x);
+    v[2] = bf16lo(u.y);
+    v[3] = bf16hi(u.y);
+  }
+  __device__ __forceinline__ static void store(bf16_t *p, size_t i, const float (&v)[4]) {
+    *reinterpret_cast<uint2 *>(p + i) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  }
+};
 template <> struct Lanes<float, 1> {
   __device__ __forceinline__ static void load(const float *p, size_t i, float (&v)[1]) { v[0] = p[i]; }
   __device__ __forceinline__ static void store(float *p, size_t i, const float (&v)[1]) { p[i] = v[0]; }
@@ -130,6 +134,53 @@ template <> struct Lanes<float, 2> {
     *reinterpret_cast<float2 *>(p + i) = make_float2(v[0], v[1]);
   }
 };
+// Storage of dxc, the gradient of the conv output: fp32 for fp32 I/O; fp16 for bf16 I/O (2^-11
+// of rounding, a quarter of the bf16 output's, in half the bytes: it is written and read back
+// twice per element; its range is that of delta, far inside fp16's at the configurations measured
+// here). One element (ld / st) or CH consecutive ones (load / store).
+template <typename T, int CH = 1> struct DxcS;
+template <int CH> struct DxcS<float, CH> {
+  typedef float type;
+  __device__ __forceinline__ static float ld(const type *p, size_t i) { return p[i]; }
+  __device__ __forceinline__ static void st(type *p, size_t i, float v) { p[i] = v; }
+  __device__ __forceinline__ static void load(const type *p, size_t i, float (&v)[CH]) {
+    Lanes<float, CH>::load(p, i, v);
+  }
+  __device__ __forceinline__ static void store(type *p, size_t i, const float (&v)[CH]) {
+    Lanes<float, CH>::store(p, i, v);
+  }
+};
+template <int CH> struct DxcS<bf16_t, CH> {
+  typedef uint16_t type;
+  __device__ __forceinline__ static float ld(const type *p, size_t i) {
+    return f16lo(static_cast<uint32_t>(p[i]));
+  }
+  __device__ __forceinline__ static void st(type *p, size_t i, float v) {
+    p[i] = static_cast<uint16_t>(pack_f16x2(v, 0.0f));
+  }
+  __device__ __forceinline__ static void load(const type *p, size_t i, float (&v)[CH]) {
+    if constexpr (CH == 4) {
+      const uint2 u = *reinterpret_cast<const uint2 *>(p + i);
+      v[0] = f16lo(u.x);
+      v[1] = f16hi(u.x);
+      v[2] = f16lo(u.y);
+      v[3] = f16hi(u.y);
+    } else if constexpr (CH == 2) {
+      const uint32_t u = *reinterpret_cast<const uint32_t *>(p + i);
+      v[0] = f16lo(u);
+      v[1] = f16hi(u);
+    } else {
+      v[0] = ld(p, i);
+    }
+  }
+  __device__ __forceinline__ static void store(type *p, size_t i, const float (&v)[CH]) {
+    if constexpr (CH == 2)
+      *reinterpret_cast<uint32_t *>(p + i) = pack_f16x2(v[0], v[1]);
+    else
+      st(p, i, v[0]);
+  }
+};
+
 // CH pre-activation pairs in their storage layout (PrePair) as one access.
 template <typename T, int CH> struct PreLanes {
   typedef typename PrePair<T>::type P;
@@ -227,7 +278,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_emit(
     const T *__restrict__ y, const T *__restrict__ dy, const float *__restrict__ h0,
     const T *__restrict__ conv_w, const float *__restrict__ Lambda,
     const float *__restrict__ carry, typename DPair<T>::type *__restrict__ dpre,
-    typename DPair<T>::type *__restrict__ dlo, float *__restrict__ dxc, float *__restrict__ part,
+    typename DxcS<T>::type *__restrict__ dxc, float *__restrict__ part,
     int B, int Tn, int D, int nC) {
   const int DL = D / CH;
   const size_t idx = static_cast<size_t>(blockIdx.x) * kBwdThreads + threadIdx.x;
@@ -326,8 +377,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_emit(
           xw[0][k] = G.xn[u][k];
         }
         const size_t o = base + static_cast<size_t>(t) * D;
-        DPair<T>::template put<CH>(dpre, dlo, o, dpa, dpx);
-        Lanes<float, CH>::store(dxc, o, dd);
+        DPair<T>::template put<CH>(dpre, o, dpa, dpx);
+        DxcS<T, CH>::store(dxc, o, dd);
       }
     }
   };
@@ -349,11 +400,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_emit(
   }
 }
 
-// ---- 4a: dxc += [dpa dpx] [W_a ; W_x] on MFMA (bf16, Dh in {32, 64, 128, 256}) -------------
-// wti[g][i][2o + q] = W_q[g][o][i] (q = 0: W_a, 1: W_x): the weights transposed and interleaved so
-// that the contraction index k = 2o + q matches the (dpa, dpx) pair layout of dpre.
+// ---- 4a: dxc += [dpa dpx] [W_a ; W_x] on MFMA (bf16 I/O, Dh in {32, 64, 128, 256}) ----------
+// wti[g][i][2o + q] = W_q[g][o][i] (q = 0: W_a, 1: W_x) as fp16: the weights transposed and
+// interleaved so that the contraction index k = 2o + q matches the (dpa, dpx) fp16 pair layout of
+// dpre (fp16 holds every bf16 weight of magnitude 2^-14 .. 65504 exactly).
 __global__ void wt_prep(const bf16_t *__restrict__ W_a, const bf16_t *__restrict__ W_x,
-                        bf16_t *__restrict__ wti, int H, int Dh) {
+                        uint16_t *__restrict__ wti, int H, int Dh) {
   const size_t n = static_cast<size_t>(H) * Dh * 2 * Dh;
   const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= n) return;
@@ -363,22 +415,23 @@ __global__ void wt_prep(const bf16_t *__restrict__ W_a, const bf16_t *__restrict
   const int g = static_cast<int>(gi / Dh);
   const int o = k >> 1;
   const bf16_t *W = (k & 1) ? W_x : W_a;
-  wti[idx] = W[(static_cast<size_t>(g) * Dh + o) * Dh + i];
+  wti[idx] = static_cast<uint16_t>(
+      pack_f16x2(bf16_to_f32(W[(static_cast<size_t>(g) * Dh + o) * Dh + i]), 0.0f));
 }
 
 template <int DH>
 __global__ __launch_bounds__(kThreads) void dxc_mfma(const uint32_t *__restrict__ dpre,
-                                                     const bf16_t *__restrict__ wti,
-                                                     float *__restrict__ dxc, int Tn, int D) {
+                                                     const uint16_t *__restrict__ wti,
+                                                     uint16_t *__restrict__ dxc, int Tn, int D) {
   typedef GateTile<DH> C;
   constexpr int K = 2 * DH;
-  constexpr int kLd = K + 8;  // LDS row stride in bf16 (16 B pad)
-  __shared__ __attribute__((aligned(16))) bf16_t lds_a[kTileRows * kLd];
+  constexpr int kLd = K + 8;  // LDS row stride in fp16 (16 B pad)
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a[kTileRows * kLd];
   const int t0 = blockIdx.x * kTileRows;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
-  // A tile: rows t0..t0+63 of this head's K = 2 DH bf16 (DH pairs), zero past T.
+  // A tile: rows t0..t0+63 of this head's K = 2 DH fp16 (DH pairs), zero past T.
   {
     constexpr int kChunks = K / 8;  // 16-byte chunks per row
     for (int q = tid; q < kTileRows * kChunks; q += kThreads) {
@@ -400,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void dxc_mfma(const uint32_t *__restrict_
   if (!active) return;
   const int lrow = lane & 31;
   const int khalf = (lane >> 5) * 8;
-  const bf16_t *wg = wti + static_cast<size_t>(g) * DH * K;
+  const uint16_t *wg = wti + static_cast<size_t>(g) * DH * K;
   f32x16_t acc[C::kGPW][C::kRPW];
 #pragma unroll
   for (int gi = 0; gi < C::kGPW; ++gi)
@@ -408,18 +461,18 @@ __global__ __launch_bounds__(kThreads) void dxc_mfma(const uint32_t *__restrict_
     for (int ri = 0; ri < C::kRPW; ++ri) acc[gi][ri] = f32x16_t{};
 #pragma unroll 2
   for (int k0 = 0; k0 < K; k0 += 16) {
-    bf16x8_t af[C::kRPW], bfr[C::kGPW];
+    f16x8_t af[C::kRPW], bfr[C::kGPW];
 #pragma unroll
     for (int ri = 0; ri < C::kRPW; ++ri)
-      af[ri] = load_bf16x8(lds_a + ((r0 + ri) * 32 + lrow) * kLd + k0 + khalf);
+      af[ri] = load_f16x8(lds_a + ((r0 + ri) * 32 + lrow) * kLd + k0 + khalf);
 #pragma unroll
     for (int gi = 0; gi < C::kGPW; ++gi)
-      bfr[gi] = load_bf16x8(wg + static_cast<size_t>((g0 + gi) * 32 + lrow) * K + k0 + khalf);
+      bfr[gi] = load_f16x8(wg + static_cast<size_t>((g0 + gi) * 32 + lrow) * K + k0 + khalf);
 #pragma unroll
     for (int gi = 0; gi < C::kGPW; ++gi)
 #pragma unroll
       for (int ri = 0; ri < C::kRPW; ++ri)
-        acc[gi][ri] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ri], bfr[gi], acc[gi][ri], 0, 0, 0);
+        acc[gi][ri] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ri], bfr[gi], acc[gi][ri], 0, 0, 0);
   }
 #pragma unroll
   for (int gi = 0; gi < C::kGPW; ++gi) {
@@ -430,8 +483,8 @@ __global__ __launch_bounds__(kThreads) void dxc_mfma(const uint32_t *__restrict_
       for (int j = 0; j < 16; ++j) {
         const int t = t0 + C::acc_row(r0 + ri, j, lane);
         if (t < Tn) {
-          float *p = dxc + (static_cast<size_t>(b) * Tn + t) * D + d;
-          *p += acc[gi][ri][j];
+          const size_t o = (static_cast<size_t>(b) * Tn + t) * D + d;
+          DxcS<bf16_t>::st(dxc, o, DxcS<bf16_t>::ld(dxc, o) + acc[gi][ri][j]);
         }
       }
   }
@@ -442,9 +495,9 @@ constexpr int kBwdValuRows = 16;
 
 template <typename T>
 __global__ __launch_bounds__(256) void dxc_valu(const typename DPair<T>::type *__restrict__ dpre,
-                                                const typename DPair<T>::type *__restrict__ dlo,
                                                 const T *__restrict__ W_a,
-                                                const T *__restrict__ W_x, float *__restrict__ dxc,
+                                                const T *__restrict__ W_x,
+                                                typename DxcS<T>::type *__restrict__ dxc,
                                                 int Tn, int D, int Dh) {
   __shared__ float sa[kBwdValuRows * 256], sx[kBwdValuRows * 256];
   const int t0 = blockIdx.x * kBwdValuRows;
@@ -455,7 +508,7 @@ __global__ __launch_bounds__(256) void dxc_valu(const typename DPair<T>::type *_
     const int t = t0 + r;
     float va = 0.0f, vx = 0.0f;
     if (t < Tn)
-      DPair<T>::get(dpre, dlo,
+      DPair<T>::get(dpre,
                     (static_cast<size_t>(b) * Tn + t) * D + static_cast<size_t>(g) * Dh + o, va, vx);
     sa[r * Dh + o] = va;
     sx[r * Dh + o] = vx;
@@ -471,7 +524,8 @@ __global__ __launch_bounds__(256) void dxc_valu(const typename DPair<T>::type *_
       acc = fmaf(sa[r * Dh + o], Elem<T>::load(W_a, wb + static_cast<size_t>(o) * Dh), acc);
       acc = fmaf(sx[r * Dh + o], Elem<T>::load(W_x, wb + static_cast<size_t>(o) * Dh), acc);
     }
-    dxc[(static_cast<size_t>(b) * Tn + t) * D + static_cast<size_t>(g) * Dh + i] += acc;
+    const size_t o = (static_cast<size_t>(b) * Tn + t) * D + static_cast<size_t>(g) * Dh + i;
+    DxcS<T>::st(dxc, o, DxcS<T>::ld(dxc, o) + acc);
   }
 }
 
@@ -479,7 +533,7 @@ __global__ __launch_bounds__(256) void dxc_valu(const typename DPair<T>::type *_
 // pcw: [B * nC][4][D] partial sums of dconv_w over each chunk.
 template <typename T, int CH>
 __global__ __launch_bounds__(kBwdThreads) void conv_bwd(const T *__restrict__ x,
-                                                        const float *__restrict__ dxc,
+                                                        const typename DxcS<T>::type *__restrict__ dxc,
                                                         const T *__restrict__ conv_w,
                                                         T *__restrict__ dx,
                                                         float *__restrict__ pcw, int B, int Tn,
@@ -501,7 +555,7 @@ __global__ __launch_bounds__(kBwdThreads) void conv_bwd(const T *__restrict__ x,
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
     if (s + k < Tn) {
-      Lanes<float, CH>::load(dxc, base + static_cast<size_t>(s + k) * D, gw[k + 1]);
+      DxcS<T, CH>::load(dxc, base + static_cast<size_t>(s + k) * D, gw[k + 1]);
     } else {
 #pragma unroll
       for (int q = 0; q < CH; ++q) gw[k + 1][q] = 0.0f;
@@ -529,7 +583,7 @@ __global__ __launch_bounds__(kBwdThreads) void conv_bwd(const T *__restrict__ x,
       const int t = t0 + u;
       if (t < e) {
         if (t + 3 < Tn) {
-          Lanes<float, CH>::load(dxc, base + static_cast<size_t>(t + 3) * D, G.gn[u]);
+          DxcS<T, CH>::load(dxc, base + static_cast<size_t>(t + 3) * D, G.gn[u]);
         } else {
 #pragma unroll
           for (int k = 0; k < CH; ++k) G.gn[u][k] = 0.0f;
@@ -579,7 +633,7 @@ __global__ __launch_bounds__(kBwdThreads) void conv_bwd(const T *__restrict__ x,
     for (int k = 0; k < CH; ++k) pcw[(prow + j) * D + d0 + k] = acc[j][k];
 }
 
-// ---- 6a: dW partials on MFMA (bf16, Dh in {128, 256}) ---------------------------------------
+// ---- 6a: dW partials on MFMA (bf16 I/O, Dh in {128, 256}) ----------------------------------
 // One workgroup: a 256 (m = 2o + q, both gates interleaved) x Dh (i) tile of head g, contracted
 // over the rows [kb, ke) of the flattened (b, t) index in steps of 32 rows; 8 waves (two per
 // SIMD) in a 4 x 2 grid, each 64 x Dh/2 (2 x Dh/64 MFMA tiles, fp32 accumulators). Per step, dp
@@ -589,13 +643,13 @@ __global__ __launch_bounds__(kBwdThreads) void conv_bwd(const T *__restrict__ x,
 // 16-byte operand reads, taken as two 8-byte halves, distinct banks too. The LDS holds two
 // steps: step s+1's loads are issued before step s's MFMAs and stored into the other buffer
 // after them, one barrier per step.
-// Precision: with both operands rounded to bf16 a dW element errs by up to 2^-9 of its largest
-// terms, and the gate gradients are heavy tailed (dz carries 1/m), so single elements of dW miss
-// by a few percent of the tensor's rms. Each operand is therefore split into bf16 hi + lo and
-// the product taken as hi*hi + lo*hi + hi*lo (the lo*lo term is below 2^-16): three MFMAs.
+// Precision: both operands in fp16 (dp as stored, xc rounded once), one MFMA per tile and k-step.
+// With bf16 operands (2^-9) a dW element erred by up to a few percent of the tensor's rms -- dW
+// sums terms of both signs and the gate gradients are heavy tailed (dz carries 1/m); fp16's 2^-11
+// brings that well inside the bound, at a third of the matrix work of a hi + lo split.
 // pw: [S][2 gates][H][Dh][Dh] fp32.
 constexpr int kDwRows = 32;            // rows per step
-constexpr int kDwLd = kDwRows + 4;     // LDS row stride in bf16 (72 bytes)
+constexpr int kDwLd = kDwRows + 4;     // LDS row stride in 16-bit words (72 bytes)
 constexpr int kDwM = 256;              // m per workgroup
 constexpr int kDwThreads = 512;
 
@@ -603,27 +657,26 @@ template <int DH> struct DwTile {
   static_assert(DH == 128 || DH == 256, "dW MFMA tile needs Dh in {128, 256}");
   static constexpr int kMt = 2 * DH / kDwM;        // m tiles per head
   static constexpr int kWN = DH / 64;              // 32-column MFMA tiles per wave
-  static constexpr int kAElems = 2 * kDwM * kDwLd;  // [hi, lo][m][k]
-  static constexpr int kBElems = 2 * DH * kDwLd;    // [hi, lo][i][k]
+  static constexpr int kAElems = kDwM * kDwLd;     // [m][k]
+  static constexpr int kBElems = DH * kDwLd;       // [i][k]
   static constexpr int kBufElems = kAElems + kBElems;
 };
 
-__device__ __forceinline__ bf16x8_t lds_read_8x2(const bf16_t *p) {
+__device__ __forceinline__ f16x8_t lds_read_f16x8(const uint16_t *p) {
   const uint2 lo = *reinterpret_cast<const uint2 *>(p);
   const uint2 hi = *reinterpret_cast<const uint2 *>(p + 4);
   const u32x4_t v = {lo.x, lo.y, hi.x, hi.y};
-  return __builtin_bit_cast(bf16x8_t, v);
+  return __builtin_bit_cast(f16x8_t, v);
 }
 
 template <int DH>
 __global__ __launch_bounds__(kDwThreads, 1) void dw_mfma(const bf16_t *__restrict__ x,
                                                          const uint32_t *__restrict__ dpre,
-                                                         const uint32_t *__restrict__ dlo,
                                                          const bf16_t *__restrict__ conv_w,
                                                          float *__restrict__ pw, int Tn, int D,
                                                          int H, int rows, int rows_per_split) {
   typedef DwTile<DH> C;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * C::kBufElems];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * C::kBufElems];
   const int mt = blockIdx.x;
   const int g = blockIdx.y;
   const int sp = blockIdx.z;
@@ -658,21 +711,15 @@ __global__ __launch_bounds__(kDwThreads, 1) void dw_mfma(const bf16_t *__restric
     }
   }
   // prefetch registers: the rows of the next step
-  u32x4_t ra[2][2];  // [hi, lo][row u]
-  u32x4_t rx[5];     // x rows r0 - 3 .. r0 + 1
-  auto load_dp = [&](int st, u32x4_t (&pa)[2][2]) {
+  u32x4_t ra[2];  // [row u]
+  u32x4_t rx[5];  // x rows r0 - 3 .. r0 + 1
+  auto load_dp = [&](int st, u32x4_t (&pa)[2]) {
     const int r0 = kb + st * kDwRows + 2 * lq;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int rr = r0 + u;
-      if (rr < ke) {
-        const size_t off = static_cast<size_t>(rr) * D + a_col;
-        pa[0][u] = *reinterpret_cast<const u32x4_t *>(dpre + off);
-        pa[1][u] = *reinterpret_cast<const u32x4_t *>(dlo + off);
-      } else {
-        pa[0][u] = u32x4_t{0u, 0u, 0u, 0u};
-        pa[1][u] = u32x4_t{0u, 0u, 0u, 0u};
-      }
+      pa[u] = rr < ke ? *reinterpret_cast<const u32x4_t *>(dpre + static_cast<size_t>(rr) * D + a_col)
+                      : u32x4_t{0u, 0u, 0u, 0u};
     }
   };
   auto load_x = [&](int st) {
@@ -686,18 +733,15 @@ __global__ __launch_bounds__(kDwThreads, 1) void dw_mfma(const bf16_t *__restric
         rx[k] = u32x4_t{0u, 0u, 0u, 0u};
     }
   };
-  // conv, hi/lo split and transposed stores of one step into buffer `buf`
-  auto store_step = [&](int st, int buf, const u32x4_t (&pa)[2][2]) {
-    bf16_t *A = lds + buf * C::kBufElems;
-    bf16_t *Bm = A + C::kAElems;
+  // conv, fp16 rounding and transposed stores of one step into buffer `buf`
+  auto store_step = [&](int st, int buf, const u32x4_t (&pa)[2]) {
+    uint16_t *A = lds + buf * C::kBufElems;
+    uint16_t *Bm = A + C::kAElems;
     // A: m = 8 lj + cc is half cc & 1 (dpa even, dpx odd) of pair cc >> 1; rows 2 lq, 2 lq + 1
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc)
-#pragma unroll
-      for (int part = 0; part < 2; ++part)
-        *reinterpret_cast<uint32_t *>(A + (part * kDwM + 8 * lj + cc) * kDwLd + 2 * lq) =
-            __builtin_amdgcn_perm(pa[part][1][cc >> 1], pa[part][0][cc >> 1],
-                                  (cc & 1) ? kHiPair : kLoPair);
+      *reinterpret_cast<uint32_t *>(A + (8 * lj + cc) * kDwLd + 2 * lq) =
+          __builtin_amdgcn_perm(pa[1][cc >> 1], pa[0][cc >> 1], (cc & 1) ? kHiPair : kLoPair);
     if (!bload) return;
     const int k0 = kb + st * kDwRows;
     const int r0 = k0 + 2 * lq;
@@ -732,12 +776,9 @@ __global__ __launch_bounds__(kDwThreads, 1) void dw_mfma(const bf16_t *__restric
       }
     }
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const uint32_t hv = pack_bf16x2(xcv[0][cc], xcv[1][cc]);
-      const uint32_t lv = pack_bf16x2(xcv[0][cc] - bf16lo(hv), xcv[1][cc] - bf16hi(hv));
-      *reinterpret_cast<uint32_t *>(Bm + (8 * lj + cc) * kDwLd + 2 * lq) = hv;
-      *reinterpret_cast<uint32_t *>(Bm + (DH + 8 * lj + cc) * kDwLd + 2 * lq) = lv;
-    }
+    for (int cc = 0; cc < 8; ++cc)
+      *reinterpret_cast<uint32_t *>(Bm + (8 * lj + cc) * kDwLd + 2 * lq) =
+          pack_f16x2(xcv[0][cc], xcv[1][cc]);
   };
 
   const int w = tid >> 6;
@@ -752,28 +793,20 @@ __global__ __launch_bounds__(kDwThreads, 1) void dw_mfma(const bf16_t *__restric
     for (int c = 0; c < C::kWN; ++c) acc[a][c] = f32x16_t{};
 
   auto mfma_step = [&](int buf) {
-    const bf16_t *A = lds + buf * C::kBufElems;
-    const bf16_t *Bm = A + C::kAElems;
+    const uint16_t *A = lds + buf * C::kBufElems;
+    const uint16_t *Bm = A + C::kAElems;
 #pragma unroll
     for (int kk = 0; kk < kDwRows; kk += 16) {
-      bf16x8_t af[2][2];  // [hi, lo][m tile]
+      f16x8_t af[2];  // [m tile]
 #pragma unroll
-      for (int part = 0; part < 2; ++part)
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-          af[part][a] = lds_read_8x2(A + (part * kDwM + wm + a * 32 + lrow) * kDwLd + kk + khalf);
+      for (int a = 0; a < 2; ++a)
+        af[a] = lds_read_f16x8(A + (wm + a * 32 + lrow) * kDwLd + kk + khalf);
 #pragma unroll
       for (int c = 0; c < C::kWN; ++c) {
-        bf16x8_t bfr[2];  // [hi, lo] of column tile c
+        const f16x8_t bfr = lds_read_f16x8(Bm + (wn + c * 32 + lrow) * kDwLd + kk + khalf);
 #pragma unroll
-        for (int part = 0; part < 2; ++part)
-          bfr[part] = lds_read_8x2(Bm + (part * DH + wn + c * 32 + lrow) * kDwLd + kk + khalf);
-#pragma unroll
-        for (int p = 0; p < 3; ++p)
-#pragma unroll
-          for (int a = 0; a < 2; ++a)
-            acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p == 1][a], bfr[p == 2],
-                                                                acc[a][c], 0, 0, 0);
+        for (int a = 0; a < 2; ++a)
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bfr, acc[a][c], 0, 0, 0);
       }
     }
   };
@@ -812,7 +845,6 @@ __global__ __launch_bounds__(kDwThreads, 1) void dw_mfma(const bf16_t *__restric
 template <typename T>
 __global__ __launch_bounds__(256) void dw_valu(const T *__restrict__ x,
                                                const typename DPair<T>::type *__restrict__ dpre,
-                                               const typename DPair<T>::type *__restrict__ dlo,
                                                const T *__restrict__ conv_w,
                                                float *__restrict__ pw, int Tn, int D, int H,
                                                int Dh, int rows, int rows_per_split) {
@@ -839,7 +871,7 @@ __global__ __launch_bounds__(256) void dw_valu(const T *__restrict__ x,
         const int m = mt * 64 + col;
         if (m < 2 * Dh) {
           float pa_, px_;
-          DPair<T>::get(dpre, dlo, rowoff + static_cast<size_t>(g) * Dh + (m >> 1), pa_, px_);
+          DPair<T>::get(dpre, rowoff + static_cast<size_t>(g) * Dh + (m >> 1), pa_, px_);
           va = (m & 1) ? px_ : pa_;
         }
         const int i = nt * 64 + col;
@@ -967,8 +999,7 @@ BwdLayout backward_layout(int B, int T, int D, int H, int io) {
   L.o_ctrl = take(kCtrlBytes);
   L.o_pre = take(L.fused ? 0 : n * pairb);
   L.o_dpre = take(n * pairb);
-  L.o_dlo = take(io == kBF16 ? n * 4 : 0);
-  L.o_dxc = take(n * sizeof(float));
+  L.o_dxc = take(n * (io == kBF16 ? 2 : 4));
   L.o_sums = take(L.fused ? 0 : P * D * sizeof(float2));
   L.o_carry = take(L.fused ? 0 : P * D * sizeof(float));
   L.o_part = take(3 * static_cast<size_t>(B) * L.nCp * D * sizeof(float));
@@ -993,8 +1024,7 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
   typedef typename DPair<T>::type DP;
   PP *pre = reinterpret_cast<PP *>(ws + L.o_pre);
   DP *dpre = reinterpret_cast<DP *>(ws + L.o_dpre);
-  DP *dlo = sizeof(T) == 2 ? reinterpret_cast<DP *>(ws + L.o_dlo) : nullptr;
-  float *dxc = reinterpret_cast<float *>(ws + L.o_dxc);
+  typename DxcS<T>::type *dxc = reinterpret_cast<typename DxcS<T>::type *>(ws + L.o_dxc);
   float2 *sums = reinterpret_cast<float2 *>(ws + L.o_sums);
   float *carry = reinterpret_cast<float *>(ws + L.o_carry);
   float *part = reinterpret_cast<float *>(ws + L.o_part);
@@ -1016,8 +1046,7 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
     if (L.fused) {
       // passes 1-3 as one tile pass (partial sums per tile of kFusedBwdRows steps)
       e = launch_fused_backward(x, y, dy, h0, dh_T, conv_w, W_a, b_a, W_x, b_x, Lambda,
-                                reinterpret_cast<uint32_t *>(dpre),
-                                reinterpret_cast<uint32_t *>(dlo), dxc, part, dh0, B, Tn, D, H,
+                                reinterpret_cast<uint32_t *>(dpre), dxc, part, dh0, B, Tn, D, H,
                                 reinterpret_cast<unsigned *>(ws + L.o_ctrl),
                                 reinterpret_cast<unsigned long long *>(ws + L.o_lb), s);
       if (e != hipSuccess) return e;
@@ -1037,15 +1066,15 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
     bwd_carry<<<lblocks, kBwdThreads, 0, s>>>(sums, dh_T, carry, dh0, B, D, L.nC);
     if (pair) {
       bwd_emit<T, 2><<<lgrid, kBwdThreads, 0, s>>>(x, pre, y, dy, h0, conv_w, Lambda, carry, dpre,
-                                                   dlo, dxc, part, B, Tn, D, L.nC);
+                                                   dxc, part, B, Tn, D, L.nC);
     } else {
       bwd_emit<T, 1><<<lgrid, kBwdThreads, 0, s>>>(x, pre, y, dy, h0, conv_w, Lambda, carry, dpre,
-                                                   dlo, dxc, part, B, Tn, D, L.nC);
+                                                   dxc, part, B, Tn, D, L.nC);
     }
   }
   if constexpr (sizeof(T) == 2) {
     if (L.mfma_dxc) {
-      bf16_t *wti = reinterpret_cast<bf16_t *>(ws + L.o_wti);
+      uint16_t *wti = reinterpret_cast<uint16_t *>(ws + L.o_wti);
       const size_t nw = static_cast<size_t>(H) * Dh * 2 * Dh;
       wt_prep<<<static_cast<unsigned>((nw + 255) / 256), 256, 0, s>>>(W_a, W_x, wti, H, Dh);
       const dim3 grid((Tn + kTileRows - 1) / kTileRows, H, B);
@@ -1063,9 +1092,15 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
   }
   if (!L.mfma_dxc) {
     const dim3 grid((Tn + kBwdValuRows - 1) / kBwdValuRows, H, B);
-    dxc_valu<T><<<grid, 256, 0, s>>>(dpre, dlo, W_a, W_x, dxc, Tn, D, Dh);
+    dxc_valu<T><<<grid, 256, 0, s>>>(dpre, W_a, W_x, dxc, Tn, D, Dh);
   }
-  if (pair) {
+  // the conv backward reads and writes 16-bit values: four channels per lane (8-byte accesses)
+  // where D allows it
+  if (sizeof(T) == 2 && D % 4 == 0) {
+    const dim3 qgrid((lblocks + 3) / 4, L.nC);
+    if constexpr (sizeof(T) == 2)
+      conv_bwd<T, 4><<<qgrid, kBwdThreads, 0, s>>>(x, dxc, conv_w, dx, pcw, B, Tn, D, L.nC);
+  } else if (pair) {
     conv_bwd<T, 2><<<lgrid, kBwdThreads, 0, s>>>(x, dxc, conv_w, dx, pcw, B, Tn, D, L.nC);
   } else {
     conv_bwd<T, 1><<<lgrid, kBwdThreads, 0, s>>>(x, dxc, conv_w, dx, pcw, B, Tn, D, L.nC);
@@ -1075,15 +1110,15 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
     if (L.mfma_dw) {
       if (Dh == 256)
         dw_mfma<256><<<dim3(DwTile<256>::kMt, H, L.S), kDwThreads, 0, s>>>(
-            x, dpre, dlo, conv_w, pw, Tn, D, H, rows, L.rows_per_split);
+            x, dpre, conv_w, pw, Tn, D, H, rows, L.rows_per_split);
       else
         dw_mfma<128><<<dim3(DwTile<128>::kMt, H, L.S), kDwThreads, 0, s>>>(
-            x, dpre, dlo, conv_w, pw, Tn, D, H, rows, L.rows_per_split);
+            x, dpre, conv_w, pw, Tn, D, H, rows, L.rows_per_split);
     }
   }
   if (!L.mfma_dw) {
     const dim3 grid(((2 * Dh + 63) / 64) * ((Dh + 63) / 64), H, L.S);
-    dw_valu<T><<<grid, 256, 0, s>>>(x, dpre, dlo, conv_w, pw, Tn, D, H, Dh, rows,
+    dw_valu<T><<<grid, 256, 0, s>>>(x, dpre, conv_w, pw, Tn, D, H, Dh, rows,
                                      L.rows_per_split);
   }
   // fixed-order sums of the partials

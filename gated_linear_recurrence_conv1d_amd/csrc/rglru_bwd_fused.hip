@@ -61,8 +61,8 @@ template <int DH> struct BwdTile {
   static_assert(kSeg == 2 && kRows * DH * 4 <= 2 * kRows * kLda * 2, "layout");
 };
 
-// dpre / dlo / dxc / part / dh0 as the separate per-element kernel writes them (layouts in
-// rglru_backward.hip); agg, incl: [nTT][B][D] words (each tile's map (A, U), and g at its start),
+// dpre / dxc / part / dh0 as the separate per-element kernel writes them (layouts in
+// rglru_backward.hip: dpre holds (dpa, dpx) as fp16 pairs); agg, incl: [nTT][B][D] words (each tile's map (A, U), and g at its start),
 // all kEmpty; ctrl: [1] give-up count, [2 + g] head g's ticket, all 0.
 template <int DH>
 __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     const float *__restrict__ h0, const float *__restrict__ dh_T, const bf16_t *__restrict__ conv_w,
     const bf16_t *__restrict__ W_a, const float *__restrict__ b_a, const bf16_t *__restrict__ W_x,
     const float *__restrict__ b_x, const float *__restrict__ Lambda, uint32_t *__restrict__ dpre,
-    uint32_t *__restrict__ dlo, float *__restrict__ dxc, float *__restrict__ part,
+    uint16_t *__restrict__ dxc, float *__restrict__ part,
     float *__restrict__ dh0, int B, int T, int D, int H, int nTT, unsigned *ctrl,
     unsigned long long *agg, unsigned long long *incl) {
   typedef BwdTile<DH> F;
@@ -337,8 +337,8 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     for (int k = 0; k < 3; ++k) xv[k] = *reinterpret_cast<const uint32_t *>(xsc + (rlast + 1 + k) * DH);
     xv[3] = 0u;
     const size_t seq = static_cast<size_t>(b) * T * D;
-    uint32_t *dpres = dpre + seq, *dlos = dlo + seq;
-    float *dxcs = dxc + seq;
+    uint32_t *dpres = dpre + seq;
+    uint16_t *dxcs = dxc + seq;
     const float hinit = h0 ? h0[static_cast<size_t>(b) * D + dc] : 0.0f;
 #pragma unroll 4
     for (int row = rlast; row > rlast - F::kSegRows; --row) {
@@ -369,10 +369,8 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
         s_rdz = fmaf(rr, dz, s_rdz);
         gk = a * delta;
         const int o = t * D + dc;
-        const uint32_t hpk = pack_bf16x2(dpa, dpx);
-        dpres[o] = hpk;
-        dlos[o] = pack_bf16x2(dpa - bf16lo(hpk), dpx - bf16hi(hpk));
-        dxcs[o] = dmg * ig;
+        dpres[o] = pack_f16x2(dpa, dpx);
+        dxcs[o] = static_cast<uint16_t>(pack_f16x2(dmg * ig, 0.0f));  // fp16
       }
     }
     psum[(0 * F::kSeg + sg) * DH + c] = s_pa;
@@ -411,7 +409,7 @@ size_t fused_backward_slots(int B, int T, int D) {
 hipError_t launch_fused_backward(const void *x, const void *y, const void *dy, const float *h0,
                                  const float *dh_T, const void *conv_w, const void *W_a,
                                  const float *b_a, const void *W_x, const float *b_x,
-                                 const float *Lambda, uint32_t *dpre, uint32_t *dlo, float *dxc,
+                                 const float *Lambda, uint32_t *dpre, uint16_t *dxc,
                                  float *part, float *dh0, int B, int T, int D, int H,
                                  unsigned *ctrl, unsigned long long *slots, hipStream_t s) {
   const int nTT = (T + kRows - 1) / kRows;
@@ -436,12 +434,12 @@ hipError_t launch_fused_backward(const void *x, const void *y, const void *dy, c
   switch (D / H) {
     case 128:
       tile_bwd<128><<<H * per, BwdTile<128>::kThreads, 0, s>>>(
-          xx, yy, dd, h0, dh_T, cw, wa, b_a, wx, b_x, Lambda, dpre, dlo, dxc, part, dh0, B, T, D,
+          xx, yy, dd, h0, dh_T, cw, wa, b_a, wx, b_x, Lambda, dpre, dxc, part, dh0, B, T, D,
           H, nTT, ctrl, agg, incl);
       break;
     case 256:
       tile_bwd<256><<<H * per, BwdTile<256>::kThreads, 0, s>>>(
-          xx, yy, dd, h0, dh_T, cw, wa, b_a, wx, b_x, Lambda, dpre, dlo, dxc, part, dh0, B, T, D,
+          xx, yy, dd, h0, dh_T, cw, wa, b_a, wx, b_x, Lambda, dpre, dxc, part, dh0, B, T, D,
           H, nTT, ctrl, agg, incl);
       break;
     default: return hipErrorInvalidValue;

@@ -198,14 +198,17 @@ __global__ __launch_bounds__(PreTile<DH>::kThreads, 2) void tile_preacts(
   }
 }
 
-// dxc[b][t][g*DH + i] += sum_k dp[b][t][g*DH .. as 2 DH bf16][k] wti[g][i][k] for the tiles of
-// head g, as above. dp rows (bf16 pairs, dpa low) are staged one row per load instruction into
-// rows padded by 16 bytes, so the A-operand reads of 32 rows fall on distinct banks; two tile
-// buffers, tile k+1 loading while tile k is in the MFMAs. Per tile: [barrier] stage tile k+1,
-// load the dxc values to update, MFMAs, one wait (vmcnt(0): staging and dxc loads), stores.
-// Vector memory completes in issue order, so the wait sits before this tile's stores -- a wait
-// after them (or a __syncthreads, which waits for every outstanding operation) would take their
-// whole round trip on every tile -- and the barrier orders LDS only.
+// dxc[b][t][g*DH + i] += sum_k dp[b][t][g*DH .. as 2 DH fp16][k] wti[g][i][k] for the tiles of
+// head g, as above (fp16 operands, dxc in fp16). dp rows (fp16 pairs, dpa low) are staged one row
+// per load instruction into rows padded by 16 bytes, so the A-operand reads of 32 rows fall on
+// distinct banks; two tile buffers, tile k+1 loading while tile k is in the MFMAs. Per tile:
+// [barrier] stage tile k+1, load this tile's dxc (16 bytes per lane, row-major), MFMAs,
+// [barrier] the products into the tile's own dp buffer (fp32, now free), [barrier] one wait
+// (vmcnt(0): staging and dxc loads), then dxc + product stored 16 bytes per lane. The detour
+// through the LDS turns the accumulator layout (one channel per lane, rows 4 apart) into
+// row-major pieces: stored straight from the accumulators, fp16 dxc went out as 2-byte stores
+// (half of a 128-byte line per wave) and took twice as long. Vector memory completes in issue
+// order, so the wait sits before this tile's stores and the barriers order LDS only.
 template <int DH> struct DxcTile {
   static_assert(DH == 128 || DH == 256, "resident dxc tile needs Dh in {128, 256}");
   static constexpr int kGPW = 1;          // 32-channel groups per wave
@@ -213,16 +216,16 @@ template <int DH> struct DxcTile {
   static constexpr int kThreads = 64 * kNW;
   static constexpr int K = 2 * DH;
   static constexpr int kKS = K / 16;
-  static constexpr int kLd = K + 8;            // bf16 row stride (row bytes + 16)
+  static constexpr int kLd = K + 8;            // fp16 row stride (row bytes + 16)
   static constexpr int kLanesPerRow = K / 8;   // 16-byte pieces per row (<= 64)
 };
 
 template <int DH>
 __global__ __launch_bounds__(DxcTile<DH>::kThreads, 2) void tile_dxc(
-    const uint32_t *__restrict__ dp, const bf16_t *__restrict__ wti, float *__restrict__ dxc,
+    const uint32_t *__restrict__ dp, const uint16_t *__restrict__ wti, uint16_t *__restrict__ dxc,
     int B, int T, int D, int H, int per) {
   typedef DxcTile<DH> F;
-  __shared__ __attribute__((aligned(16))) bf16_t la[2 * kRows * F::kLd];
+  __shared__ __attribute__((aligned(16))) uint16_t la[2 * kRows * F::kLd];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -232,12 +235,12 @@ __global__ __launch_bounds__(DxcTile<DH>::kThreads, 2) void tile_dxc(
   const int nTT = (T + kRows - 1) / kRows;
   const int ntiles = B * nTT;
   const int ci0 = w * 32 * F::kGPW + lrow;  // output channels ci0 + 32 gi within the head
-  bf16x8_t wr[F::kGPW][F::kKS];
+  f16x8_t wr[F::kGPW][F::kKS];
 #pragma unroll
   for (int gi = 0; gi < F::kGPW; ++gi) {
-    const bf16_t *row = wti + (static_cast<size_t>(g) * DH + ci0 + 32 * gi) * F::K + half * 8;
+    const uint16_t *row = wti + (static_cast<size_t>(g) * DH + ci0 + 32 * gi) * F::K + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < F::kKS; ++ks) wr[gi][ks] = load_bf16x8(row + ks * 16);
+    for (int ks = 0; ks < F::kKS; ++ks) wr[gi][ks] = load_f16x8(row + ks * 16);
   }
   // staging: tile row r by wave r % kNW, lanes 0 .. kLanesPerRow-1; rows past T read zeros
   const bool slane = lane < F::kLanesPerRow;
@@ -258,32 +261,26 @@ __global__ __launch_bounds__(DxcTile<DH>::kThreads, 2) void tile_dxc(
   __builtin_amdgcn_s_waitcnt(0x0F70);
   for (int it = 0; j < ntiles; j += per, ++it) {
     // this tile's rows are in buffer it & 1; the other buffer's readers (the previous tile's
-    // MFMAs) are past this barrier
+    // MFMAs and product reads) are past this barrier
     lds_barrier();
     // the next tile's rows, then the dxc values this lane updates (neither depends on the MFMAs;
     // both land while they run)
     const int jn = j + per;
     if (jn < ntiles) stage(jn, (it + 1) & 1);
     const int b = j % B, t0 = (j / B) * kRows;
-    unsigned Dv = static_cast<unsigned>(D);
-    asm volatile("" : "+s"(Dv));
-    char *tile = reinterpret_cast<char *>(dxc + (static_cast<size_t>(b) * T + t0) * D + g * DH);
-    const unsigned lane_off = (static_cast<unsigned>(ci0) + 4u * half * Dv) * 4u;
-    const bool full = t0 + kRows <= T;
-    auto at = [&](int gi, int r) {  // r: half 0's row
-      return reinterpret_cast<float *>(tile + static_cast<size_t>(r) * Dv * 4u + lane_off + 128u * gi);
-    };
-    float old[F::kGPW][2][16];
+    // this tile's dxc values, 16 bytes (8 channels) per lane and piece, rows past T as zeros
+    constexpr int kPieces = kRows * DH / 8;
+    constexpr int kPer = kPieces / F::kThreads;
+    static_assert(kPieces % F::kThreads == 0, "pieces per thread");
+    uint16_t *tile = dxc + (static_cast<size_t>(b) * T + t0) * D + g * DH;
+    u32x4_t dv[kPer];
 #pragma unroll
-    for (int gi = 0; gi < F::kGPW; ++gi)
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          const int r = rt * 32 + 8 * (jj >> 2) + (jj & 3);
-          old[gi][rt][jj] = (full || t0 + r + 4 * half < T) ? *at(gi, r) : 0.0f;
-        }
-    const bf16_t *lt = la + (it & 1) * kRows * F::kLd;
+    for (int q = 0; q < kPer; ++q) {
+      const int idx = tid + q * F::kThreads, r = idx / (DH / 8), c8 = idx % (DH / 8);
+      dv[q] = t0 + r < T ? *reinterpret_cast<const u32x4_t *>(tile + static_cast<size_t>(r) * D + 8 * c8)
+                         : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    const uint16_t *lt = la + (it & 1) * kRows * F::kLd;
     f32x16_t acc[F::kGPW][2];
 #pragma unroll
     for (int gi = 0; gi < F::kGPW; ++gi) acc[gi][0] = acc[gi][1] = f32x16_t{};
@@ -291,21 +288,40 @@ __global__ __launch_bounds__(DxcTile<DH>::kThreads, 2) void tile_dxc(
     for (int ks = 0; ks < F::kKS; ++ks)
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        const bf16x8_t af = load_bf16x8(lt + (rt * 32 + lrow) * F::kLd + ks * 16 + half * 8);
+        const f16x8_t af = load_f16x8(lt + (rt * 32 + lrow) * F::kLd + ks * 16 + half * 8);
 #pragma unroll
         for (int gi = 0; gi < F::kGPW; ++gi)
-          acc[gi][rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wr[gi][ks], acc[gi][rt], 0, 0, 0);
+          acc[gi][rt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, wr[gi][ks], acc[gi][rt], 0, 0, 0);
       }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile's staging and the dxc values
+    // the products, row-major in fp32, over this tile's dp rows (kRows x (DH + 4) floats: the
+    // same bytes as kRows x kLd fp16)
+    constexpr int kLdo = DH + 4;
+    static_assert(kRows * kLdo * 4 == kRows * F::K * 2 + kRows * 16, "product tile fits");
+    float *po = reinterpret_cast<float *>(la + (it & 1) * kRows * F::kLd);
+    lds_barrier();  // every wave is done with this tile's dp rows
 #pragma unroll
     for (int gi = 0; gi < F::kGPW; ++gi)
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          const int r = rt * 32 + 8 * (jj >> 2) + (jj & 3);
-          if (full || t0 + r + 4 * half < T) *at(gi, r) = old[gi][rt][jj] + acc[gi][rt][jj];
-        }
+        for (int jj = 0; jj < 16; ++jj)
+          po[(rt * 32 + 8 * (jj >> 2) + 4 * half + (jj & 3)) * kLdo + ci0 + 32 * gi] = acc[gi][rt][jj];
+    lds_barrier();  // products complete
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile's staging and the dxc values
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int idx = tid + q * F::kThreads, r = idx / (DH / 8), c8 = idx % (DH / 8);
+      if (t0 + r < T) {
+        const float4 p0 = *reinterpret_cast<const float4 *>(po + r * kLdo + 8 * c8);
+        const float4 p1 = *reinterpret_cast<const float4 *>(po + r * kLdo + 8 * c8 + 4);
+        u32x4_t o;
+        o[0] = pack_f16x2(f16lo(dv[q][0]) + p0.x, f16hi(dv[q][0]) + p0.y);
+        o[1] = pack_f16x2(f16lo(dv[q][1]) + p0.z, f16hi(dv[q][1]) + p0.w);
+        o[2] = pack_f16x2(f16lo(dv[q][2]) + p1.x, f16hi(dv[q][2]) + p1.y);
+        o[3] = pack_f16x2(f16lo(dv[q][3]) + p1.z, f16hi(dv[q][3]) + p1.w);
+        *reinterpret_cast<u32x4_t *>(tile + static_cast<size_t>(r) * D + 8 * c8) = o;
+      }
+    }
   }
 }
 
@@ -353,11 +369,11 @@ hipError_t launch_resident_preacts(const void *x, const void *conv_w, const void
   return hipGetLastError();
 }
 
-hipError_t launch_resident_dxc(const void *dp, const void *wti, float *dxc, int B, int T, int D,
+hipError_t launch_resident_dxc(const void *dp, const void *wti, uint16_t *dxc, int B, int T, int D,
                                int H, hipStream_t s) {
   const int per = std::max(1, cu_count() / H);
   const uint32_t *p = static_cast<const uint32_t *>(dp);
-  const bf16_t *wt = static_cast<const bf16_t *>(wti);
+  const uint16_t *wt = static_cast<const uint16_t *>(wti);
   switch (D / H) {
     case 128: tile_dxc<128><<<H * per, DxcTile<128>::kThreads, 0, s>>>(p, wt, dxc, B, T, D, H, per); break;
     case 256: tile_dxc<256><<<H * per, DxcTile<256>::kThreads, 0, s>>>(p, wt, dxc, B, T, D, H, per); break;

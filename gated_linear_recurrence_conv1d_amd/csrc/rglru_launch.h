@@ -71,19 +71,19 @@ hipError_t launch_resident_preacts(const void *x, const void *conv_w, const void
                                    const float *b_a, const void *W_x, const float *b_x,
                                    void *pre, int B, int T, int D, int H, hipStream_t s,
                                    bool split);
-hipError_t launch_resident_dxc(const void *dp, const void *wti, float *dxc, int B, int T, int D,
+hipError_t launch_resident_dxc(const void *dp, const void *wti, uint16_t *dxc, int B, int T, int D,
                                int H, hipStream_t s);
 
 // The backward's per-element part in one pass over kFusedBwdRows-step tiles, latest first (bf16, Dh in
 // {128, 256}, T * D * 4 < 2^31): pre-activations recomputed on MFMA, the adjoint carried from
-// tile to tile, and dpre / dlo / dxc / the per-tile partial sums / dh0 as the separate kernels
-// produce them. ctrl: 2 + H words, slots: fused_backward_slots(B, T, D) words (both reset here).
+// tile to tile, and dpre (fp16 pairs) / dxc / the per-tile partial sums / dh0 as the separate
+// kernels produce them. ctrl: 2 + H words, slots: fused_backward_slots(B, T, D) words (both reset here).
 bool fused_backward_supported(int Dh);
 size_t fused_backward_slots(int B, int T, int D);
 hipError_t launch_fused_backward(const void *x, const void *y, const void *dy, const float *h0,
                                  const float *dh_T, const void *conv_w, const void *W_a,
                                  const float *b_a, const void *W_x, const float *b_x,
-                                 const float *Lambda, uint32_t *dpre, uint32_t *dlo, float *dxc,
+                                 const float *Lambda, uint32_t *dpre, uint16_t *dxc,
                                  float *part, float *dh0, int B, int T, int D, int H,
                                  unsigned *ctrl, unsigned long long *slots, hipStream_t s);
 
@@ -105,7 +105,7 @@ struct BwdLayout {
   int rows_per_split;         // rows of the flattened (b, t) index per split
   bool mfma_dxc, mfma_dw;     // which contractions run on MFMA
   bool fused;                 // the per-element part as one tile pass (no pre, sums, carry)
-  size_t o_pre, o_dpre, o_dlo, o_dxc, o_sums, o_carry, o_part, o_pcw, o_pw, o_wti, o_ctrl, o_lb,
+  size_t o_pre, o_dpre, o_dxc, o_sums, o_carry, o_part, o_pcw, o_pw, o_wti, o_ctrl, o_lb,
       total;
 };
 BwdLayout backward_layout(int B, int T, int D, int H, int io);

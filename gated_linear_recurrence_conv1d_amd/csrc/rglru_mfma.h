@@ -55,6 +55,14 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t *p) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// fp16 operands (v_mfma_f32_32x32x16_f16: the same lane layout as the bf16 instruction), held as
+// raw 16-bit words in memory.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f16x8_t load_f16x8(const uint16_t *p) {
+  u32x4_t v = *reinterpret_cast<const u32x4_t *>(p);
+  return __builtin_bit_cast(f16x8_t, v);
+}
+
 // acc[gi][ri][gate] = A(rows of row tile r0+ri) * W_gate(rows of group g0+gi)^T over k = 0..DH.
 // lds_a: [64][kLda] bf16 conv output of the tile. Wa_g / Wx_g: this head's [DH][DH] weights.
 // SPLIT: lds_lo holds the bf16 residual of the conv output (xc - hi) and A = hi + lo, which makes

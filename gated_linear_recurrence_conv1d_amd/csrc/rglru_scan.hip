@@ -29,27 +29,32 @@ template <typename T> struct StepData {
   typename PrePair<T>::type p[kGroup];
 };
 
+// The loads of steps [t, min(t + kGroup, tend)); xp / pp point at step t of the channel.
 template <typename T>
-__device__ __forceinline__ void load_group(StepData<T> &s, const T *xp, const typename PrePair<T>::type *pp,
-                                           int t, int tend, int D) {
+__device__ __forceinline__ void load_group(StepData<T> &s, const T *xp,
+                                           const typename PrePair<T>::type *pp, int n, int D) {
 #pragma unroll
   for (int u = 0; u < kGroup; ++u) {
-    if (t + u < tend) {
-      s.x[u] = Elem<T>::load(xp, static_cast<size_t>(t + u) * D);
-      s.p[u] = pp[static_cast<size_t>(t + u) * D];
+    if (u < n) {
+      s.x[u] = Elem<T>::load(xp, 0);
+      s.p[u] = *pp;
     }
+    xp += D;
+    pp += D;
   }
 }
 
-// Runs steps [t, min(t + kGroup, tend)) of one channel. WRITE: store y; otherwise only advance
-// the state and the sum of log a.
-template <typename T, bool WRITE>
+// Runs steps [t, t + n) (n <= kGroup) of one channel; yp points at step t. WRITE: store y;
+// otherwise only advance the state and the sum of log a. NH: some channel of the wave has
+// kd < -1/4, so log a can leave the polynomial's range [-1/4, 0] (a wave-uniform choice: the
+// usual decays never pay for the exp2 of the other branch).
+template <typename T, bool WRITE, bool NH>
 __device__ __forceinline__ void run_group(const StepData<T> &s, const float (&w)[4], float kd,
-                                          float (&xm)[3], float &h, float &slog, T *yp, int t,
-                                          int tend, int D) {
+                                          float (&xm)[3], float &h, float &slog, T *yp, int n,
+                                          int D) {
 #pragma unroll
   for (int u = 0; u < kGroup; ++u) {
-    if (t + u < tend) {
+    if (u < n) {
       const float xv = s.x[u];
       const float xc = fmaf(w[3], xv, fmaf(w[2], xm[2], fmaf(w[1], xm[1], w[0] * xm[0])));
       xm[0] = xm[1];
@@ -57,29 +62,31 @@ __device__ __forceinline__ void run_group(const StepData<T> &s, const float (&w)
       xm[2] = xv;
       const float pa = PrePair<T>::pa(s.p[u]);
       const float px = PrePair<T>::px(s.p[u]);
-      float r = fast_sigmoid(pa);
-      float ig = fast_sigmoid(px);
-      float z = kd * r;
-      float e = expm1_nonpos(z);
-      float a = 1.0f + e;
-      float m = __builtin_amdgcn_sqrtf(-e * (2.0f + e));
+      const float r = fast_sigmoid(pa);
+      const float ig = fast_sigmoid(px);
+      const float z = kd * r;
+      const float e = NH ? expm1_nonpos(z) : expm1_poly(z);
+      const float a = 1.0f + e;
+      const float m = __builtin_amdgcn_sqrtf(-e * (2.0f + e));
       h = fmaf(a, h, m * (ig * xc));
       if (WRITE) {
-        Elem<T>::store(yp, static_cast<size_t>(t + u) * D, h);
+        Elem<T>::store(yp, 0, h);
       } else {
         slog += z;
       }
     }
+    if (WRITE) yp += D;
   }
 }
 
 // Scans steps [tbeg, tend) of channel (b, d) starting from state h. Returns the final state;
-// when !WRITE also the sum of log a over the range.
-template <typename T, bool WRITE>
-__device__ __forceinline__ float scan_range(const T *__restrict__ xb,
-                                            const typename PrePair<T>::type *__restrict__ pb,
-                                            T *__restrict__ yb, const float (&w)[4], float kd,
-                                            int tbeg, int tend, int D, float h, float &slog) {
+// when !WRITE also the sum of log a over the range. Pointers advance by D per step (no 64-bit
+// index arithmetic per access).
+template <typename T, bool WRITE, bool NH>
+__device__ __forceinline__ float scan_range_nh(const T *__restrict__ xb,
+                                               const typename PrePair<T>::type *__restrict__ pb,
+                                               T *__restrict__ yb, const float (&w)[4], float kd,
+                                               int tbeg, int tend, int D, float h, float &slog) {
   float xm[3];
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
@@ -87,17 +94,35 @@ __device__ __forceinline__ float scan_range(const T *__restrict__ xb,
     xm[k] = (s >= 0) ? Elem<T>::load(xb, static_cast<size_t>(s) * D) : 0.0f;
   }
   slog = 0.0f;
+  const size_t o = static_cast<size_t>(tbeg) * D;
+  const T *xp = xb + o;
+  const typename PrePair<T>::type *pp = pb + o;
+  T *yp = WRITE ? yb + o : nullptr;
+  const size_t stride = static_cast<size_t>(kGroup) * D;
   StepData<T> cur, nxt;
   int t = tbeg;
-  if (t < tend) load_group<T>(cur, xb, pb, t, tend, D);
+  if (t < tend) load_group<T>(cur, xp, pp, tend - t, D);
   while (t < tend) {
     const int tn = t + kGroup;
-    if (tn < tend) load_group<T>(nxt, xb, pb, tn, tend, D);
-    run_group<T, WRITE>(cur, w, kd, xm, h, slog, yb, t, tend, D);
+    xp += stride;
+    pp += stride;
+    if (tn < tend) load_group<T>(nxt, xp, pp, tend - tn, D);
+    run_group<T, WRITE, NH>(cur, w, kd, xm, h, slog, yp, tend - t, D);
+    if (WRITE) yp += stride;
     cur = nxt;
     t = tn;
   }
   return h;
+}
+
+template <typename T, bool WRITE>
+__device__ __forceinline__ float scan_range(const T *__restrict__ xb,
+                                            const typename PrePair<T>::type *__restrict__ pb,
+                                            T *__restrict__ yb, const float (&w)[4], float kd,
+                                            int tbeg, int tend, int D, float h, float &slog) {
+  if (__builtin_amdgcn_readfirstlane(__any(kd < -0.25f) ? 1 : 0))
+    return scan_range_nh<T, WRITE, true>(xb, pb, yb, w, kd, tbeg, tend, D, h, slog);
+  return scan_range_nh<T, WRITE, false>(xb, pb, yb, w, kd, tbeg, tend, D, h, slog);
 }
 
 template <typename T>

@@ -3,11 +3,11 @@ gradients, element by element, on the same seeded inputs and output gradients.
 
 Bound, per gradient tensor (dx, dconv_w, dW_a, dW_x, db_a, db_x, dLambda, dh0): the error of the
 forward's tests, err = max_i |g_i - ref_i| / max(|ref_i|, rms(ref)), below 1e-4 for fp32 I/O and
-2e-2 for bf16 I/O. The bf16 path reads h[t-1] from the bf16 y and stores the pre-activations in
-fp16 and (dpa, dpx) as bf16 pairs for the dx contraction; the contractions whose errors the
-gradients amplify (the recomputed gate pre-activations and dW) take their activation operands as
-bf16 hi + lo. Single elements then err by a few 1e-3 of the rms (with bf16 operands there, dW
-missed by up to 2.5e-2 on these cases); a mistake in a gradient formula moves the error to O(1).
+2e-2 for bf16 I/O. The bf16 path reads h[t-1] from the bf16 y, stores the pre-activations and
+(dpa, dpx) as fp16 pairs, and runs the dx and dW contractions on fp16 operands; the recomputed gate
+pre-activations, whose errors the gradients amplify, take the conv output as bf16 hi + lo. Single
+elements then err by a few 1e-3 of the rms (with bf16 operands in the dW contraction, dW missed by
+up to 2.5e-2 on these cases); a mistake in a gradient formula moves the error to O(1).
 Exact cases: run-to-run bitwise reproducibility (fixed-order sums, no atomics), and the
 workspace's prior contents having no effect.
 """
