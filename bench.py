@@ -106,6 +106,14 @@ PROFILE_CMDS = {
     "leg_trace": "rocprofv3 --kernel-trace --stats -d OUT/trace_W -o bench --output-format csv -- "
                  "python3 REPO/bench.py --workload W --steps 20 --warmup 10 --no-cpu-baseline "
                  "--no-backward --no-decode --no-mqa --no-plan-legs",
+    "bwd_pmc1": "rocprofv3 --pmc " + " ".join(PMC_PASSES[0]) + " --kernel-include-regex "
+                "'tile_|bwd_|wt_prep|dxc_|conv_bwd|dw_|colsum' -d OUT/bpmc1 -o run --output-format "
+                "csv -- python3 REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-decode "
+                "--no-mqa --no-plan-legs --bwd-warmup 2 --bwd-reps 3",
+    "bwd_pmc2": "rocprofv3 --pmc " + " ".join(PMC_PASSES[1]) + " --kernel-include-regex "
+                "'tile_|bwd_|wt_prep|dxc_|conv_bwd|dw_|colsum' -d OUT/bpmc2 -o run --output-format "
+                "csv -- python3 REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-decode "
+                "--no-mqa --no-plan-legs --bwd-warmup 2 --bwd-reps 3",
     "pmc1": "rocprofv3 --pmc " + " ".join(PMC_PASSES[0]) + " -d OUT/pmc1 -o run "
             "--output-format csv -- python3 REPO/bench.py --steps 5 --warmup 2 --no-cpu-baseline "
             "--no-backward --no-decode --no-mqa --no-plan-legs",
@@ -200,10 +208,11 @@ def backward_traffic_summary(fetch_csv, write_csv, workload, copy_mib=256):
     print(open(path).read(), end="")
 
 
-def counter_summary(p1_csv, p2_csv, workload):
+def counter_summary(p1_csv, p2_csv, workload, backward=False):
     """Per-launch instruction and busy counts of every kernel of the bench's forward (fused plan
-    and the split plan's stages) from the two counter passes of PMC_PASSES, with the derived
-    rates. The first dispatch of each kernel (cold caches, code load) is left out."""
+    and the split plan's stages) -- or, with backward, of one rglru_backward call -- from the two
+    counter passes of PMC_PASSES, with the derived rates. The first dispatch of each kernel (cold
+    caches, code load) is left out."""
     import collections
     from workloads import WORKLOADS
     w = [v for v in WORKLOADS.values() if v.name == workload][0]
@@ -215,6 +224,8 @@ def counter_summary(p1_csv, p2_csv, workload):
         for r in _counter_rows(path):
             if "rglru::" not in r["Kernel_Name"]:
                 continue  # torch's input set-up, the runtime's copies
+            if backward != is_backward_kernel(r["Kernel_Name"]):
+                continue
             k = r["Kernel_Name"].replace("void ", "").split("(")[0].replace("rglru::", "")
             disp[(k, r["Dispatch_Id"])][r["Counter_Name"]] = float(r["Counter_Value"])
             disp[(k, r["Dispatch_Id"])]["_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
@@ -230,13 +241,17 @@ def counter_summary(p1_csv, p2_csv, workload):
                 else:
                     vals[k][f"p{p}:{c}"].append(v)
     mean = lambda xs: sum(xs) / len(xs) if xs else float("nan")
-    path = os.path.join(ROOT, "profiles", f"counters_{workload}.txt")
+    tag = "backward_" if backward else ""
+    cmds = ("bwd_pmc1", "bwd_pmc2") if backward else ("pmc1", "pmc2")
+    path = os.path.join(ROOT, "profiles", f"counters_{tag}{workload}.txt")
     with open(path, "w") as f:
-        f.write("# Instruction and busy counters per launch of the forward's kernels (rocprofv3).\n")
+        f.write("# Instruction and busy counters per launch of the "
+                f"{'backward' if backward else 'forward'}'s kernels (rocprofv3).\n")
         f.write("# Made by (REPO = this repository, OUT = a scratch directory; run from /tmp):\n")
-        f.write(f"#   {PROFILE_CMDS['pmc1']}\n#   {PROFILE_CMDS['pmc2']}\n")
-        f.write("#   python3 REPO/bench.py --counter-summary OUT/pmc1/run_counter_collection.csv "
-                "OUT/pmc2/run_counter_collection.csv\n")
+        f.write(f"#   {PROFILE_CMDS[cmds[0]]}\n#   {PROFILE_CMDS[cmds[1]]}\n")
+        f.write(f"#   python3 REPO/bench.py --{'backward-' if backward else ''}counter-summary "
+                f"OUT/{'b' if backward else ''}pmc1/run_counter_collection.csv "
+                f"OUT/{'b' if backward else ''}pmc2/run_counter_collection.csv\n")
         f.write("# Means over the dispatches of each kernel after its first. Derived rates:\n"
                 "#   cycles = GRBM_GUI_ACTIVE / 8 (one count per XCD); simd_cycles = 1024 * cycles\n"
                 "#   mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / simd_cycles\n"
@@ -248,7 +263,7 @@ def counter_summary(p1_csv, p2_csv, workload):
                 "#   lds_bank_conflict = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS\n"
                 "#   per_element: over B*T*D of the workload\n")
         f.write(f"workload: {workload}\n")
-        f.write(f"source_hash: {kernel_source_hash()}\n")
+        f.write(f"source_hash: {kernel_source_hash(BACKWARD_SOURCES if backward else None)}\n")
         for k in sorted(vals, key=lambda k: -mean(dur[k])):
             v = {c: mean(xs) for c, xs in vals[k].items()}
             valu, mfma = v.get("p1:SQ_INSTS_VALU", 0.0), v.get("p1:SQ_INSTS_MFMA", 0.0)
@@ -595,16 +610,20 @@ def main():
     ap.add_argument("--counter-summary", nargs=2, metavar=("PMC1_CSV", "PMC2_CSV"),
                     help="write profiles/counters_<workload>.txt from the two counter passes and "
                          "exit (no GPU needed)")
+    ap.add_argument("--backward-counter-summary", nargs=2, metavar=("PMC1_CSV", "PMC2_CSV"),
+                    help="write profiles/counters_backward_<workload>.txt likewise")
     ap.add_argument("--trace-summary", nargs="+", metavar="CSV",
                     help="write profiles/kernel_trace_fused_<workload>.txt from a rocprofv3 "
                          "kernel_stats.csv (and optionally the bench stdout) and exit")
     args = ap.parse_args()
     if (args.traffic_summary or args.trace_summary or args.backward_traffic_summary
-            or args.counter_summary):
+            or args.counter_summary or args.backward_counter_summary):
         from workloads import WORKLOADS
         wname = WORKLOADS[args.workload].name
         if args.counter_summary:
             counter_summary(*args.counter_summary, wname)
+        if args.backward_counter_summary:
+            counter_summary(*args.backward_counter_summary, wname, backward=True)
         if args.traffic_summary:
             traffic_summary(*args.traffic_summary, wname)
         if args.backward_traffic_summary:
