@@ -1037,6 +1037,7 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
   const bool pair = D % 2 == 0;
   const dim3 lgrid(pair ? (lblocks + 1) / 2 : lblocks, L.nC);
   hipError_t e = hipSuccess;
+  bool fused_conv = false;  // the dxc pass also ran the conv's transpose
   if (!L.fused) {
     // no waits on this path: the failure count is zero
     e = launch_clear_words(reinterpret_cast<unsigned *>(ws + L.o_ctrl), 2, s);
@@ -1079,8 +1080,10 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
       wt_prep<<<static_cast<unsigned>((nw + 255) / 256), 256, 0, s>>>(W_a, W_x, wti, H, Dh);
       const dim3 grid((Tn + kTileRows - 1) / kTileRows, H, B);
       if (resident && resident_dxc_supported(Dh)) {
-        e = launch_resident_dxc(dpre, wti, dxc, B, Tn, D, H, s);
+        // the conv's transpose included: dx and the dconv_w partials come out of this pass
+        e = launch_resident_dxc(dpre, wti, dxc, x, conv_w, dx, pcw, B, Tn, D, H, s);
         if (e != hipSuccess) return e;
+        fused_conv = true;
       } else switch (Dh) {
         case 32: dxc_mfma<32><<<grid, kThreads, 0, s>>>(dpre, wti, dxc, Tn, D); break;
         case 64: dxc_mfma<64><<<grid, kThreads, 0, s>>>(dpre, wti, dxc, Tn, D); break;
@@ -1096,7 +1099,9 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
   }
   // the conv backward reads and writes 16-bit values: four channels per lane (8-byte accesses)
   // where D allows it
-  if (sizeof(T) == 2 && D % 4 == 0) {
+  if (fused_conv) {
+    // done by the dxc pass
+  } else if (sizeof(T) == 2 && D % 4 == 0) {
     const dim3 qgrid((lblocks + 3) / 4, L.nC);
     if constexpr (sizeof(T) == 2)
       conv_bwd<T, 4><<<qgrid, kBwdThreads, 0, s>>>(x, dxc, conv_w, dx, pcw, B, Tn, D, L.nC);

@@ -29,6 +29,7 @@
 // the tiles after it have finished their first pass; it is bounded all the same (a lost word
 // gives NaN and bumps a counter, never a hang).
 #include <algorithm>
+#include <type_traits>
 
 #include "rglru_launch.h"
 #include "rglru_mfma.h"
@@ -132,6 +133,10 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     w23c = as_bf16x2(__builtin_amdgcn_perm(cw[3], cw[2], csel));
   }
   const float kd = decay_coeff(Lambda[dc]);
+  // expm1(log a) takes the polynomial alone unless some channel of the wave has a decay below
+  // e^-1/4 (log a can then leave the polynomial's range): a wave-uniform choice of loop variant,
+  // so the usual decays never evaluate the exp2 of the other branch
+  const bool fast = __builtin_amdgcn_readfirstlane(__any(kd < -0.25f) ? 1 : 0) != 0;
 
   // conv of staged rows q .. q+3 (time t - 3 .. t for tile row q), as pair words: both channels
   // of the pair, or channel c alone
@@ -166,22 +171,25 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     const int b = j % B, t0 = (nTT - 1 - j / B) * kRows;
     const size_t so = static_cast<size_t>(b) * T * D;
     const __amdgpu_buffer_rsrc_t sx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t *>(x + so), static_cast<short>(0), T * D * 2, kRawWord3);
+        const_cast<bf16_t *>(x + so), static_cast<short>(0), rec_bytes(T, D, 2u),
+        kRawWord3);
     const __amdgpu_buffer_rsrc_t sdy = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t *>(dy + so), static_cast<short>(0), T * D * 2, kRawWord3);
+        const_cast<bf16_t *>(dy + so), static_cast<short>(0), rec_bytes(T, D, 2u),
+        kRawWord3);
     const __amdgpu_buffer_rsrc_t sy = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t *>(y + so), static_cast<short>(0), T * D * 2, kRawWord3);
+        const_cast<bf16_t *>(y + so), static_cast<short>(0), rec_bytes(T, D, 2u),
+        kRawWord3);
     for (int i = w; i < F::kLoads; i += F::kNW) {  // wave-uniform
       if (i < F::kXLoads) {
-        const unsigned row_off = static_cast<unsigned>((t0 - 3 + i * F::kRowsPerLoad) * 2 * D);
+        const unsigned row_off = row_bytes(t0 - 3 + i * F::kRowsPerLoad, D, 2u);
         dma_16b(sx, row_off + lane_off, lds_addr(xr[bf] + i * F::kRowsPerLoad * DH));
       } else if (i < F::kXLoads + F::kRLoads) {
         const int q = i - F::kXLoads;
-        const unsigned row_off = static_cast<unsigned>((t0 + q * F::kRowsPerLoad) * 2 * D);
+        const unsigned row_off = row_bytes(t0 + q * F::kRowsPerLoad, D, 2u);
         dma_16b(sdy, row_off + lane_off, lds_addr(dyr[bf] + q * F::kRowsPerLoad * DH));
       } else {
         const int q = i - F::kXLoads - F::kRLoads;
-        const unsigned row_off = static_cast<unsigned>((t0 - 1 + q * F::kRowsPerLoad) * 2 * D);
+        const unsigned row_off = row_bytes(t0 - 1 + q * F::kRowsPerLoad, D, 2u);
         dma_16b(sy, row_off + lane_off, lds_addr(yr[bf] + q * F::kRowsPerLoad * DH));
       }
     }
@@ -255,14 +263,21 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     const bf16_t *yt = yr[cur] + c;    // row r: y at t0 + r - 1 (zero for t0 + r - 1 < 0)
     const int rlast = sg * F::kSegRows + F::kSegRows - 1;  // the segment's last tile row
     float A = 1.0f, U = 0.0f;
+    auto pass1 = [&](auto nh) {
 #pragma unroll 4
-    for (int row = rlast; row > rlast - F::kSegRows; --row) {
-      const float pa = f16lo(preL[row * DH + c]);
-      const bool in = t0 + row < T;
-      const float a = in ? 1.0f + expm1_nonpos(kd * fast_sigmoid(pa)) : 1.0f;
-      U = a * ((in ? bf16_to_f32(dyt[row * DH]) : 0.0f) + U);
-      A *= a;
-    }
+      for (int row = rlast; row > rlast - F::kSegRows; --row) {
+        const float pa = f16lo(preL[row * DH + c]);
+        const bool in = t0 + row < T;
+        const float z = kd * fast_sigmoid(pa);
+        const float a = in ? 1.0f + (decltype(nh)::value ? expm1_nonpos(z) : expm1_poly(z)) : 1.0f;
+        U = a * ((in ? bf16_to_f32(dyt[row * DH]) : 0.0f) + U);
+        A *= a;
+      }
+    };
+    if (fast)
+      pass1(std::true_type{});
+    else
+      pass1(std::false_type{});
     sc[sg * DH + c] = make_float2(A, U);
     lds_barrier();  // segment maps ready
     // ---- the tile's map, g at its end from the next tile in time, g at its start published
@@ -336,43 +351,52 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
 #pragma unroll
     for (int k = 0; k < 3; ++k) xv[k] = *reinterpret_cast<const uint32_t *>(xsc + (rlast + 1 + k) * DH);
     xv[3] = 0u;
-    const size_t seq = static_cast<size_t>(b) * T * D;
-    uint32_t *dpres = dpre + seq;
-    uint16_t *dxcs = dxc + seq;
+    // the element (t0 + rlast, dc) of dpre / dxc; one row (D elements) back per step
+    const size_t o0 = (static_cast<size_t>(b) * T + t0 + rlast) * D + dc;
     const float hinit = h0 ? h0[static_cast<size_t>(b) * D + dc] : 0.0f;
+    auto pass2 = [&](auto nh) {
+      uint32_t *dpo = dpre + o0;
+      uint16_t *dxo = dxc + o0;
 #pragma unroll 4
-    for (int row = rlast; row > rlast - F::kSegRows; --row) {
-      const int t = t0 + row;
-      xv[3] = xv[2];
-      xv[2] = xv[1];
-      xv[1] = xv[0];
-      xv[0] = *reinterpret_cast<const uint32_t *>(xsc + row * DH);
-      if (t < T) {
-        const uint32_t pp = preL[row * DH + c];
-        const float xc = conv1(xv);
-        const float rr = fast_sigmoid(f16lo(pp));
-        const float ig = fast_sigmoid(f16hi(pp));
-        const float e = expm1_nonpos(kd * rr);
-        const float a = 1.0f + e;
-        const float m = __builtin_amdgcn_sqrtf(-e * (2.0f + e));
-        const float delta = bf16_to_f32(dyt[row * DH]) + gk;
-        const float hp = t > 0 ? bf16_to_f32(yt[row * DH]) : hinit;
-        const float dx_ = delta * xc, dmg = delta * m;
-        const float dm = dx_ * ig;
-        const float di = dmg * xc;
-        float dz = delta * hp * a;
-        if (m > 0.0f) dz -= dm * (a * a) * __builtin_amdgcn_rcpf(m);
-        const float dpa = kd * dz * (rr * (1.0f - rr));
-        const float dpx = di * (ig * (1.0f - ig));
-        s_pa += dpa;
-        s_px += dpx;
-        s_rdz = fmaf(rr, dz, s_rdz);
-        gk = a * delta;
-        const int o = t * D + dc;
-        dpres[o] = pack_f16x2(dpa, dpx);
-        dxcs[o] = static_cast<uint16_t>(pack_f16x2(dmg * ig, 0.0f));  // fp16
+      for (int row = rlast; row > rlast - F::kSegRows; --row) {
+        const int t = t0 + row;
+        xv[3] = xv[2];
+        xv[2] = xv[1];
+        xv[1] = xv[0];
+        xv[0] = *reinterpret_cast<const uint32_t *>(xsc + row * DH);
+        if (t < T) {
+          const uint32_t pp = preL[row * DH + c];
+          const float xc = conv1(xv);
+          const float rr = fast_sigmoid(f16lo(pp));
+          const float ig = fast_sigmoid(f16hi(pp));
+          const float z = kd * rr;
+          const float e = decltype(nh)::value ? expm1_nonpos(z) : expm1_poly(z);
+          const float a = 1.0f + e;
+          const float m = __builtin_amdgcn_sqrtf(-e * (2.0f + e));
+          const float delta = bf16_to_f32(dyt[row * DH]) + gk;
+          const float hp = t > 0 ? bf16_to_f32(yt[row * DH]) : hinit;
+          const float dx_ = delta * xc, dmg = delta * m;
+          const float dm = dx_ * ig;
+          const float di = dmg * xc;
+          float dz = delta * hp * a;
+          if (m > 0.0f) dz -= dm * (a * a) * __builtin_amdgcn_rcpf(m);
+          const float dpa = kd * dz * (rr * (1.0f - rr));
+          const float dpx = di * (ig * (1.0f - ig));
+          s_pa += dpa;
+          s_px += dpx;
+          s_rdz = fmaf(rr, dz, s_rdz);
+          gk = a * delta;
+          *dpo = pack_f16x2(dpa, dpx);
+          *dxo = static_cast<uint16_t>(pack_f16x2(dmg * ig, 0.0f));  // fp16
+        }
+        dpo -= D;
+        dxo -= D;
       }
-    }
+    };
+    if (fast)
+      pass2(std::true_type{});
+    else
+      pass2(std::false_type{});
     psum[(0 * F::kSeg + sg) * DH + c] = s_pa;
     psum[(1 * F::kSeg + sg) * DH + c] = s_px;
     psum[(2 * F::kSeg + sg) * DH + c] = s_rdz;

@@ -109,10 +109,10 @@ __global__ __launch_bounds__(PreTile<DH>::kThreads, 2) void tile_preacts(
   auto stage = [&](int j) {
     const int b = j % B, t0 = (j / B) * kRows;
     const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t *>(x + static_cast<size_t>(b) * T * D), static_cast<short>(0), T * D * 2,
-        kWord3);
+        const_cast<bf16_t *>(x + static_cast<size_t>(b) * T * D), static_cast<short>(0),
+        rec_bytes(T, D, 2u), kWord3);
     for (int i = w; i < F::kLoads; i += F::kNW) {
-      const unsigned row_off = static_cast<unsigned>((t0 - 3 + i * F::kRowsPerLoad) * 2 * D);
+      const unsigned row_off = row_bytes(t0 - 3 + i * F::kRowsPerLoad, D, 2u);
       dma_16b(seq, row_off + lane_off, lds_addr(xr + i * F::kRowsPerLoad * DH));
     }
   };
@@ -198,17 +198,21 @@ __global__ __launch_bounds__(PreTile<DH>::kThreads, 2) void tile_preacts(
   }
 }
 
-// dxc[b][t][g*DH + i] += sum_k dp[b][t][g*DH .. as 2 DH fp16][k] wti[g][i][k] for the tiles of
-// head g, as above (fp16 operands, dxc in fp16). dp rows (fp16 pairs, dpa low) are staged one row
-// per load instruction into rows padded by 16 bytes, so the A-operand reads of 32 rows fall on
-// distinct banks; two tile buffers, tile k+1 loading while tile k is in the MFMAs. Per tile:
-// [barrier] stage tile k+1, load this tile's dxc (16 bytes per lane, row-major), MFMAs,
-// [barrier] the products into the tile's own dp buffer (fp32, now free), [barrier] one wait
-// (vmcnt(0): staging and dxc loads), then dxc + product stored 16 bytes per lane. The detour
-// through the LDS turns the accumulator layout (one channel per lane, rows 4 apart) into
-// row-major pieces: stored straight from the accumulators, fp16 dxc went out as 2-byte stores
-// (half of a 128-byte line per wave) and took twice as long. Vector memory completes in issue
-// order, so the wait sits before this tile's stores and the barriers order LDS only.
+// The rest of the backward for the tiles of head g, one 64-step tile at a time and nothing per
+// element written but dx: dxc = (its direct part, fp16 from the per-element pass) + sum_k dp[k]
+// wti[g][i][k] (fp16 MFMA, Wt resident), then the conv's transpose dx[t] = sum_j w_j dxc[t+3-j]
+// and the tile's partial sums dconv_w[j] += dxc[t] x[t-3+j]. dx of the tile's rows needs dxc of
+// the next three rows, so each tile computes dxc for 67 rows -- its own and three of the next
+// tile -- with one more pass of MFMAs over a 32-row tile of which three rows are kept (half as
+// many again MFMAs, no dependence between tiles and no dxc in HBM).
+// dp rows (fp16 pairs, dpa low) are staged one row per load instruction into rows padded by 16
+// bytes, so the A-operand reads of 32 rows fall on distinct banks; two tile buffers, tile k+1
+// loading while tile k is in the MFMAs. Per tile: [barrier] stage tile k+1, load the direct
+// part (16 bytes per lane, row-major), MFMAs, [barrier] the products (fp32) over the tile's own
+// dp buffer, [barrier] + direct part, [barrier] dx and the dconv_w sums (thread = channel pair x
+// 16 rows, x read 4 bytes per lane), [barrier] the sums over the four row blocks. The LDS detour
+// turns the accumulator layout (one channel per lane, rows 4 apart) into rows. Vector memory
+// completes in issue order and the barriers order LDS only.
 template <int DH> struct DxcTile {
   static_assert(DH == 128 || DH == 256, "resident dxc tile needs Dh in {128, 256}");
   static constexpr int kGPW = 1;          // 32-channel groups per wave
@@ -218,14 +222,25 @@ template <int DH> struct DxcTile {
   static constexpr int kKS = K / 16;
   static constexpr int kLd = K + 8;            // fp16 row stride (row bytes + 16)
   static constexpr int kLanesPerRow = K / 8;   // 16-byte pieces per row (<= 64)
+  static constexpr int kRowsX = kRows + 3;     // the tile and the next tile's first three rows
+  static constexpr int kLdo = DH + 4;          // fp32 row stride of the dxc rows
+  static constexpr int kPieces = kRowsX * DH / 8;                           // 16-byte pieces
+  static constexpr int kPer = (kPieces + kThreads - 1) / kThreads;          // per thread
+  static constexpr int kRB = kThreads / (DH / 2);  // row blocks of the conv's transpose (4)
+  static constexpr int kRBRows = kRows / kRB;      // 16
+  static_assert(kRowsX * kLdo * 4 == kRowsX * kLd * 2, "dxc rows fill one dp buffer");
+  static_assert(kRB == 4, "four row blocks");
 };
 
 template <int DH>
 __global__ __launch_bounds__(DxcTile<DH>::kThreads, 2) void tile_dxc(
-    const uint32_t *__restrict__ dp, const uint16_t *__restrict__ wti, uint16_t *__restrict__ dxc,
-    int B, int T, int D, int H, int per) {
+    const uint32_t *__restrict__ dp, const uint16_t *__restrict__ wti,
+    const uint16_t *__restrict__ dxd, const bf16_t *__restrict__ x,
+    const bf16_t *__restrict__ conv_w, bf16_t *__restrict__ dx, float *__restrict__ pcw, int B,
+    int T, int D, int H, int per) {
   typedef DxcTile<DH> F;
-  __shared__ __attribute__((aligned(16))) uint16_t la[2 * kRows * F::kLd];
+  __shared__ __attribute__((aligned(16))) uint16_t la[2 * F::kRowsX * F::kLd];
+  __shared__ float red[F::kRB * 4 * DH];  // [row block][tap][channel] partial sums
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -242,17 +257,28 @@ __global__ __launch_bounds__(DxcTile<DH>::kThreads, 2) void tile_dxc(
 #pragma unroll
     for (int ks = 0; ks < F::kKS; ++ks) wr[gi][ks] = load_f16x8(row + ks * 16);
   }
-  // staging: tile row r by wave r % kNW, lanes 0 .. kLanesPerRow-1; rows past T read zeros
+  // the conv's transpose: thread = channel pair pc (channels 2 pc, 2 pc + 1), rows rb * 16 ..
+  const int pc = tid % (DH / 2), rb = tid / (DH / 2);
+  float cw[4][2];  // taps of the two channels
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t v = *reinterpret_cast<const uint32_t *>(conv_w + static_cast<size_t>(j) * D +
+                                                           g * DH + 2 * pc);
+    cw[j][0] = bf16lo(v);
+    cw[j][1] = bf16hi(v);
+  }
+  // staging: tile row r (0 .. kRowsX - 1) by wave r % kNW, lanes 0 .. kLanesPerRow-1; rows past
+  // T read zeros
   const bool slane = lane < F::kLanesPerRow;
   auto stage = [&](int j, int buf) {
     const int b = j % B, t0 = (j / B) * kRows;
     const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint32_t *>(dp + static_cast<size_t>(b) * T * D), static_cast<short>(0),
-        T * D * 4, kWord3);
+        rec_bytes(T, D, 4u), kWord3);
     if (slane) {
-      for (int r = w; r < kRows; r += F::kNW) {
-        const unsigned off = static_cast<unsigned>(((t0 + r) * D + g * DH) * 4 + lane * 16);
-        dma_16b(seq, off, lds_addr(la + (buf * kRows + r) * F::kLd));
+      for (int r = w; r < F::kRowsX; r += F::kNW) {
+        const unsigned off = row_bytes(t0 + r, D, 4u) + static_cast<unsigned>(g * DH * 4 + lane * 16);
+        dma_16b(seq, off, lds_addr(la + (buf * F::kRowsX + r) * F::kLd));
       }
     }
   };
@@ -261,66 +287,122 @@ __global__ __launch_bounds__(DxcTile<DH>::kThreads, 2) void tile_dxc(
   __builtin_amdgcn_s_waitcnt(0x0F70);
   for (int it = 0; j < ntiles; j += per, ++it) {
     // this tile's rows are in buffer it & 1; the other buffer's readers (the previous tile's
-    // MFMAs and product reads) are past this barrier
+    // MFMAs and dxc reads) are past this barrier
     lds_barrier();
-    // the next tile's rows, then the dxc values this lane updates (neither depends on the MFMAs;
-    // both land while they run)
     const int jn = j + per;
     if (jn < ntiles) stage(jn, (it + 1) & 1);
     const int b = j % B, t0 = (j / B) * kRows;
-    // this tile's dxc values, 16 bytes (8 channels) per lane and piece, rows past T as zeros
-    constexpr int kPieces = kRows * DH / 8;
-    constexpr int kPer = kPieces / F::kThreads;
-    static_assert(kPieces % F::kThreads == 0, "pieces per thread");
-    uint16_t *tile = dxc + (static_cast<size_t>(b) * T + t0) * D + g * DH;
-    u32x4_t dv[kPer];
+    // the direct part of dxc of rows t0 .. t0 + 66, 16 bytes (8 channels) per lane and piece,
+    // rows past T as zeros
+    const uint16_t *dtile = dxd + (static_cast<size_t>(b) * T + t0) * D + g * DH;
+    u32x4_t dv[F::kPer];
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
+    for (int q = 0; q < F::kPer; ++q) {
       const int idx = tid + q * F::kThreads, r = idx / (DH / 8), c8 = idx % (DH / 8);
-      dv[q] = t0 + r < T ? *reinterpret_cast<const u32x4_t *>(tile + static_cast<size_t>(r) * D + 8 * c8)
-                         : u32x4_t{0u, 0u, 0u, 0u};
+      dv[q] = idx < F::kPieces && t0 + r < T
+                  ? *reinterpret_cast<const u32x4_t *>(dtile + static_cast<size_t>(r) * D + 8 * c8)
+                  : u32x4_t{0u, 0u, 0u, 0u};
     }
-    const uint16_t *lt = la + (it & 1) * kRows * F::kLd;
-    f32x16_t acc[F::kGPW][2];
+    const uint16_t *lt = la + (it & 1) * F::kRowsX * F::kLd;
+    f32x16_t acc[F::kGPW][3];  // row tiles: rows 0-31, 32-63, 64-95 (of which 64-66 are kept)
 #pragma unroll
-    for (int gi = 0; gi < F::kGPW; ++gi) acc[gi][0] = acc[gi][1] = f32x16_t{};
+    for (int gi = 0; gi < F::kGPW; ++gi) acc[gi][0] = acc[gi][1] = acc[gi][2] = f32x16_t{};
+    const int rx = min(64 + lrow, F::kRowsX - 1);  // the third tile's row (clamped: not kept)
 #pragma unroll
     for (int ks = 0; ks < F::kKS; ++ks)
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const f16x8_t af = load_f16x8(lt + (rt * 32 + lrow) * F::kLd + ks * 16 + half * 8);
+      for (int rt = 0; rt < 3; ++rt) {
+        const int row = rt < 2 ? rt * 32 + lrow : rx;
+        const f16x8_t af = load_f16x8(lt + row * F::kLd + ks * 16 + half * 8);
 #pragma unroll
         for (int gi = 0; gi < F::kGPW; ++gi)
           acc[gi][rt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, wr[gi][ks], acc[gi][rt], 0, 0, 0);
       }
-    // the products, row-major in fp32, over this tile's dp rows (kRows x (DH + 4) floats: the
-    // same bytes as kRows x kLd fp16)
-    constexpr int kLdo = DH + 4;
-    static_assert(kRows * kLdo * 4 == kRows * F::K * 2 + kRows * 16, "product tile fits");
-    float *po = reinterpret_cast<float *>(la + (it & 1) * kRows * F::kLd);
+    // the products, row-major in fp32, over this tile's dp rows
+    float *po = reinterpret_cast<float *>(la + (it & 1) * F::kRowsX * F::kLd);
     lds_barrier();  // every wave is done with this tile's dp rows
 #pragma unroll
     for (int gi = 0; gi < F::kGPW; ++gi)
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < 3; ++rt)
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj)
-          po[(rt * 32 + 8 * (jj >> 2) + 4 * half + (jj & 3)) * kLdo + ci0 + 32 * gi] = acc[gi][rt][jj];
-    lds_barrier();  // products complete
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile's staging and the dxc values
+        for (int jj = 0; jj < 16; ++jj) {
+          const int r = rt * 32 + 8 * (jj >> 2) + 4 * half + (jj & 3);
+          if (rt < 2 || r < F::kRowsX) po[r * F::kLdo + ci0 + 32 * gi] = acc[gi][rt][jj];
+        }
+    // x rows t0 + 16 rb - 3 .. t0 + 16 rb + 15 of this thread's channel pair (the dconv_w sums),
+    // in flight while the products and the direct part are added
+    uint32_t xw[F::kRBRows + 3];
+    {
+      const bf16_t *xs = x + (static_cast<size_t>(b) * T) * D + g * DH + 2 * pc;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int idx = tid + q * F::kThreads, r = idx / (DH / 8), c8 = idx % (DH / 8);
-      if (t0 + r < T) {
-        const float4 p0 = *reinterpret_cast<const float4 *>(po + r * kLdo + 8 * c8);
-        const float4 p1 = *reinterpret_cast<const float4 *>(po + r * kLdo + 8 * c8 + 4);
-        u32x4_t o;
-        o[0] = pack_f16x2(f16lo(dv[q][0]) + p0.x, f16hi(dv[q][0]) + p0.y);
-        o[1] = pack_f16x2(f16lo(dv[q][1]) + p0.z, f16hi(dv[q][1]) + p0.w);
-        o[2] = pack_f16x2(f16lo(dv[q][2]) + p1.x, f16hi(dv[q][2]) + p1.y);
-        o[3] = pack_f16x2(f16lo(dv[q][3]) + p1.z, f16hi(dv[q][3]) + p1.w);
-        *reinterpret_cast<u32x4_t *>(tile + static_cast<size_t>(r) * D + 8 * c8) = o;
+      for (int k = 0; k < F::kRBRows + 3; ++k) {
+        const int t = t0 + rb * F::kRBRows - 3 + k;
+        xw[k] = t >= 0 && t < T ? *reinterpret_cast<const uint32_t *>(xs + static_cast<size_t>(t) * D)
+                                : 0u;
       }
+    }
+    lds_barrier();  // products complete
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile's staging, direct part, x rows
+#pragma unroll
+    for (int q = 0; q < F::kPer; ++q) {
+      const int idx = tid + q * F::kThreads, r = idx / (DH / 8), c8 = idx % (DH / 8);
+      if (idx < F::kPieces) {
+        float4 *pp = reinterpret_cast<float4 *>(po + r * F::kLdo + 8 * c8);
+        float4 p0 = pp[0], p1 = pp[1];
+        p0.x += f16lo(dv[q][0]);
+        p0.y += f16hi(dv[q][0]);
+        p0.z += f16lo(dv[q][1]);
+        p0.w += f16hi(dv[q][1]);
+        p1.x += f16lo(dv[q][2]);
+        p1.y += f16hi(dv[q][2]);
+        p1.z += f16lo(dv[q][3]);
+        p1.w += f16hi(dv[q][3]);
+        pp[0] = p0;
+        pp[1] = p1;
+      }
+    }
+    lds_barrier();  // dxc of the 67 rows complete
+    // dx[t] = sum_j w_j dxc[t + 3 - j] over this thread's 16 rows; dconv_w[j] += dxc[t] x[t-3+j]
+    {
+      float s[4][2] = {};
+      const float *pr = po + 2 * pc;
+      bf16_t *dxs = dx + (static_cast<size_t>(b) * T) * D + g * DH + 2 * pc;
+      float2 gw[4];  // dxc rows r .. r + 3
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        gw[k + 1] = *reinterpret_cast<const float2 *>(pr + (rb * F::kRBRows + k) * F::kLdo);
+#pragma unroll
+      for (int u = 0; u < F::kRBRows; ++u) {
+        const int r = rb * F::kRBRows + u;
+        gw[0] = gw[1];
+        gw[1] = gw[2];
+        gw[2] = gw[3];
+        gw[3] = *reinterpret_cast<const float2 *>(pr + (r + 3) * F::kLdo);
+        const float v0 = fmaf(cw[0][0], gw[3].x, fmaf(cw[1][0], gw[2].x,
+                                                      fmaf(cw[2][0], gw[1].x, cw[3][0] * gw[0].x)));
+        const float v1 = fmaf(cw[0][1], gw[3].y, fmaf(cw[1][1], gw[2].y,
+                                                      fmaf(cw[2][1], gw[1].y, cw[3][1] * gw[0].y)));
+        if (t0 + r < T)
+          *reinterpret_cast<uint32_t *>(dxs + static_cast<size_t>(t0 + r) * D) = pack_bf16x2(v0, v1);
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {  // x[t - 3 + jt] is xw[u + jt]
+          s[jt][0] = fmaf(gw[0].x, bf16lo(xw[u + jt]), s[jt][0]);
+          s[jt][1] = fmaf(gw[0].y, bf16hi(xw[u + jt]), s[jt][1]);
+        }
+      }
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+        *reinterpret_cast<float2 *>(red + (rb * 4 + jt) * DH + 2 * pc) = make_float2(s[jt][0], s[jt][1]);
+    }
+    lds_barrier();  // row-block sums ready
+    // the tile's dconv_w partial sums, in a fixed order: pcw[b][tile][j][d]
+    for (int i = tid; i < 4 * DH; i += F::kThreads) {
+      const int jt = i / DH, c = i % DH;
+      float v = 0.0f;
+#pragma unroll
+      for (int q = 0; q < F::kRB; ++q) v += red[(q * 4 + jt) * DH + c];
+      pcw[((static_cast<size_t>(b) * nTT + t0 / kRows) * 4 + jt) * D + g * DH + c] = v;
     }
   }
 }
@@ -369,14 +451,24 @@ hipError_t launch_resident_preacts(const void *x, const void *conv_w, const void
   return hipGetLastError();
 }
 
-hipError_t launch_resident_dxc(const void *dp, const void *wti, uint16_t *dxc, int B, int T, int D,
-                               int H, hipStream_t s) {
+hipError_t launch_resident_dxc(const void *dp, const void *wti, const uint16_t *dxd,
+                               const void *x, const void *conv_w, void *dx, float *pcw, int B,
+                               int T, int D, int H, hipStream_t s) {
   const int per = std::max(1, cu_count() / H);
   const uint32_t *p = static_cast<const uint32_t *>(dp);
   const uint16_t *wt = static_cast<const uint16_t *>(wti);
+  const bf16_t *xx = static_cast<const bf16_t *>(x);
+  const bf16_t *cw = static_cast<const bf16_t *>(conv_w);
+  bf16_t *dd = static_cast<bf16_t *>(dx);
   switch (D / H) {
-    case 128: tile_dxc<128><<<H * per, DxcTile<128>::kThreads, 0, s>>>(p, wt, dxc, B, T, D, H, per); break;
-    case 256: tile_dxc<256><<<H * per, DxcTile<256>::kThreads, 0, s>>>(p, wt, dxc, B, T, D, H, per); break;
+    case 128:
+      tile_dxc<128><<<H * per, DxcTile<128>::kThreads, 0, s>>>(p, wt, dxd, xx, cw, dd, pcw, B, T,
+                                                                D, H, per);
+      break;
+    case 256:
+      tile_dxc<256><<<H * per, DxcTile<256>::kThreads, 0, s>>>(p, wt, dxd, xx, cw, dd, pcw, B, T,
+                                                                D, H, per);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

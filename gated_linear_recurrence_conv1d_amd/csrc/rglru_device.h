@@ -153,6 +153,17 @@ __device__ __forceinline__ void st_relaxed(unsigned long long *p, unsigned long 
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Byte count or offset of n rows of D elements of `bytes` bytes, in unsigned 32-bit arithmetic:
+// callers keep every such value below 2^32 (the buffer descriptors' range), and a negative row
+// (the conv halo before t = 0) wraps past the end of the buffer, as the range check needs.
+__device__ __forceinline__ unsigned row_bytes(int rows, int D, unsigned bytes) {
+  return static_cast<unsigned>(rows) * static_cast<unsigned>(D) * bytes;
+}
+// The same as the int the buffer-descriptor builtin takes for its record count.
+__device__ __forceinline__ int rec_bytes(int T, int D, unsigned bytes) {
+  return __builtin_bit_cast(int, row_bytes(T, D, bytes));
+}
+
 // One 16-byte-per-lane buffer load straight into LDS (the wave's 64 lanes fill 1 KB from byte
 // lds_base on), written as inline asm: for the builtin form the compiler cannot tell which LDS
 // bytes the load writes, so it makes later LDS reads -- and every __syncthreads -- wait for all of

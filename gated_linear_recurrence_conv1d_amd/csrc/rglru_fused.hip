@@ -109,7 +109,7 @@ __device__ __forceinline__ void stage_x(const bf16_t *__restrict__ x, bf16_t *xr
   constexpr int kPerWave = (F::kLoads + NW - 1) / NW;
   const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16_t *>(x + static_cast<size_t>(b) * T * D), static_cast<short>(0),
-      T * D * 2, kBufferWord3);
+      rec_bytes(T, D, 2u), kBufferWord3);
   // opaque: keeps the compiler from folding the lane's row into a 64-bit multiply-add per load
   unsigned lane_off =
       static_cast<unsigned>((lane / kLanesPerRow) * 2 * D + g * DH * 2 + (lane % kLanesPerRow) * 16);
@@ -118,7 +118,7 @@ __device__ __forceinline__ void stage_x(const bf16_t *__restrict__ x, bf16_t *xr
   for (int k = 0; k < kPerWave; ++k) {
     const int i = w + k * NW;  // wave-uniform
     if (kPerWave * NW == F::kLoads || i < F::kLoads) {
-      const unsigned row_off = static_cast<unsigned>((t0 - 3 + i * F::kRowsPerLoad) * 2 * D);
+      const unsigned row_off = row_bytes(t0 - 3 + i * F::kRowsPerLoad, D, 2u);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(seq, (lds_void *)(xr + i * F::kRowsPerLoad * DH),
                                                16, row_off + lane_off, 0, 0, 0);
     }

@@ -71,8 +71,11 @@ hipError_t launch_resident_preacts(const void *x, const void *conv_w, const void
                                    const float *b_a, const void *W_x, const float *b_x,
                                    void *pre, int B, int T, int D, int H, hipStream_t s,
                                    bool split);
-hipError_t launch_resident_dxc(const void *dp, const void *wti, uint16_t *dxc, int B, int T, int D,
-                               int H, hipStream_t s);
+// dxd: the direct part of dxc (fp16, from the per-element pass); writes dx and the dconv_w
+// partial sums pcw[B][ceil(T / 64)][4][D] (the conv's transpose fused in).
+hipError_t launch_resident_dxc(const void *dp, const void *wti, const uint16_t *dxd,
+                               const void *x, const void *conv_w, void *dx, float *pcw, int B,
+                               int T, int D, int H, hipStream_t s);
 
 // The backward's per-element part in one pass over kFusedBwdRows-step tiles, latest first (bf16, Dh in
 // {128, 256}, T * D * 4 < 2^31): pre-activations recomputed on MFMA, the adjoint carried from
