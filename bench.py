@@ -437,6 +437,13 @@ def backward_leg(torch, rg, w, g, y, warmup=200, reps=100):
     nbytes = 4 * n * eb + params + grads + 2 * 4 * B * D
     gbs = nbytes / (ms * 1e-3) / 1e9
     traffic = measured_traffic("backward", w.name, "hbm_bytes_per_call", BACKWARD_SOURCES)
+    # The three gate contractions of the backward, 2 n 2Dh flops each: the pre-activations
+    # recomputed, dxc = dp W, dW = dp^T xc. Executed on the matrix cores (bf16 I/O, Dh in {128,
+    # 256}): the pre-activations twice (conv output as bf16 hi + lo) and dxc one half again (each
+    # tile also computes three rows of the next one), 4.5 contractions in all.
+    flops = 3 * 2.0 * n * 2 * Dh
+    executed = 4.5 * 2.0 * n * 2 * Dh if io == torch.bfloat16 and Dh in (128, 256) else None
+    tf = flops / (ms * 1e-3) / 1e12
     return {"workload": w.name, "ms": round(ms, 4), "value": n / (ms * 1e-3),
             "unit": "tokens·channels/s", "reps": reps, "warmup": warmup,
             "workspace_bytes": ws.numel(),
@@ -444,7 +451,14 @@ def backward_leg(torch, rg, w, g, y, warmup=200, reps=100):
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "algorithmic_bytes": nbytes, "traffic": traffic,
                          "note": "whole backward call (all kernels) against x, y, dy in + dx out; "
-                                 "traffic = measured HBM bytes of all its kernels per call"}}
+                                 "traffic = measured HBM bytes of all its kernels per call"},
+            "roofline_mfma": {"bound": "mfma", "achieved": round(tf, 1),
+                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "algorithmic_flops": flops, "executed_flops": executed,
+                              "executed_frac": (round(executed / (ms * 1e-3) / 1e12
+                                                      / MFMA_BF16_PEAK_TFLOPS, 4)
+                                                if executed else None)}}
 
 
 def mqa_leg(torch, rg, warmup=20, reps=50):
