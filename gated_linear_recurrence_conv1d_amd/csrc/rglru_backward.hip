@@ -641,8 +641,10 @@ __global__ __launch_bounds__(kBwdThreads) void conv_bwd(const T *__restrict__ x,
 // contiguous, as pairs of rows: a row of 32 k plus 4 pad is 72 bytes, so the 4-byte stores of
 // one instruction (16 row pairs x 2 octets of m per half-wave) hit 32 distinct banks and the
 // 16-byte operand reads, taken as two 8-byte halves, distinct banks too. The LDS holds two
-// steps: step s+1's loads are issued before step s's MFMAs and stored into the other buffer
-// after them, one barrier per step.
+// steps and the registers the loads of two more: step s+2's loads are issued before step s's
+// MFMAs, and step s+1 (loaded a step earlier) is converted into the other buffer after them,
+// one barrier per step. (With one step of look-ahead each step waited for the round trip of the
+// loads it had just issued: 133 against 104 us per call at B8 T2048 D2560 H10.)
 // Precision: both operands in fp16 (dp as stored, xc rounded once), one MFMA per tile and k-step.
 // With bf16 operands (2^-9) a dW element erred by up to a few percent of the tensor's rms -- dW
 // sums terms of both signs and the gate gradients are heavy tailed (dz carries 1/m); fp16's 2^-11
@@ -677,9 +679,21 @@ __global__ __launch_bounds__(kDwThreads, 1) void dw_mfma(const bf16_t *__restric
                                                          int H, int rows, int rows_per_split) {
   typedef DwTile<DH> C;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * C::kBufElems];
-  const int mt = blockIdx.x;
-  const int g = blockIdx.y;
-  const int sp = blockIdx.z;
+  // (head, split) groups in a 1-D grid. With two m tiles per head, the pair of workgroups that
+  // share a group's x rows are 8 apart: workgroups go to the 8 XCDs round-robin, so both land
+  // on one XCD and its L2 serves the second read of x.
+  const int nsplit = (rows + rows_per_split - 1) / rows_per_split;
+  int mt, grp;
+  if constexpr (C::kMt == 1) {
+    mt = 0;
+    grp = blockIdx.x;
+  } else {
+    mt = (blockIdx.x >> 3) & 1;
+    grp = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7);
+  }
+  if (grp >= H * nsplit) return;  // padding of the last set of 16 (uniform per workgroup)
+  const int g = grp % H;
+  const int sp = grp / H;
   const int kb = sp * rows_per_split;
   const int ke = min(kb + rows_per_split, rows);
   const int nsteps = (ke - kb + kDwRows - 1) / kDwRows;
@@ -710,41 +724,40 @@ __global__ __launch_bounds__(kDwThreads, 1) void dw_mfma(const bf16_t *__restric
       w23[2 * h + 1] = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(cwv[3][h], cwv[2][h], kHiPair));
     }
   }
-  // prefetch registers: the rows of the next step
-  u32x4_t ra[2];  // [row u]
-  u32x4_t rx[5];  // x rows r0 - 3 .. r0 + 1
-  auto load_dp = [&](int st, u32x4_t (&pa)[2]) {
+  // prefetch registers: the dp rows [u] and x rows r0 - 3 .. r0 + 1 of a step; two sets, so
+  // that a step's loads are in flight for two steps' MFMAs
+  u32x4_t ra0[2], ra1[2];
+  u32x4_t rx0[5], rx1[5];
+  // The loads are unconditional, their rows clamped into the tensor (a load under a per-lane
+  // branch makes the compiler wait for every outstanding load before the next use of any); rows
+  // past the split are zeroed when the step is converted, and taps before a sequence's start by
+  // the conv's own mask.
+  auto load_step = [&](int st, u32x4_t (&pa)[2], u32x4_t (&rx)[5]) {
     const int r0 = kb + st * kDwRows + 2 * lq;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int rr = r0 + u;
-      pa[u] = rr < ke ? *reinterpret_cast<const u32x4_t *>(dpre + static_cast<size_t>(rr) * D + a_col)
-                      : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
-  auto load_x = [&](int st) {
-    const int r0 = kb + st * kDwRows + 2 * lq;
+    for (int u = 0; u < 2; ++u)
+      pa[u] = *reinterpret_cast<const u32x4_t *>(
+          dpre + static_cast<size_t>(min(r0 + u, rows - 1)) * D + a_col);
 #pragma unroll
-    for (int k = 0; k < 5; ++k) {
-      const int rr = r0 - 3 + k;
-      if (bload && rr >= 0 && rr < ke)
-        rx[k] = *reinterpret_cast<const u32x4_t *>(x + static_cast<size_t>(rr) * D + b_col);
-      else
-        rx[k] = u32x4_t{0u, 0u, 0u, 0u};
-    }
+    for (int k = 0; k < 5; ++k)
+      rx[k] = *reinterpret_cast<const u32x4_t *>(
+          x + static_cast<size_t>(min(max(r0 - 3 + k, 0), rows - 1)) * D + b_col);
   };
   // conv, fp16 rounding and transposed stores of one step into buffer `buf`
-  auto store_step = [&](int st, int buf, const u32x4_t (&pa)[2]) {
+  auto store_step = [&](int st, int buf, const u32x4_t (&pa)[2], const u32x4_t (&rx)[5]) {
     uint16_t *A = lds + buf * C::kBufElems;
     uint16_t *Bm = A + C::kAElems;
+    const int k0 = kb + st * kDwRows;
+    const int r0 = k0 + 2 * lq;
+    const bool in0 = r0 < ke, in1 = r0 + 1 < ke;  // rows of this split
     // A: m = 8 lj + cc is half cc & 1 (dpa even, dpx odd) of pair cc >> 1; rows 2 lq, 2 lq + 1
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc)
-      *reinterpret_cast<uint32_t *>(A + (8 * lj + cc) * kDwLd + 2 * lq) =
-          __builtin_amdgcn_perm(pa[1][cc >> 1], pa[0][cc >> 1], (cc & 1) ? kHiPair : kLoPair);
-    if (!bload) return;
-    const int k0 = kb + st * kDwRows;
-    const int r0 = k0 + 2 * lq;
+      *reinterpret_cast<uint32_t *>(A + (8 * lj + cc) * kDwLd + 2 * lq) = __builtin_amdgcn_perm(
+          in1 ? pa[1][cc >> 1] : 0u, in0 ? pa[0][cc >> 1] : 0u, (cc & 1) ? kHiPair : kLoPair);
+    // (every thread converts x rows at Dh 256; a per-lane branch here would cost the steady
+    // loop its load accounting, as above)
+    if (DH < 256 && !bload) return;
     // Does this step hold one of the first three rows of a sequence (uniform over the
     // workgroup)? Only then do conv taps need masking at the sequence start.
     const int f = k0 % Tn;
@@ -778,7 +791,7 @@ __global__ __launch_bounds__(kDwThreads, 1) void dw_mfma(const bf16_t *__restric
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc)
       *reinterpret_cast<uint32_t *>(Bm + (8 * lj + cc) * kDwLd + 2 * lq) =
-          pack_f16x2(xcv[0][cc], xcv[1][cc]);
+          pack_f16x2(in0 ? xcv[0][cc] : 0.0f, in1 ? xcv[1][cc] : 0.0f);
   };
 
   const int w = tid >> 6;
@@ -810,22 +823,41 @@ __global__ __launch_bounds__(kDwThreads, 1) void dw_mfma(const bf16_t *__restric
       }
     }
   };
-  // Step st: operands in LDS buffer st & 1; step st + 1 is loaded before its MFMAs and
-  // converted into the other buffer after them.
-  load_dp(0, ra);
-  load_x(0);
-  store_step(0, 0, ra);
-  __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    const bool more = st + 1 < nsteps;
-    if (more) {
-      load_dp(st + 1, ra);
-      load_x(st + 1);
-    }
+  // Step st: operands in LDS buffer st & 1. Its MFMAs run while step st + 1's loads (issued a
+  // step earlier) and step st + 2's (issued now, into the registers step st's conversion has
+  // freed) are in flight; step st + 1 is then converted into the other buffer. One step of
+  // look-ahead left every step waiting on the round trip of the loads it had just issued.
+  // The steady-state loop has no conditions: on a path that skips a step's loads the compiler
+  // can no longer tell which loads are outstanding and waits for all of them. The last steps
+  // (at most three) take the conditional form.
+  auto body = [&](int st, const u32x4_t (&pa_next)[2], const u32x4_t (&rx_next)[5],
+                  u32x4_t (&pa_free)[2], u32x4_t (&rx_free)[5]) {
+    load_step(st + 2, pa_free, rx_free);
+    __builtin_amdgcn_sched_barrier(0);  // the loads go out first, not after the conversion
     mfma_step(st & 1);
-    if (more) store_step(st + 1, (st + 1) & 1, ra);
+    store_step(st + 1, (st + 1) & 1, pa_next, rx_next);
     __syncthreads();
+  };
+  auto tail = [&](int st, const u32x4_t (&pa_next)[2], const u32x4_t (&rx_next)[5],
+                  u32x4_t (&pa_free)[2], u32x4_t (&rx_free)[5]) {
+    if (st >= nsteps) return;
+    if (st + 2 < nsteps) load_step(st + 2, pa_free, rx_free);
+    mfma_step(st & 1);
+    if (st + 1 < nsteps) store_step(st + 1, (st + 1) & 1, pa_next, rx_next);
+    __syncthreads();
+  };
+  load_step(0, ra0, rx0);
+  if (nsteps > 1) load_step(1, ra1, rx1);
+  store_step(0, 0, ra0, rx0);
+  __syncthreads();
+  int st = 0;
+  for (; st + 3 < nsteps; st += 2) {
+    body(st, ra1, rx1, ra0, rx0);
+    body(st + 1, ra0, rx0, ra1, rx1);
   }
+  tail(st, ra1, rx1, ra0, rx0);
+  tail(st + 1, ra0, rx0, ra1, rx1);
+  tail(st + 2, ra1, rx1, ra0, rx0);
   // ---- partial out: pw[sp][gate][g][o][i], m = 2 o + gate
   const size_t gstride = static_cast<size_t>(H) * DH * DH;
 #pragma unroll
@@ -1113,12 +1145,14 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
   const int rows = B * Tn;  // < 2^31, checked by the caller
   if constexpr (sizeof(T) == 2) {
     if (L.mfma_dw) {
+      // (head, split) groups; two m tiles per head at Dh 256 go out in sets of 16 workgroups
+      const int groups = H * L.S;
       if (Dh == 256)
-        dw_mfma<256><<<dim3(DwTile<256>::kMt, H, L.S), kDwThreads, 0, s>>>(
+        dw_mfma<256><<<16 * ((groups + 7) / 8), kDwThreads, 0, s>>>(
             x, dpre, conv_w, pw, Tn, D, H, rows, L.rows_per_split);
       else
-        dw_mfma<128><<<dim3(DwTile<128>::kMt, H, L.S), kDwThreads, 0, s>>>(
-            x, dpre, conv_w, pw, Tn, D, H, rows, L.rows_per_split);
+        dw_mfma<128><<<groups, kDwThreads, 0, s>>>(x, dpre, conv_w, pw, Tn, D, H, rows,
+                                                    L.rows_per_split);
     }
   }
   if (!L.mfma_dw) {
