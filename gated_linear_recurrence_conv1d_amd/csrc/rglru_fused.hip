@@ -19,9 +19,11 @@
 //   2. [64 x Dh] x [Dh x 2Dh] on v_mfma_f32_32x32x16_bf16, fp32 accumulators; the B operand is
 //      this head's W_a / W_x rows, resident in registers for the kernel's life;
 //   3. gates elementwise in the accumulator layout -> (a, u) per element;
-//   4. scan inside the tile: each lane owns one channel and four runs of 4 consecutive steps per
-//      32-row tile, interleaved with its partner lane (lane ^ 32); in-lane scans of the runs,
-//      then a chain over the 16 runs in time order with the partner's values fetched by lane swap;
+//   4. scan inside the tile: the MFMA A operand's rows are permuted so that each lane holds two
+//      runs of 16 consecutive steps of its channel, the lanes of the other half the two runs in
+//      between; runs are scanned in-lane, their affine maps exchanged between the halves with
+//      v_permlane32_swap and chained in every lane. Row tile 1's MFMAs are interleaved with
+//      row tile 0's gate math;
 //   5. decoupled look-back: publish the tile's aggregate (A, U) per channel, walk back over the
 //      predecessor tiles of the same (sequence, head), combining aggregates until an inclusive
 //      state (or the sequence start) is found, publish this tile's inclusive state;
@@ -59,7 +61,7 @@ template <int DH> struct Fused {
   static constexpr int kThreads = 64 * kNW;
   static constexpr int kKS = DH / 16;                // MFMA k-steps
   static constexpr int kLda = DH + 8;                // bf16 A-tile row stride (elements)
-  static constexpr int kLdx = DH + 4;                // fp32 conv-output row stride (floats)
+  static constexpr int kLdx = DH + 2;  // fp32 conv-output row stride: rows 16 apart 32 banks apart
   static constexpr int kRowsPerLoad = 1024 / (2 * DH);  // x rows per wave-wide 16 B/lane load
   static constexpr int kLoads = (kFusedRows + 3 + kRowsPerLoad - 1) / kRowsPerLoad;
   static constexpr int kXRows = kLoads * kRowsPerLoad;  // staged rows (tile + 3-row halo)
@@ -180,83 +182,38 @@ __device__ __forceinline__ void conv_prologue(const bf16_t *xr, bf16_t *xa, floa
   }
 }
 
-// Gates and in-tile scan of one tile, in the accumulator layout. Accumulator jj of this lane
-// holds tile row rt*32 + 8*(jj/4) + 4*half + (jj%4): run k = rt*4 + jj/4 covers 4 consecutive
-// rows; in time order the runs alternate between the halves (run index 2k + half). On return
-// acc[rt][0][jj] is the product of a from the start of its run and acc[rt][1][jj] the state
-// reached from 0 at the start of its run; (qz[k], cz[k]) is the start of this lane's run k as an
-// affine map of the tile's carry-in; (At, Ut) is the whole tile's map.
-// expm1(log a): kds = kd 2^-nh with nh (wave-uniform) the smallest power that brings every
-// channel's kd into the polynomial's range [-1/4, 0]; the polynomial gives e' = expm1(z 2^-nh)
-// and nh doublings e <- e (e + 2) (exact algebra of expm1(2z) = expm1(z)(expm1(z) + 2), no
-// cancellation) recover e. nh = 0 for decays with a^c >= e^-1/4, which is every channel of the
-// usual configurations; the loop is wave-uniform, so that case costs nothing per element.
-template <int DH>
-__device__ __forceinline__ void gate_scan(f32x16_t (&acc)[2][2], const float *xf, int lane, int cl,
-                                          float kds, int nh, float ba2, float bx2, float (&cz)[8],
-                                          float (&qz)[8], float &At, float &Ut) {
-  typedef Fused<DH> F;
-  const int half = lane >> 5;
-  // (a) recurrence gate -> e = expm1(log a), overwriting the pa accumulator. The sigmoids take
-  // exp2(-log2(e) (acc + b)), with ba2 = -log2(e) b_a folded into one FMA.
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const float r = __builtin_amdgcn_rcpf(
-          1.0f + __builtin_amdgcn_exp2f(fmaf(acc[rt][0][jj], -kLog2e, ba2)));
-      acc[rt][0][jj] = expm1_poly(kds * r);
-      if ((jj & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-    }
+// Both halves' values of v in every lane: lo from lane (l & 31), hi from lane (l | 32).
+// v_permlane32_swap exchanges lanes 32..63 of its first operand with lanes 0..31 of its second;
+// with both operands holding v, the first then holds the low half twice and the second the high.
+__device__ __forceinline__ void halves(float v, float &lo, float &hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
+// One element of the gate math and of its run's scan. From the accumulators (pa, px):
+// r = sigmoid(pa) with exp2(-log2(e) (pa + b_a)) (ba2 = -log2(e) b_a folded into one FMA);
+// e = expm1(log a) = expm1(kd r) as the polynomial of kd r 2^-nh followed by nh exact doublings
+// e <- e (e + 2) (nh is wave-uniform, 0 unless the wave holds a channel with a^c < e^-1/4);
+// a = 1 + e, m = sqrt(1 - a^2) = sqrt(-e (2 + e)), i = sigmoid(px), u = m i x. Then the run's
+// product and state advance, P <- P a, S <- a S + u (from P = 1, S = 0 at the run's start); the
+// caller overwrites the accumulators with (P, S).
+__device__ __forceinline__ void gate_step(float pa, float px, float xv, float kds, int nh,
+                                          float ba2, float bx2, float &P, float &S, bool first) {
+  const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(fmaf(pa, -kLog2e, ba2)));
+  float e = expm1_poly(kds * r);
   if (nh > 0) {
-    for (int i = 0; i < nh; ++i)
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) acc[rt][0][jj] *= acc[rt][0][jj] + 2.0f;
-    // a = exp(log a) >= 0: clamp what rounding (or an overflowing kd) may leave below -1
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) acc[rt][0][jj] = fmaxf(acc[rt][0][jj], -1.0f);
+    for (int i = 0; i < nh; ++i) e *= e + 2.0f;
+    e = fmaxf(e, -1.0f);  // a = exp(log a) >= 0: clamp what rounding may leave below -1
   }
-  // (b) input gate, normaliser, runs of 4 steps, and the chain over the 16 runs in time order:
-  // this lane's run k pairs with the partner half's run k (runs 2k and 2k+1 of the tile).
-  // One base address per lane, all rows as constant offsets from it.
-  const float *xfl = xf + 4 * half * F::kLdx + cl;
-  float c = 0.0f, qp = 1.0f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int rt = k >> 2, jb = k & 3;
-    float Pp = 1.0f, S = 0.0f;
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const int jj = jb * 4 + e4;
-      const float e = acc[rt][0][jj];
-      const float a = 1.0f + e;
-      const float m = __builtin_amdgcn_sqrtf(-e * (2.0f + e));
-      const float ig = __builtin_amdgcn_rcpf(
-          1.0f + __builtin_amdgcn_exp2f(fmaf(acc[rt][1][jj], -kLog2e, bx2)));
-      const float u = m * (ig * xfl[(rt * 32 + 8 * jb + e4) * F::kLdx]);
-      S = fmaf(a, S, u);
-      Pp *= a;
-      acc[rt][0][jj] = Pp;
-      acc[rt][1][jj] = S;
-    }
-    const float pa_ = __shfl_xor(Pp, 32, 64);
-    const float pu_ = __shfl_xor(S, 32, 64);
-    const float A0 = half ? pa_ : Pp, U0 = half ? pu_ : S;
-    const float A1 = half ? Pp : pa_, U1 = half ? S : pu_;
-    const float c1 = fmaf(A0, c, U0), q1 = qp * A0;  // start of run 2k+1
-    cz[k] = half ? c1 : c;
-    qz[k] = half ? q1 : qp;
-    c = fmaf(A1, c1, U1);
-    qp = q1 * A1;
-    // keep the scheduler from hoisting later runs' loads and transcendentals (live ranges)
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  At = qp;
-  Ut = c;
+  const float a = 1.0f + e;
+  const float m = __builtin_amdgcn_sqrtf(-e * (2.0f + e));
+  const float ig =
+      __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(fmaf(px, -kLog2e, bx2)));
+  const float u = m * (ig * xv);
+  S = first ? u : fmaf(a, S, u);
+  P = first ? a : P * a;
 }
 
 // One tile per loop iteration:
@@ -343,7 +300,14 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
     conv_prologue<DH>(xr, xa, xf, cws, tid);
     __syncthreads();
 
-    // ---- gate projections on MFMA: 64 rows x (32 channels x 2 gates) per wave.
+    // ---- gate projections on MFMA: 64 rows x (32 channels x 2 gates) per wave. The A operand's
+    // rows are permuted so that accumulator jj of lane (j, half) holds time row
+    // rt*32 + 16*half + jj: every lane owns two runs of 16 consecutive steps of its channel.
+    // Row tile 0 first; row tile 1's MFMAs are then interleaved, one k-step at a time, with the
+    // gate math and scan of row tile 0 (one step per k-step), so that the matrix cores and the
+    // vector ALU work at the same time.
+    const int prow = 16 * ((lrow >> 2) & 1) + 4 * (lrow >> 3) + (lrow & 3);
+    const bf16_t *xap = xa + prow * F::kLda + half * 8;
     f32x16_t acc[2][2];  // [row tile][gate]
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
@@ -352,12 +316,9 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
     }
 #pragma unroll
     for (int ks = 0; ks < F::kKS; ++ks) {
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const bf16x8_t af = load_bf16x8(xa + (rt * 32 + lrow) * F::kLda + ks * 16 + half * 8);
-        acc[rt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wa[ks], acc[rt][0], 0, 0, 0);
-        acc[rt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wx[ks], acc[rt][1], 0, 0, 0);
-      }
+      const bf16x8_t af = load_bf16x8(xap + ks * 16);
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wa[ks], acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wx[ks], acc[0][1], 0, 0, 0);
     }
 
     // ---- stage the next tile's rows (the prologue that read the buffer finished before the
@@ -368,9 +329,57 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
       if (jn < ntiles) stage_x<DH, 1>(x, xr, jn % B, (jn / B) * kFusedRows, g, 0, lane, T, D);
     }
 
-    float cz[8], qz[8], At, Ut;
-    gate_scan<DH>(acc, xf, lane, cl, kds, nh, ba2, bx2, cz, qz, At, Ut);
-
+    // x of this lane's runs, fp32 (time row rt*32 + 16*half + jj, channel cl)
+    const float *xfl = xf + 16 * half * F::kLdx + cl;
+    float Ar[2], Ur[2];
+    {
+      // one step of row tile 0 per k-step of row tile 1 (Dh < 256: the MFMAs end early); each
+      // step's x is read one step ahead
+      float P = 1.0f, S = 0.0f;
+      float xn = xfl[0];
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        if (ks < F::kKS) {
+          const bf16x8_t af = load_bf16x8(xap + 32 * F::kLda + ks * 16);
+          acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wa[ks], acc[1][0], 0, 0, 0);
+          acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wx[ks], acc[1][1], 0, 0, 0);
+        }
+        const float xv = xn;
+        if (ks + 1 < 16) xn = xfl[(ks + 1) * F::kLdx];
+        gate_step(acc[0][0][ks], acc[0][1][ks], xv, kds, nh, ba2, bx2, P, S, ks == 0);
+        acc[0][0][ks] = P;
+        acc[0][1][ks] = S;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      Ar[0] = P;
+      Ur[0] = S;
+    }
+    {
+      float P = 1.0f, S = 0.0f;
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        gate_step(acc[1][0][jj], acc[1][1][jj], xfl[(32 + jj) * F::kLdx], kds, nh, ba2, bx2, P,
+                  S, jj == 0);
+        acc[1][0][jj] = P;
+        acc[1][1][jj] = S;
+        if ((jj & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+      Ar[1] = P;
+      Ur[1] = S;
+    }
+    // Runs in time order: (row tile 0, half 0), (0, 1), (1, 0), (1, 1). Every lane gets all
+    // four maps and chains them: (q, c) = the start of one of its runs as an affine map of the
+    // tile's carry-in; (At, Ut) = the whole tile.
+    float A0, A1, A2, A3, U0, U1, U2, U3;
+    halves(Ar[0], A0, A1);
+    halves(Ar[1], A2, A3);
+    halves(Ur[0], U0, U1);
+    halves(Ur[1], U2, U3);
+    const float q2 = A1 * A0, c2 = fmaf(A1, U0, U1);
+    const float q3 = A2 * q2, c3 = fmaf(A2, c2, U2);
+    const float At = A3 * q3, Ut = fmaf(A3, c3, U3);
+    const float qa = half ? A0 : 1.0f, ca = half ? U0 : 0.0f;
+    const float qb = half ? q3 : q2, cb = half ? c3 : c2;
 
     // ---- decoupled look-back on half 0 (one channel per lane): publish this tile's aggregate
     // and put the first predecessor's word in flight...
@@ -422,35 +431,36 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
       else if (h_T && tc.t0 + kFusedRows == T)
         h_T[static_cast<size_t>(tc.b) * D + d] = h_end;
     }
-    h_in = __shfl(h_in, lrow, 64);
+    {
+      float hl, hh;
+      halves(h_in, hl, hh);
+      h_in = hl;
+    }
     // The staged rows must have landed before the barrier that opens the next tile; waiting here
     // (the look-back has mostly waited already) keeps this tile's stores out of the wait.
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
-    // ---- fix-up and store y. Each run of 4 rows converts two rows per bf16 pair and stores
-    // the halves separately. Row addresses are wave-uniform: a scalar row pointer plus the
-    // lane's 32-bit byte offset (its channel and its half's 4-row shift). Dv is re-materialised
+    // ---- fix-up h_t = P_t * (state at its run's start) + S_t and store y, two rows per bf16
+    // conversion, the halves stored separately. Row addresses are wave-uniform: a scalar row
+    // pointer plus the lane's 32-bit byte offset (its channel and its half's 16-row shift). Dv is
+    // re-materialised
     // through an empty asm so that the compiler cannot hoist the 32 row offsets out of the tile
     // loop (it would keep them in registers, spill them and reload one per store).
     unsigned Dv = static_cast<unsigned>(D);
     asm volatile("" : "+s"(Dv));
     const char *yg = reinterpret_cast<const char *>(
         y + (static_cast<size_t>(tc.b) * T + tc.t0) * D + g * DH);  // tile row 0, head g
-    const unsigned lane_off = (static_cast<unsigned>(cl) + 4u * half * Dv) * 2u;
-    float carry[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) carry[k] = fmaf(qz[k], h_in, cz[k]);
+    const unsigned lane_off = (static_cast<unsigned>(cl) + 16u * half * Dv) * 2u;
+    const float carry[2] = {fmaf(qa, h_in, ca), fmaf(qb, h_in, cb)};
     if (tc.t0 + kFusedRows <= T) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int jj = 0; jj < 16; jj += 2) {
-          const int r = rt * 32 + 8 * (jj >> 2) + (jj & 3);  // row of half 0; half 1: 4 further
-          const float c_ = carry[rt * 4 + (jj >> 2)];
-          uint32_t pk = pack_bf16x2(fmaf(acc[rt][0][jj], c_, acc[rt][1][jj]),
-                                    fmaf(acc[rt][0][jj + 1], c_, acc[rt][1][jj + 1]));
+          uint32_t pk = pack_bf16x2(fmaf(acc[rt][0][jj], carry[rt], acc[rt][1][jj]),
+                                    fmaf(acc[rt][0][jj + 1], carry[rt], acc[rt][1][jj + 1]));
           asm volatile("" : "+v"(pk));  // keep one conversion for the pair
-          char *row0 = const_cast<char *>(yg) + r * Dv * 2u;
+          char *row0 = const_cast<char *>(yg) + (rt * 32 + jj) * Dv * 2u;
           *reinterpret_cast<bf16_t *>(row0 + lane_off) = static_cast<bf16_t>(pk);
           *reinterpret_cast<bf16_t *>(row0 + Dv * 2u + lane_off) = static_cast<bf16_t>(pk >> 16);
         }
@@ -459,10 +469,9 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
-          const int r = rt * 32 + 8 * (jj >> 2) + (jj & 3);
-          const float hv = fmaf(acc[rt][0][jj], carry[rt * 4 + (jj >> 2)], acc[rt][1][jj]);
-          const int t = tc.t0 + r + 4 * half;
-          char *row0 = const_cast<char *>(yg) + r * Dv * 2u;
+          const float hv = fmaf(acc[rt][0][jj], carry[rt], acc[rt][1][jj]);
+          const int t = tc.t0 + rt * 32 + 16 * half + jj;
+          char *row0 = const_cast<char *>(yg) + (rt * 32 + jj) * Dv * 2u;
           if (t < T) *reinterpret_cast<bf16_t *>(row0 + lane_off) = f32_to_bf16(hv);
           if (t == T - 1 && h_T) h_T[static_cast<size_t>(tc.b) * D + d] = hv;
         }
