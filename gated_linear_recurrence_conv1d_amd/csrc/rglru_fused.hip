@@ -192,21 +192,32 @@ __device__ __forceinline__ void halves(float v, float &lo, float &hi) {
   hi = __uint_as_float(r[1]);
 }
 
-// One element of the gate math and of its run's scan. From the accumulators (pa, px):
-// r = sigmoid(pa) with exp2(-log2(e) (pa + b_a)) (ba2 = -log2(e) b_a folded into one FMA);
-// e = expm1(log a) = expm1(kd r) as the polynomial of kd r 2^-nh followed by nh exact doublings
-// e <- e (e + 2) (nh is wave-uniform, 0 unless the wave holds a channel with a^c < e^-1/4);
-// a = 1 + e, m = sqrt(1 - a^2) = sqrt(-e (2 + e)), i = sigmoid(px), u = m i x. Then the run's
-// product and state advance, P <- P a, S <- a S + u (from P = 1, S = 0 at the run's start); the
-// caller overwrites the accumulators with (P, S).
-__device__ __forceinline__ void gate_step(float pa, float px, float xv, float kds, int nh,
-                                          float ba2, float bx2, float &P, float &S, bool first) {
+// The gate math of one element in two steps, with the wave-uniform expm1 doubling (below)
+// between them for the whole run (a branch per element would split every step into its own
+// block and keep the scheduler from overlapping neighbouring elements).
+// Step (a): r = sigmoid(pa) with exp2(-log2(e) (pa + b_a)) (ba2 = -log2(e) b_a folded into one
+// FMA), then e' = expm1(kd r 2^-nh) by the polynomial.
+__device__ __forceinline__ float gate_a(float pa, float kds, float ba2) {
   const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(fmaf(pa, -kLog2e, ba2)));
-  float e = expm1_poly(kds * r);
+  return expm1_poly(kds * r);
+}
+// e = expm1(log a) from e' by nh exact doublings e <- e (e + 2) (nh is wave-uniform, 0 unless the
+// wave holds a channel with a^c < e^-1/4), over n accumulators of one run.
+__device__ __forceinline__ void gate_double(f32x16_t &e, int lo, int n, int nh) {
   if (nh > 0) {
-    for (int i = 0; i < nh; ++i) e *= e + 2.0f;
-    e = fmaxf(e, -1.0f);  // a = exp(log a) >= 0: clamp what rounding may leave below -1
+    for (int i = 0; i < nh; ++i)
+#pragma unroll
+      for (int jj = lo; jj < lo + n; ++jj) e[jj] *= e[jj] + 2.0f;
+    // a = exp(log a) >= 0: clamp what rounding may leave below -1
+#pragma unroll
+    for (int jj = lo; jj < lo + n; ++jj) e[jj] = fmaxf(e[jj], -1.0f);
   }
+}
+// Step (b): a = 1 + e, m = sqrt(1 - a^2) = sqrt(-e (2 + e)), i = sigmoid(px), u = m i x; then the
+// run's product and state advance, P <- P a, S <- a S + u (from P = 1, S = 0 at the run's start);
+// the caller overwrites the accumulators with (P, S).
+__device__ __forceinline__ void gate_b(float e, float px, float xv, float bx2, float &P, float &S,
+                                       bool first) {
   const float a = 1.0f + e;
   const float m = __builtin_amdgcn_sqrtf(-e * (2.0f + e));
   const float ig =
@@ -333,10 +344,11 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
     const float *xfl = xf + 16 * half * F::kLdx + cl;
     float Ar[2], Ur[2];
     {
-      // one step of row tile 0 per k-step of row tile 1 (Dh < 256: the MFMAs end early); each
-      // step's x is read one step ahead
+      // Row tile 1's k-steps carry row tile 0's gate math: step (a) of two elements per k-step
+      // over the first half, the doublings, then step (b) and the scan of two elements per
+      // k-step (Dh < 256: the MFMAs end early); x is read one k-step ahead.
       float P = 1.0f, S = 0.0f;
-      float xn = xfl[0];
+      float xn0 = xfl[0], xn1 = xfl[F::kLdx];
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) {
         if (ks < F::kKS) {
@@ -344,22 +356,41 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
           acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wa[ks], acc[1][0], 0, 0, 0);
           acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wx[ks], acc[1][1], 0, 0, 0);
         }
-        const float xv = xn;
-        if (ks + 1 < 16) xn = xfl[(ks + 1) * F::kLdx];
-        gate_step(acc[0][0][ks], acc[0][1][ks], xv, kds, nh, ba2, bx2, P, S, ks == 0);
-        acc[0][0][ks] = P;
-        acc[0][1][ks] = S;
+        if (ks < 8) {
+          acc[0][0][2 * ks] = gate_a(acc[0][0][2 * ks], kds, ba2);
+          acc[0][0][2 * ks + 1] = gate_a(acc[0][0][2 * ks + 1], kds, ba2);
+        } else {
+          const int jj = 2 * (ks - 8);
+          if (ks == 8) gate_double(acc[0][0], 0, 16, nh);
+          const float xv0 = xn0, xv1 = xn1;
+          if (jj + 2 < 16) {
+            xn0 = xfl[(jj + 2) * F::kLdx];
+            xn1 = xfl[(jj + 3) * F::kLdx];
+          }
+          gate_b(acc[0][0][jj], acc[0][1][jj], xv0, bx2, P, S, jj == 0);
+          acc[0][0][jj] = P;
+          acc[0][1][jj] = S;
+          gate_b(acc[0][0][jj + 1], acc[0][1][jj + 1], xv1, bx2, P, S, false);
+          acc[0][0][jj + 1] = P;
+          acc[0][1][jj + 1] = S;
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       Ar[0] = P;
       Ur[0] = S;
     }
     {
+      // row tile 1: step (a), the doublings, step (b) and the scan
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        acc[1][0][jj] = gate_a(acc[1][0][jj], kds, ba2);
+        if ((jj & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+      gate_double(acc[1][0], 0, 16, nh);
       float P = 1.0f, S = 0.0f;
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
-        gate_step(acc[1][0][jj], acc[1][1][jj], xfl[(32 + jj) * F::kLdx], kds, nh, ba2, bx2, P,
-                  S, jj == 0);
+        gate_b(acc[1][0][jj], acc[1][1][jj], xfl[(32 + jj) * F::kLdx], bx2, P, S, jj == 0);
         acc[1][0][jj] = P;
         acc[1][1][jj] = S;
         if ((jj & 3) == 3) __builtin_amdgcn_sched_barrier(0);
