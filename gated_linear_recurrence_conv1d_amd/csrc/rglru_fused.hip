@@ -100,7 +100,10 @@ struct TileCtx {
 
 // Stage the x rows t0-3 .. t0+63 of one (sequence, head) tile -- the tile plus the conv halo --
 // into LDS with direct buffer-to-LDS loads (16 bytes per lane, one contiguous 1 KB block per
-// load), spread over the waves. The buffer covers exactly sequence b, so its range check returns
+// load), spread over the waves. They go through dma_16b, which the compiler does not track (for
+// the builtin it cannot tell which LDS bytes the loads write, and would make the first LDS read
+// after them -- the gate math's -- wait for all of them); the kernel waits for them itself
+// (vmcnt) before the barrier that hands the rows to the conv. The buffer covers exactly sequence b, so its range check returns
 // zeros for rows before t = 0 (the causal zero padding; negative offsets wrap past the end) and
 // for rows past T-1 (which only feed rows that are not stored).
 template <int DH, int NW>
@@ -116,13 +119,13 @@ __device__ __forceinline__ void stage_x(const bf16_t *__restrict__ x, bf16_t *xr
   unsigned lane_off =
       static_cast<unsigned>((lane / kLanesPerRow) * 2 * D + g * DH * 2 + (lane % kLanesPerRow) * 16);
   asm volatile("" : "+v"(lane_off));
+  const unsigned base = lds_addr(xr);
 #pragma unroll
   for (int k = 0; k < kPerWave; ++k) {
     const int i = w + k * NW;  // wave-uniform
     if (kPerWave * NW == F::kLoads || i < F::kLoads) {
       const unsigned row_off = row_bytes(t0 - 3 + i * F::kRowsPerLoad, D, 2u);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(seq, (lds_void *)(xr + i * F::kRowsPerLoad * DH),
-                                               16, row_off + lane_off, 0, 0, 0);
+      dma_16b(seq, row_off + lane_off, base + i * F::kRowsPerLoad * DH * 2u);
     }
   }
 }
