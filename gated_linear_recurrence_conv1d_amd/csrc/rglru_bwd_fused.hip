@@ -78,12 +78,8 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
   __shared__ __attribute__((aligned(16))) bf16_t xr[2][F::kXRows * DH];  // x rows t0-3 ..
   __shared__ __attribute__((aligned(16))) bf16_t dyr[2][kRows * DH];     // dy rows t0 ..
   __shared__ __attribute__((aligned(16))) bf16_t yr[2][kRows * DH];      // y rows t0-1 ..
-  __shared__ __attribute__((aligned(16))) bf16_t xa[2 * kRows * F::kLda];  // conv hi / lo; then pre
-  __shared__ float2 sc[F::kSeg * DH];      // per (segment, channel): the segment's map (A, U)
-  __shared__ float psum[3 * F::kSeg * DH];  // per (sum, segment, channel): partial sums
-  __shared__ float gin[DH];                // g at the tile's end, per channel
+  __shared__ __attribute__((aligned(16))) bf16_t xa[2 * kRows * F::kLda];  // conv hi / lo
   __shared__ int s_tile[2];
-  uint32_t *const preL = reinterpret_cast<uint32_t *>(xa);  // [32][Dh] fp16 pairs (pa, px)
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -93,8 +89,12 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
   const int g = blockIdx.x % H;
   const int ntiles = B * nTT;
   unsigned *ticket = ctrl + 2 + g;
-  // MFMA role: this lane's output channel, and its W_a / W_x rows (the B operand)
+  // This lane's channel (the MFMA output column) and its W_a / W_x rows (the B operand). The lane
+  // phase works on the accumulators where they are: lane (channel, half) holds tile rows
+  // 16 half .. 16 half + 15 of its channel, because the A operand's rows are fed permuted (lane i
+  // of the A operand supplies tile row 16 ((i / 4) mod 2) + 4 (i / 8) + i mod 4).
   const int cl = w * 32 + lrow;
+  const int prow = 16 * ((lrow >> 2) & 1) + 4 * (lrow >> 3) + (lrow & 3);
   const float ba = b_a[g * DH + cl], bx = b_x[g * DH + cl];
   bf16x8_t wa[F::kKS], wx[F::kKS];
   {
@@ -106,17 +106,14 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
       wx[ks] = load_bf16x8(rx + ks * 16);
     }
   }
-  // conv role: channel pair cp (channels 2cp, 2cp + 1), tile rows cr * 16 .. + 15; lane-phase
-  // role: channel c, rows sg * 32 .. + 31
+  // conv role: channel pair cp (channels 2cp, 2cp + 1), tile rows cr * kCRows ..
   const int cp = tid % F::kPP;
   const int cr = tid / F::kPP;
-  const int c = tid % DH;
-  const int sg = tid / DH;
-  const int dc = g * DH + c;
-  // conv taps as bf16 pairs (w0, w1), (w2, w3): of the channel pair (conv role) and of channel c
+  const int dc = g * DH + cl;
+  // conv taps as bf16 pairs (w0, w1), (w2, w3): of the channel pair (conv role) and of channel cl
   // (selector of its half of each pair: the lane phase reads the pair's staged words)
   bf16x2_t w01l, w23l, w01h, w23h, w01c, w23c;
-  const uint32_t csel = (c & 1) ? kHiPair : kLoPair;
+  const uint32_t csel = (cl & 1) ? kHiPair : kLoPair;
   {
     uint32_t cw[4];
 #pragma unroll
@@ -139,7 +136,7 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
   const bool fast = __builtin_amdgcn_readfirstlane(__any(kd < -0.25f) ? 1 : 0) != 0;
 
   // conv of staged rows q .. q+3 (time t - 3 .. t for tile row q), as pair words: both channels
-  // of the pair, or channel c alone
+  // of the pair, or channel cl alone
   auto conv2 = [&](const uint32_t (&xv)[4], float &o0, float &o1) {
     o0 = __builtin_amdgcn_fdot2_f32_bf16(
         as_bf16x2(__builtin_amdgcn_perm(xv[3], xv[2], kLoPair)), w23l,
@@ -203,9 +200,9 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): own staging loads landed
   }
   // Barriers inside the loop order LDS only (lds_barrier): the staging loads are waited for
-  // explicitly (vmcnt(0) in pass 2, before the next tile's first barrier), and no global memory
-  // is exchanged between the waves, so no barrier needs to wait for the y stores or the staging
-  // loads in flight.
+  // explicitly (vmcnt(0) before pass 2, before the next tile's first barrier), and no global
+  // memory is exchanged between the waves, so no barrier needs to wait for the gradient stores or
+  // the staging loads in flight. After the MFMAs each wave works on its own channels alone.
   int cur = 0;
   for (;;) {
     lds_barrier();  // this tile's rows staged; the previous tile's LDS reads done
@@ -238,39 +235,36 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
       const int jn = __builtin_amdgcn_readfirstlane(s_tile[cur ^ 1]);
       if (jn < ntiles) stage(jn, cur ^ 1);  // its last readers finished before the loop top
     }
-    // ---- [32 x DH] x [DH x 2 DH]: A = hi + lo
+    // ---- [32 x DH] x [DH x 2 DH]: A = hi + lo, rows permuted
     f32x16_t acc[2];  // [gate]
     acc[0] = acc[1] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < F::kKS; ++ks)
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
-        const bf16x8_t af = load_bf16x8(xa + (pt * kRows + lrow) * F::kLda + ks * 16 + half * 8);
+        const bf16x8_t af = load_bf16x8(xa + (pt * kRows + prow) * F::kLda + ks * 16 + half * 8);
         acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wa[ks], acc[0], 0, 0, 0);
         acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wx[ks], acc[1], 0, 0, 0);
       }
-    lds_barrier();  // every wave is done with xa
-    // ---- pre-activations (with the biases) as fp16 pairs over the conv tile: row r, channel cl
-#pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const int r = 8 * (jj >> 2) + 4 * half + (jj & 3);
-      preL[r * DH + cl] = pack_f16x2(acc[0][jj] + ba, acc[1][jj] + bx);
-    }
-    lds_barrier();  // pre ready
-    // ---- lane phase, pass 1: this segment's map g_start = A g_end + U, walking it backward.
-    // Rows at or past T (only in the last tile) are the identity (a = 1, dy = 0).
-    const bf16_t *dyt = dyr[cur] + c;  // row r: dy at t0 + r
-    const bf16_t *yt = yr[cur] + c;    // row r: y at t0 + r - 1 (zero for t0 + r - 1 < 0)
-    const int rlast = sg * F::kSegRows + F::kSegRows - 1;  // the segment's last tile row
+    // ---- pass 1: this half's map g_start = A g_end + U over its 16 rows, walking them backward;
+    // r (in place of its pre-activation) and expm1(log a) kept for pass 2. Rows at or past T
+    // (only in the last tile) are the identity (a = 1, dy = 0).
+    const bf16_t *dyt = dyr[cur] + 16 * half * DH + cl;  // row jj: dy at t0 + 16 half + jj
+    const bf16_t *yt = yr[cur] + 16 * half * DH + cl;    // row jj: y at t0 + 16 half + jj - 1
+    const int tl = t0 + 16 * half;                        // time of this half's row 0
+    float ev[16];
     float A = 1.0f, U = 0.0f;
     auto pass1 = [&](auto nh) {
-#pragma unroll 4
-      for (int row = rlast; row > rlast - F::kSegRows; --row) {
-        const float pa = f16lo(preL[row * DH + c]);
-        const bool in = t0 + row < T;
-        const float z = kd * fast_sigmoid(pa);
-        const float a = in ? 1.0f + (decltype(nh)::value ? expm1_nonpos(z) : expm1_poly(z)) : 1.0f;
-        U = a * ((in ? bf16_to_f32(dyt[row * DH]) : 0.0f) + U);
+#pragma unroll
+      for (int jj = 15; jj >= 0; --jj) {
+        const bool in = tl + jj < T;
+        const float rr = fast_sigmoid(acc[0][jj] + ba);
+        const float z = kd * rr;
+        const float e = in ? (decltype(nh)::value ? expm1_nonpos(z) : expm1_poly(z)) : 0.0f;
+        acc[0][jj] = rr;
+        ev[jj] = e;
+        const float a = 1.0f + e;
+        U = a * ((in ? bf16_to_f32(dyt[jj * DH]) : 0.0f) + U);
         A *= a;
       }
     };
@@ -278,17 +272,15 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
       pass1(std::true_type{});
     else
       pass1(std::false_type{});
-    sc[sg * DH + c] = make_float2(A, U);
-    lds_barrier();  // segment maps ready
     // ---- the tile's map, g at its end from the next tile in time, g at its start published
-    if (sg == 0) {
-      float At = 1.0f, Ut = 0.0f;
-#pragma unroll
-      for (int s = F::kSeg - 1; s >= 0; --s) {
-        const float2 m = sc[s * DH + c];
-        Ut = fmaf(m.x, Ut, m.y);
-        At *= m.x;
-      }
+    // (half 0's lanes; g_start = A0 (A1 g_end + U1) + U0)
+    float A0, A1, U0, U1;
+    halves(A, A0, A1);
+    halves(U, U0, U1);
+    float gend = 0.0f;
+    if (half == 0) {
+      const float At = A1 * A0;
+      const float Ut = fmaf(A0, U1, U0);
       // tile tt's words of this channel: agg (its map) and incl (g at its start), word k at
       // bd + k B D
       const size_t bd = static_cast<size_t>(b) * D + dc;
@@ -299,7 +291,6 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
       // out (a map never waits for anything), then apply the maps in between in the fold's own
       // order: every incl word is an intermediate value of that one fold, so the result does not
       // depend on which words happened to be out (bitwise the same from run to run).
-      float gend = 0.0f;
       int k = tt + 1;
       unsigned long long vi = kEmpty;
       unsigned spins = 0;
@@ -333,48 +324,44 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
         st_relaxed(incl + bd + static_cast<size_t>(tt) * tstride, pack2(gstart, 0.0f));
       else if (dh0)
         dh0[bd] = gstart;
-      gin[c] = gend;
     }
-    lds_barrier();  // g at the tile's end ready
-    // ---- pass 2: from g at this segment's end, backward over its rows: gradients and sums
-    float gk = gin[c];
-    for (int s = F::kSeg - 1; s > sg; --s) {
-      const float2 m = sc[s * DH + c];
-      gk = fmaf(m.x, gk, m.y);
+    {
+      float glo, ghi;
+      halves(gend, glo, ghi);
+      gend = glo;
     }
+    // ---- pass 2: from g at this half's end, backward over its rows: gradients and sums
+    float gk = half ? gend : fmaf(A1, gend, U1);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile's staged rows landed
     float s_pa = 0.0f, s_px = 0.0f, s_rdz = 0.0f;
     // staged pair words of rows row .. row+3 (time t-3 .. t), slid down one row per step; start
-    // with the rows above the segment's last row
-    const bf16_t *xsc = xs + (c & ~1);
+    // with the rows above this half's last row
+    const bf16_t *xsc = xs + 16 * half * DH + (cl & ~1);
     uint32_t xv[4];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) xv[k] = *reinterpret_cast<const uint32_t *>(xsc + (rlast + 1 + k) * DH);
+    for (int k = 0; k < 3; ++k) xv[k] = *reinterpret_cast<const uint32_t *>(xsc + (16 + k) * DH);
     xv[3] = 0u;
-    // the element (t0 + rlast, dc) of dpre / dxc; one row (D elements) back per step
-    const size_t o0 = (static_cast<size_t>(b) * T + t0 + rlast) * D + dc;
     const float hinit = h0 ? h0[static_cast<size_t>(b) * D + dc] : 0.0f;
+    // element (t0 + 16 half + jj, dc) of dpre / dxc: a wave-uniform row base plus a lane offset
+    const size_t rbase = (static_cast<size_t>(b) * T + t0) * D;
+    const unsigned loff = static_cast<unsigned>(16 * half * D + dc);
     auto pass2 = [&](auto nh) {
-      uint32_t *dpo = dpre + o0;
-      uint16_t *dxo = dxc + o0;
-#pragma unroll 4
-      for (int row = rlast; row > rlast - F::kSegRows; --row) {
-        const int t = t0 + row;
+#pragma unroll
+      for (int jj = 15; jj >= 0; --jj) {
+        const int t = tl + jj;
         xv[3] = xv[2];
         xv[2] = xv[1];
         xv[1] = xv[0];
-        xv[0] = *reinterpret_cast<const uint32_t *>(xsc + row * DH);
+        xv[0] = *reinterpret_cast<const uint32_t *>(xsc + jj * DH);
         if (t < T) {
-          const uint32_t pp = preL[row * DH + c];
           const float xc = conv1(xv);
-          const float rr = fast_sigmoid(f16lo(pp));
-          const float ig = fast_sigmoid(f16hi(pp));
-          const float z = kd * rr;
-          const float e = decltype(nh)::value ? expm1_nonpos(z) : expm1_poly(z);
+          const float rr = acc[0][jj];
+          const float ig = fast_sigmoid(acc[1][jj] + bx);
+          const float e = ev[jj];
           const float a = 1.0f + e;
           const float m = __builtin_amdgcn_sqrtf(-e * (2.0f + e));
-          const float delta = bf16_to_f32(dyt[row * DH]) + gk;
-          const float hp = t > 0 ? bf16_to_f32(yt[row * DH]) : hinit;
+          const float delta = bf16_to_f32(dyt[jj * DH]) + gk;
+          const float hp = t > 0 ? bf16_to_f32(yt[jj * DH]) : hinit;
           const float dx_ = delta * xc, dmg = delta * m;
           const float dm = dx_ * ig;
           const float di = dmg * xc;
@@ -386,30 +373,31 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
           s_px += dpx;
           s_rdz = fmaf(rr, dz, s_rdz);
           gk = a * delta;
-          *dpo = pack_f16x2(dpa, dpx);
-          *dxo = static_cast<uint16_t>(pack_f16x2(dmg * ig, 0.0f));  // fp16
+          const size_t ro = rbase + static_cast<size_t>(jj) * D;
+          dpre[ro + loff] = pack_f16x2(dpa, dpx);
+          dxc[ro + loff] = static_cast<uint16_t>(pack_f16x2(dmg * ig, 0.0f));  // fp16
         }
-        dpo -= D;
-        dxo -= D;
       }
     };
     if (fast)
       pass2(std::true_type{});
     else
       pass2(std::false_type{});
-    psum[(0 * F::kSeg + sg) * DH + c] = s_pa;
-    psum[(1 * F::kSeg + sg) * DH + c] = s_px;
-    psum[(2 * F::kSeg + sg) * DH + c] = s_rdz;
-    lds_barrier();  // partial sums ready
-    if (sg == 0) {
+    // ---- the tile's partial sums (half 0 + half 1), written by half 0
+    {
       const size_t PD = static_cast<size_t>(B) * nTT * D;
       const size_t pidx = (static_cast<size_t>(b) * nTT + tt) * D + dc;
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        float sum = 0.0f;
-#pragma unroll
-        for (int s = 0; s < F::kSeg; ++s) sum += psum[(q * F::kSeg + s) * DH + c];
-        part[q * PD + pidx] = sum;
+      float lo, hi;
+      halves(s_pa, lo, hi);
+      const float q0 = lo + hi;
+      halves(s_px, lo, hi);
+      const float q1 = lo + hi;
+      halves(s_rdz, lo, hi);
+      const float q2 = lo + hi;
+      if (half == 0) {
+        part[pidx] = q0;
+        part[PD + pidx] = q1;
+        part[2 * PD + pidx] = q2;
       }
     }
     cur ^= 1;

@@ -189,6 +189,16 @@ __device__ __forceinline__ unsigned lds_addr(const void *p) {
   return __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>(p)));
 }
 
+// Both halves' values of v in every lane: lo from lane (l & 31), hi from lane (l | 32).
+// v_permlane32_swap exchanges lanes 32..63 of its first operand with lanes 0..31 of its second;
+// with both operands holding v, the first then holds the low half twice and the second the high.
+__device__ __forceinline__ void halves(float v, float &lo, float &hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
 // Workgroup barrier that orders LDS accesses only: unlike __syncthreads it does not wait for the
 // wave's outstanding vector memory loads and stores, so they stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {

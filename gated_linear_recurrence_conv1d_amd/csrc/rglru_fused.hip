@@ -185,16 +185,6 @@ __device__ __forceinline__ void conv_prologue(const bf16_t *xr, bf16_t *xa, floa
   }
 }
 
-// Both halves' values of v in every lane: lo from lane (l & 31), hi from lane (l | 32).
-// v_permlane32_swap exchanges lanes 32..63 of its first operand with lanes 0..31 of its second;
-// with both operands holding v, the first then holds the low half twice and the second the high.
-__device__ __forceinline__ void halves(float v, float &lo, float &hi) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  lo = __uint_as_float(r[0]);
-  hi = __uint_as_float(r[1]);
-}
-
 // The gate math of one element in two steps, with the wave-uniform expm1 doubling (below)
 // between them for the whole run (a branch per element would split every step into its own
 // block and keep the scheduler from overlapping neighbouring elements).
