@@ -248,7 +248,8 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
       }
     // ---- pass 1: this half's map g_start = A g_end + U over its 16 rows, walking them backward;
     // r (in place of its pre-activation) and expm1(log a) kept for pass 2. Rows at or past T
-    // (only in the last tile) are the identity (a = 1, dy = 0).
+    // (only in the last tile) are the identity: a = 1, and dy there is 0 (the staging loads' range
+    // check). Every load is unconditional, so the 16 rows are one block for the scheduler.
     const bf16_t *dyt = dyr[cur] + 16 * half * DH + cl;  // row jj: dy at t0 + 16 half + jj
     const bf16_t *yt = yr[cur] + 16 * half * DH + cl;    // row jj: y at t0 + 16 half + jj - 1
     const int tl = t0 + 16 * half;                        // time of this half's row 0
@@ -257,14 +258,15 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     auto pass1 = [&](auto nh) {
 #pragma unroll
       for (int jj = 15; jj >= 0; --jj) {
-        const bool in = tl + jj < T;
+        const float dyv = bf16_to_f32(dyt[jj * DH]);
         const float rr = fast_sigmoid(acc[0][jj] + ba);
         const float z = kd * rr;
-        const float e = in ? (decltype(nh)::value ? expm1_nonpos(z) : expm1_poly(z)) : 0.0f;
+        const float ez = decltype(nh)::value ? expm1_nonpos(z) : expm1_poly(z);
+        const float e = tl + jj < T ? ez : 0.0f;
         acc[0][jj] = rr;
         ev[jj] = e;
         const float a = 1.0f + e;
-        U = a * ((in ? bf16_to_f32(dyt[jj * DH]) : 0.0f) + U);
+        U = a * (dyv + U);
         A *= a;
       }
     };
@@ -342,47 +344,65 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     for (int k = 0; k < 3; ++k) xv[k] = *reinterpret_cast<const uint32_t *>(xsc + (16 + k) * DH);
     xv[3] = 0u;
     const float hinit = h0 ? h0[static_cast<size_t>(b) * D + dc] : 0.0f;
-    // element (t0 + 16 half + jj, dc) of dpre / dxc: a wave-uniform row base plus a lane offset
-    const size_t rbase = (static_cast<size_t>(b) * T + t0) * D;
-    const unsigned loff = static_cast<unsigned>(16 * half * D + dc);
-    auto pass2 = [&](auto nh) {
+    // dpre / dxc of sequence b as buffers: element (t0 + 16 half + jj, dc) at a wave-uniform row
+    // offset (soffset) plus this lane's fixed offset. In the last tile of a sequence whose length
+    // is not a multiple of the tile, rows at or past T get a lane offset past the buffer's end,
+    // which the range check drops, and add nothing to the sums.
+    const size_t sb = static_cast<size_t>(b) * T * D;
+    const __amdgpu_buffer_rsrc_t rdp = __builtin_amdgcn_make_buffer_rsrc(
+        dpre + sb, static_cast<short>(0), rec_bytes(T, D, 4u), kRawWord3);
+    const __amdgpu_buffer_rsrc_t rdx = __builtin_amdgcn_make_buffer_rsrc(
+        dxc + sb, static_cast<short>(0), rec_bytes(T, D, 2u), kRawWord3);
+    const unsigned le = static_cast<unsigned>(16 * half * D + dc);
+    auto pass2 = [&](auto nh, auto full) {
 #pragma unroll
       for (int jj = 15; jj >= 0; --jj) {
         const int t = tl + jj;
+        const bool in = decltype(full)::value || t < T;
         xv[3] = xv[2];
         xv[2] = xv[1];
         xv[1] = xv[0];
         xv[0] = *reinterpret_cast<const uint32_t *>(xsc + jj * DH);
-        if (t < T) {
-          const float xc = conv1(xv);
-          const float rr = acc[0][jj];
-          const float ig = fast_sigmoid(acc[1][jj] + bx);
-          const float e = ev[jj];
-          const float a = 1.0f + e;
-          const float m = __builtin_amdgcn_sqrtf(-e * (2.0f + e));
-          const float delta = bf16_to_f32(dyt[jj * DH]) + gk;
-          const float hp = t > 0 ? bf16_to_f32(yt[jj * DH]) : hinit;
-          const float dx_ = delta * xc, dmg = delta * m;
-          const float dm = dx_ * ig;
-          const float di = dmg * xc;
-          float dz = delta * hp * a;
-          if (m > 0.0f) dz -= dm * (a * a) * __builtin_amdgcn_rcpf(m);
-          const float dpa = kd * dz * (rr * (1.0f - rr));
-          const float dpx = di * (ig * (1.0f - ig));
-          s_pa += dpa;
-          s_px += dpx;
-          s_rdz = fmaf(rr, dz, s_rdz);
-          gk = a * delta;
-          const size_t ro = rbase + static_cast<size_t>(jj) * D;
-          dpre[ro + loff] = pack_f16x2(dpa, dpx);
-          dxc[ro + loff] = static_cast<uint16_t>(pack_f16x2(dmg * ig, 0.0f));  // fp16
-        }
+        const float dyv = bf16_to_f32(dyt[jj * DH]);
+        const float yv = bf16_to_f32(yt[jj * DH]);
+        const float xc = conv1(xv);
+        const float rr = acc[0][jj];
+        const float ig = fast_sigmoid(acc[1][jj] + bx);
+        const float e = ev[jj];
+        const float a = 1.0f + e;
+        const float m = __builtin_amdgcn_sqrtf(-e * (2.0f + e));
+        const float delta = dyv + gk;
+        const float hp = t > 0 ? yv : hinit;
+        const float dx_ = delta * xc, dmg = delta * m;
+        const float dm = dx_ * ig;
+        const float di = dmg * xc;
+        float dz = delta * hp * a;
+        if (m > 0.0f) dz -= dm * (a * a) * __builtin_amdgcn_rcpf(m);
+        const float dpa = kd * dz * (rr * (1.0f - rr));
+        const float dpx = di * (ig * (1.0f - ig));
+        s_pa += in ? dpa : 0.0f;
+        s_px += in ? dpx : 0.0f;
+        s_rdz = in ? fmaf(rr, dz, s_rdz) : s_rdz;
+        gk = a * delta;
+        const int so = static_cast<int>(row_bytes(t0 + jj, D, 1u));
+        __builtin_amdgcn_raw_buffer_store_b32(pack_f16x2(dpa, dpx), rdp,
+                                              static_cast<int>(in ? 4u * le : 0x80000000u), 4 * so, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(
+            static_cast<uint16_t>(pack_f16x2(dmg * ig, 0.0f)), rdx,  // fp16
+            static_cast<int>(in ? 2u * le : 0x80000000u), 2 * so, 0);
       }
     };
-    if (fast)
-      pass2(std::true_type{});
-    else
-      pass2(std::false_type{});
+    if (t0 + kRows <= T) {
+      if (fast)
+        pass2(std::true_type{}, std::true_type{});
+      else
+        pass2(std::false_type{}, std::true_type{});
+    } else {
+      if (fast)
+        pass2(std::true_type{}, std::false_type{});
+      else
+        pass2(std::false_type{}, std::false_type{});
+    }
     // ---- the tile's partial sums (half 0 + half 1), written by half 0
     {
       const size_t PD = static_cast<size_t>(B) * nTT * D;
