@@ -44,6 +44,16 @@ constexpr int kRows = kFusedBwdRows;                               // rows per t
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
 }  // namespace
 
+// p, the same in every lane, read from the first one: its 64-bit offset arithmetic runs on the
+// vector ALU (there is no scalar 64-bit multiply), and a buffer descriptor made from a vector
+// register is handled as divergent, with every access wrapped in a loop over its distinct values.
+template <typename P> __device__ __forceinline__ P *wave_uniform(P *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<P *>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 template <int DH> struct BwdTile {
   static_assert(DH == 128 || DH == 256, "fused backward tile needs Dh in {128, 256}");
   static constexpr int kNW = DH / 32;                // waves, 32 channels each for the MFMA
@@ -110,10 +120,8 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
   const int cp = tid % F::kPP;
   const int cr = tid / F::kPP;
   const int dc = g * DH + cl;
-  // conv taps as bf16 pairs (w0, w1), (w2, w3): of the channel pair (conv role) and of channel cl
-  // (selector of its half of each pair: the lane phase reads the pair's staged words)
-  bf16x2_t w01l, w23l, w01h, w23h, w01c, w23c;
-  const uint32_t csel = (cl & 1) ? kHiPair : kLoPair;
+  // conv taps of the channel pair (conv role) as bf16 pairs (w0, w1), (w2, w3)
+  bf16x2_t w01l, w23l, w01h, w23h;
   {
     uint32_t cw[4];
 #pragma unroll
@@ -123,11 +131,6 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     w23l = as_bf16x2(__builtin_amdgcn_perm(cw[3], cw[2], kLoPair));
     w01h = as_bf16x2(__builtin_amdgcn_perm(cw[1], cw[0], kHiPair));
     w23h = as_bf16x2(__builtin_amdgcn_perm(cw[3], cw[2], kHiPair));
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      cw[k] = *reinterpret_cast<const uint32_t *>(conv_w + static_cast<size_t>(k) * D + (dc & ~1));
-    w01c = as_bf16x2(__builtin_amdgcn_perm(cw[1], cw[0], csel));
-    w23c = as_bf16x2(__builtin_amdgcn_perm(cw[3], cw[2], csel));
   }
   const float kd = decay_coeff(Lambda[dc]);
   // expm1(log a) takes the polynomial alone unless some channel of the wave has a decay below
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
   const bool fast = __builtin_amdgcn_readfirstlane(__any(kd < -0.25f) ? 1 : 0) != 0;
 
   // conv of staged rows q .. q+3 (time t - 3 .. t for tile row q), as pair words: both channels
-  // of the pair, or channel cl alone
+  // of the pair
   auto conv2 = [&](const uint32_t (&xv)[4], float &o0, float &o1) {
     o0 = __builtin_amdgcn_fdot2_f32_bf16(
         as_bf16x2(__builtin_amdgcn_perm(xv[3], xv[2], kLoPair)), w23l,
@@ -149,14 +152,6 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
                                         0.0f, false),
         false);
   };
-  auto conv1 = [&](const uint32_t (&xv)[4]) {
-    return __builtin_amdgcn_fdot2_f32_bf16(
-        as_bf16x2(__builtin_amdgcn_perm(xv[3], xv[2], csel)), w23c,
-        __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(__builtin_amdgcn_perm(xv[1], xv[0], csel)), w01c,
-                                        0.0f, false),
-        false);
-  };
-
   // staging of tile j into buffer bf: x rows t0-3 .. t0+31 (+ a few unused), dy rows t0 ..
   // t0+31 and y rows t0-1 .. t0+30, spread over the waves. Each buffer covers exactly sequence
   // b, so its range check returns zeros before t = 0 (negative offsets wrap past the end) and
@@ -215,6 +210,16 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     if (tid == 0) claim = atomicAdd(ticket, 1u);
     const int b = j % B, tt = nTT - 1 - j / B, t0 = tt * kRows;
     const bf16_t *xs = xr[cur];
+    // The lane's roles again, from a thread index opaque to the compiler: otherwise it hoists
+    // every per-lane address made from them (LDS rows, look-back words, h0, dh_T) out of the
+    // loop and holds them in registers for the whole kernel, which does not fit next to the
+    // resident weights. Rebuilding them costs a few instructions per tile.
+    int tid_o = tid;
+    asm volatile("" : "+v"(tid_o));
+    const int lane = tid_o & 63, lrow = lane & 31, half = lane >> 5;
+    const int cl = w * 32 + lrow, dc = g * DH + cl;
+    const int cp = tid_o % F::kPP, cr = tid_o / F::kPP;
+    const int prow = 16 * ((lrow >> 2) & 1) + 4 * (lrow >> 3) + (lrow & 3);
     // ---- conv -> hi / lo bf16
 #pragma unroll 4
     for (int r = 0; r < F::kCRows; ++r) {
@@ -236,16 +241,29 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
       if (jn < ntiles) stage(jn, cur ^ 1);  // its last readers finished before the loop top
     }
     // ---- [32 x DH] x [DH x 2 DH]: A = hi + lo, rows permuted
+    // (A operands loaded one k-step ahead, one k-step per scheduling region: the weights take
+    // half the registers, so the loads must not all be in flight at once)
     f32x16_t acc[2];  // [gate]
     acc[0] = acc[1] = f32x16_t{};
+    {
+      const bf16_t *ap = xa + prow * F::kLda + half * 8;
+      bf16x8_t af[2][2];  // [ks & 1][pt]
+      af[0][0] = load_bf16x8(ap);
+      af[0][1] = load_bf16x8(ap + kRows * F::kLda);
 #pragma unroll
-    for (int ks = 0; ks < F::kKS; ++ks)
+      for (int ks = 0; ks < F::kKS; ++ks) {
+        if (ks + 1 < F::kKS) {
+          af[(ks + 1) & 1][0] = load_bf16x8(ap + (ks + 1) * 16);
+          af[(ks + 1) & 1][1] = load_bf16x8(ap + kRows * F::kLda + (ks + 1) * 16);
+        }
 #pragma unroll
-      for (int pt = 0; pt < 2; ++pt) {
-        const bf16x8_t af = load_bf16x8(xa + (pt * kRows + prow) * F::kLda + ks * 16 + half * 8);
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wa[ks], acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wx[ks], acc[1], 0, 0, 0);
+        for (int pt = 0; pt < 2; ++pt) {
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][pt], wa[ks], acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][pt], wx[ks], acc[1], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
     // ---- pass 1: this half's map g_start = A g_end + U over its 16 rows, walking them backward;
     // r (in place of its pre-activation) and expm1(log a) kept for pass 2. Rows at or past T
     // (only in the last tile) are the identity: a = 1, and dy there is 0 (the staging loads' range
@@ -256,9 +274,13 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     float ev[16];
     float A = 1.0f, U = 0.0f;
     auto pass1 = [&](auto nh) {
+      bf16_t dq[2];  // dy two rows ahead; each row fenced off for the scheduler
+      dq[1] = dyt[15 * DH];
+      dq[0] = dyt[14 * DH];
 #pragma unroll
       for (int jj = 15; jj >= 0; --jj) {
-        const float dyv = bf16_to_f32(dyt[jj * DH]);
+        const float dyv = bf16_to_f32(dq[jj & 1]);
+        if (jj >= 2) dq[jj & 1] = dyt[(jj - 2) * DH];
         const float rr = fast_sigmoid(acc[0][jj] + ba);
         const float z = kd * rr;
         const float ez = decltype(nh)::value ? expm1_nonpos(z) : expm1_poly(z);
@@ -268,6 +290,7 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
         const float a = 1.0f + e;
         U = a * (dyv + U);
         A *= a;
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     if (fast)
@@ -336,13 +359,9 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     float gk = half ? gend : fmaf(A1, gend, U1);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile's staged rows landed
     float s_pa = 0.0f, s_px = 0.0f, s_rdz = 0.0f;
-    // staged pair words of rows row .. row+3 (time t-3 .. t), slid down one row per step; start
-    // with the rows above this half's last row
-    const bf16_t *xsc = xs + 16 * half * DH + (cl & ~1);
-    uint32_t xv[4];
-#pragma unroll
-    for (int k = 0; k < 3; ++k) xv[k] = *reinterpret_cast<const uint32_t *>(xsc + (16 + k) * DH);
-    xv[3] = 0u;
+    // x~ of row jj is hi + lo of the conv tile (still intact: nothing writes it before the next
+    // tile's conv)
+    const bf16_t *xh = xa + (16 * half) * F::kLda + cl;
     const float hinit = h0 ? h0[static_cast<size_t>(b) * D + dc] : 0.0f;
     // dpre / dxc of sequence b as buffers: element (t0 + 16 half + jj, dc) at a wave-uniform row
     // offset (soffset) plus this lane's fixed offset. In the last tile of a sequence whose length
@@ -350,22 +369,31 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     // which the range check drops, and add nothing to the sums.
     const size_t sb = static_cast<size_t>(b) * T * D;
     const __amdgpu_buffer_rsrc_t rdp = __builtin_amdgcn_make_buffer_rsrc(
-        dpre + sb, static_cast<short>(0), rec_bytes(T, D, 4u), kRawWord3);
+        wave_uniform(dpre + sb), static_cast<short>(0), rec_bytes(T, D, 4u), kRawWord3);
     const __amdgpu_buffer_rsrc_t rdx = __builtin_amdgcn_make_buffer_rsrc(
-        dxc + sb, static_cast<short>(0), rec_bytes(T, D, 2u), kRawWord3);
+        wave_uniform(dxc + sb), static_cast<short>(0), rec_bytes(T, D, 2u), kRawWord3);
     const unsigned le = static_cast<unsigned>(16 * half * D + dc);
     auto pass2 = [&](auto nh, auto full) {
+      // The LDS values of row jj (x~ hi and lo, dy, y) are loaded two rows ahead, and each row
+      // is fenced off for the scheduler: left free it interleaves many rows and runs out of
+      // registers.
+      bf16_t hq[2], lq[2], dq[2], yq[2];
+      auto fetch = [&](int jj) {
+        hq[jj & 1] = xh[jj * F::kLda];
+        lq[jj & 1] = xh[(kRows + jj) * F::kLda];
+        dq[jj & 1] = dyt[jj * DH];
+        yq[jj & 1] = yt[jj * DH];
+      };
+      fetch(15);
+      fetch(14);
 #pragma unroll
       for (int jj = 15; jj >= 0; --jj) {
         const int t = tl + jj;
         const bool in = decltype(full)::value || t < T;
-        xv[3] = xv[2];
-        xv[2] = xv[1];
-        xv[1] = xv[0];
-        xv[0] = *reinterpret_cast<const uint32_t *>(xsc + jj * DH);
-        const float dyv = bf16_to_f32(dyt[jj * DH]);
-        const float yv = bf16_to_f32(yt[jj * DH]);
-        const float xc = conv1(xv);
+        const float xc = bf16_to_f32(hq[jj & 1]) + bf16_to_f32(lq[jj & 1]);
+        const float dyv = bf16_to_f32(dq[jj & 1]);
+        const float yv = bf16_to_f32(yq[jj & 1]);
+        if (jj >= 2) fetch(jj - 2);
         const float rr = acc[0][jj];
         const float ig = fast_sigmoid(acc[1][jj] + bx);
         const float e = ev[jj];
@@ -377,7 +405,8 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
         const float dm = dx_ * ig;
         const float di = dmg * xc;
         float dz = delta * hp * a;
-        if (m > 0.0f) dz -= dm * (a * a) * __builtin_amdgcn_rcpf(m);
+        const float dr = dm * (a * a) * __builtin_amdgcn_rcpf(m);  // selected, not branched on
+        dz -= m > 0.0f ? dr : 0.0f;
         const float dpa = kd * dz * (rr * (1.0f - rr));
         const float dpx = di * (ig * (1.0f - ig));
         s_pa += in ? dpa : 0.0f;
@@ -390,6 +419,7 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
         __builtin_amdgcn_raw_buffer_store_b16(
             static_cast<uint16_t>(pack_f16x2(dmg * ig, 0.0f)), rdx,  // fp16
             static_cast<int>(in ? 2u * le : 0x80000000u), 2 * so, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     if (t0 + kRows <= T) {
