@@ -1166,7 +1166,10 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
   const size_t PD = static_cast<size_t>(Pp) * D;
   const size_t nW = static_cast<size_t>(H) * Dh * Dh;
   ColSums cs;
-  const int GP = 4, GS = 4;  // (16 interleaved sums for the 256-partial vectors measured slower)
+  // 16 interleaved sums for the per-tile and per-chunk vectors (hundreds of partials over a few
+  // thousand columns: with 4, their few blocks' serial load chains set the kernel's time; 32
+  // and 64 measured slower again), 4 for the dW splits (about a dozen partials)
+  const int GP = 16, GS = 4;
   cs.seg[0] = ColSum{part, static_cast<size_t>(D), static_cast<size_t>(D), Pp, GP, db_a, nullptr};
   cs.seg[1] = ColSum{part + PD, static_cast<size_t>(D), static_cast<size_t>(D), Pp, GP, db_x,
                      nullptr};
