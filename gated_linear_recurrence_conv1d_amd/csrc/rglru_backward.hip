@@ -957,6 +957,9 @@ __global__ __launch_bounds__(256) void dw_valu(const T *__restrict__ x,
 // pairwise in a fixed tree -- a fixed order, so the result does not depend on scheduling. G is
 // 16 for segments with many partials (the per-chunk vectors), 4 otherwise. With `lambda` set,
 // out[j] is scaled by 8 sigmoid(-L_j) (dLambda from the sums of r dz).
+// Segments with few partials over many columns (the dW splits) take G = 0 instead: each thread
+// sums four adjacent columns (16-byte loads and store) over p = 0, 1, .. in order, with no tree
+// (n, ld and both pointers then multiples of 4 floats; the host checks).
 struct ColSum {
   const float *in;
   size_t ld, n;
@@ -972,6 +975,21 @@ struct ColSums {
 __global__ __launch_bounds__(256) void colsum(ColSums segs) {
   __shared__ float red[256];
   const ColSum &sg = segs.seg[blockIdx.y];
+  if (sg.G == 0) {
+    const size_t j4 = (static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (j4 >= sg.n) return;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 4
+    for (int p = 0; p < sg.P; ++p) {
+      const float4 v = *reinterpret_cast<const float4 *>(sg.in + static_cast<size_t>(p) * sg.ld + j4);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    *reinterpret_cast<float4 *>(sg.out + j4) = acc;
+    return;
+  }
   const int G = sg.G, C = 256 / G;
   const int c = threadIdx.x % C, q = threadIdx.x / C;
   const size_t j = static_cast<size_t>(blockIdx.x) * C + c;
@@ -1168,7 +1186,8 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
   ColSums cs;
   // 16 interleaved sums for the per-tile and per-chunk vectors (hundreds of partials over a few
   // thousand columns: with 4, their few blocks' serial load chains set the kernel's time; 32
-  // and 64 measured slower again), 4 for the dW splits (about a dozen partials)
+  // and 64 measured slower again), 4 for the dW splits (about a dozen partials) when they cannot
+  // take the four-column form
   const int GP = 16, GS = 4;
   cs.seg[0] = ColSum{part, static_cast<size_t>(D), static_cast<size_t>(D), Pp, GP, db_a, nullptr};
   cs.seg[1] = ColSum{part + PD, static_cast<size_t>(D), static_cast<size_t>(D), Pp, GP, db_x,
@@ -1177,11 +1196,16 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
                      dLambda, Lambda};
   cs.seg[3] = ColSum{pcw, 4 * static_cast<size_t>(D), 4 * static_cast<size_t>(D), P, GP, dconv_w,
                      nullptr};
-  cs.seg[4] = ColSum{pw, 2 * nW, nW, L.S, GS, dW_a, nullptr};
-  cs.seg[5] = ColSum{pw + nW, 2 * nW, nW, L.S, GS, dW_x, nullptr};
+  // dW: four columns per thread where the layout allows 16-byte accesses
+  auto al16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool v4 = nW % 4 == 0 && al16(pw) && al16(pw + nW) && al16(dW_a) && al16(dW_x);
+  cs.seg[4] = ColSum{pw, 2 * nW, nW, L.S, v4 ? 0 : GS, dW_a, nullptr};
+  cs.seg[5] = ColSum{pw + nW, 2 * nW, nW, L.S, v4 ? 0 : GS, dW_x, nullptr};
   size_t nblk = 0;
-  for (int i = 0; i < kMaxSeg; ++i)
-    nblk = std::max(nblk, (cs.seg[i].n + 256 / cs.seg[i].G - 1) / (256 / cs.seg[i].G));
+  for (int i = 0; i < kMaxSeg; ++i) {
+    const size_t cols = cs.seg[i].G ? 256 / cs.seg[i].G : 1024;  // columns per block
+    nblk = std::max(nblk, (cs.seg[i].n + cols - 1) / cols);
+  }
   colsum<<<dim3(static_cast<unsigned>(nblk), kMaxSeg), 256, 0, s>>>(cs);
   return hipGetLastError();
 }
