@@ -465,8 +465,9 @@ def mqa_leg(torch, rg, warmup=20, reps=50):
     """Local sliding-window multi-query attention (rglru_local_mqa) on the Griffin-2B-shaped
     attention layer: B=8, T=2048, 10 query heads of 256 sharing one key/value head, window 1024,
     bf16, seeded N(0,1) inputs. Roofline: MFMA (bf16 dense peak) against the algorithmic flops
-    4 * B * Hq * dh * (number of visible (query, key) pairs); the kernel issues 1.5x that in MFMA
-    work (the probabilities enter the second contraction as bf16 hi + lo)."""
+    4 * B * Hq * dh * (number of visible (query, key) pairs); the kernel issues up to 1.5x that
+    in MFMA work (the probabilities enter the second contraction as bf16 hi + lo in the query
+    blocks whose rows see fewer than 256 keys, 2 of the 16 here)."""
     from workloads import make_attention_inputs
     B, T, Hq, dh, W = 8, 2048, 10, 256, 1024
     inp = make_attention_inputs(B, T, Hq, dh, seed=0)

@@ -44,16 +44,6 @@ constexpr int kRows = kFusedBwdRows;                               // rows per t
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
 }  // namespace
 
-// p, the same in every lane, read from the first one: its 64-bit offset arithmetic runs on the
-// vector ALU (there is no scalar 64-bit multiply), and a buffer descriptor made from a vector
-// register is handled as divergent, with every access wrapped in a loop over its distinct values.
-template <typename P> __device__ __forceinline__ P *wave_uniform(P *p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-  return reinterpret_cast<P *>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-
 template <int DH> struct BwdTile {
   static_assert(DH == 128 || DH == 256, "fused backward tile needs Dh in {128, 256}");
   static constexpr int kNW = DH / 32;                // waves, 32 channels each for the MFMA

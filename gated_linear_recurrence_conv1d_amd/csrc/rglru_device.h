@@ -199,6 +199,18 @@ __device__ __forceinline__ void halves(float v, float &lo, float &hi) {
   hi = __uint_as_float(r[1]);
 }
 
+// p, the same in every lane, read from the first one, so that the compiler keeps it (and a buffer
+// descriptor made from it) in scalar registers: where it cannot prove a value uniform (64-bit
+// offset arithmetic runs on the vector ALU; values that cross a lambda or a divergent loop), a
+// descriptor in vector registers wraps every access in a loop over its distinct values, and an
+// inline-asm operand that needs scalar registers does not assemble.
+template <typename P> __device__ __forceinline__ P *wave_uniform(P *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<P *>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Workgroup barrier that orders LDS accesses only: unlike __syncthreads it does not wait for the
 // wave's outstanding vector memory loads and stores, so they stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {

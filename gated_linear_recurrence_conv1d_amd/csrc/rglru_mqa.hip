@@ -12,9 +12,10 @@
 // walks the 64-key blocks of the rows' windows. Both contractions put one query row in each lane:
 //   S^T = K Q^T  (A = K rows from LDS, B = the pair's Q rows, in registers for the kernel's life),
 //   O^T += V^T P^T (A = V^T from LDS, B = P),
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulators (P as bf16 hi + lo). The two waves of a pair
-// split each block's keys for S and the softmax (32 keys each) and split dh for O (DH/2 columns
-// each): per block they exchange the rows' maxima and then their P through LDS, so each wave
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulators (P as bf16 hi + lo where rows see few keys).
+// The two waves of a pair split each block's keys for S and the softmax (32 keys each) and split
+// dh for O (DH/2 columns each): per block they exchange the rows' maxima and then their P through
+// LDS, so each wave
 // holds half of O and does half of the softmax, fits in 256 registers, and two waves share each
 // SIMD. The running max m and the rescales are the same in both waves of a pair (same inputs),
 // each keeps the sum l over its own keys, and the two sums are added at the end.
@@ -72,6 +73,8 @@ template <int DH> struct Mqa {
   static constexpr int kLdsBytes = 4 * kKElems * 2 + kXpBytes;
 };
 
+constexpr int kSplitKeys = 256;  // P as hi + lo below this many keys per row (see split)
+
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
@@ -126,6 +129,14 @@ __global__ __launch_bounds__(Mqa<DH>::kThreads, 1) void local_mqa_fwd(
 #pragma unroll
     for (int s = 0; s < M::kKS; ++s) asm volatile("" ::"v"(qf[s]));
   }
+  // P enters P.V as bf16 hi + lo only where some row of the workgroup sees fewer than
+  // kSplitKeys keys (its first row: min(q0 + 1, W) keys). With more keys the rounding of P to
+  // bf16 averages out below the output's rms (an fp64 emulation of B1 T2048 dh256 W1024: worst
+  // element 8.4e-3 of the rms with bf16 P on rows with 256 keys or more, 3.9e-2 with bf16 P on
+  // all rows, 3.9e-3 with hi + lo throughout), and the lo half's MFMAs -- a third of the
+  // kernel's matrix work -- are skipped (a branch on a workgroup-uniform flag: a second copy of
+  // the block loop without them spilled).
+  const bool split = min(q0 + 1, W) < kSplitKeys;
   // keys this workgroup needs: [lo, hi]
   const int lo = max(0, q0 - W + 1);
   const int hi = min(T - 1, q0 + M::kQB - 1);
@@ -245,9 +256,9 @@ __global__ __launch_bounds__(Mqa<DH>::kThreads, 1) void local_mqa_fwd(
   // raised only when a block's max exceeds it by more than 2^8 (in exp2 units) for some row of the
   // wave: the rescale of the O accumulators then happens about once per row instead of every
   // block, and the probabilities stay below 2^8. Numerator and denominator use the same m, so the
-  // result does not change; both waves of the pair take the same decisions. P enters P.V as two
-  // MFMAs (hi, lo) on the same V^T fragment: with P in bf16 alone, rows that attend to few keys
-  // and whose output cancels (|o| well below its terms) lose ~1e-2 of the output's rms.
+  // result does not change; both waves of the pair take the same decisions. With split, P enters
+  // P.V as two MFMAs (hi, lo) on the same V^T fragment: with P in bf16 alone, rows that attend to
+  // few keys and whose output cancels (|o| well below its terms) lose ~1e-2 of the output's rms.
   auto block_softmax = [&](auto with_loads, int kn) {
     constexpr bool kLd = decltype(with_loads)::value;  // block kn's K rows (kn < 0: zeros)
     const float m2 = fmaxf(mx, mx_in[lrow]);
@@ -280,15 +291,19 @@ __global__ __launch_bounds__(Mqa<DH>::kThreads, 1) void local_mqa_fwd(
         const float p0 = sacc[8 * st + 2 * e], p1 = sacc[8 * st + 2 * e + 1];
         const uint32_t hw = pack_bf16x2(p0, p1);
         pown[2 * st][e] = hw;
-        pown[2 * st + 1][e] = pack_bf16x2(p0 - bf16lo(hw), p1 - bf16hi(hw));
+        pown[2 * st + 1][e] = pack_bf16x2(p0 - bf16lo(hw), p1 - bf16hi(hw));  // (unused unless split)
       }
     }
     if (kLd) {
 #pragma unroll
       for (int ii = 0; ii < M::kLPW; ++ii) load_rows(false, ii, kn, kn_buf);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xp_me[i * 64 + lane] = pown[i];
+    xp_me[lane] = pown[0];
+    xp_me[2 * 64 + lane] = pown[2];
+    if (split) {
+      xp_me[64 + lane] = pown[1];
+      xp_me[3 * 64 + lane] = pown[3];
+    }
   };
 
   // ---- O^T += V^T P^T over block kb's 4 steps of 16 keys, my own two (steps 2 side, 2 side + 1)
@@ -316,12 +331,15 @@ __global__ __launch_bounds__(Mqa<DH>::kThreads, 1) void local_mqa_fwd(
       if (kLd && t < M::kLPW) load_rows(false, t, kn, kn_buf);
       const bf16x8_t pfh =
           __builtin_bit_cast(bf16x8_t, t < 2 ? pown[2 * st] : xp_pa[(2 * st) * 64 + lane]);
-      const bf16x8_t pfl =
-          __builtin_bit_cast(bf16x8_t, t < 2 ? pown[2 * st + 1] : xp_pa[(2 * st + 1) * 64 + lane]);
 #pragma unroll
-      for (int j = 0; j < M::kDT; ++j) {
+      for (int j = 0; j < M::kDT; ++j)
         oacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t & 1][j], pfh, oacc[j], 0, 0, 0);
-        oacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t & 1][j], pfl, oacc[j], 0, 0, 0);
+      if (split) {
+        const bf16x8_t pfl = __builtin_bit_cast(
+            bf16x8_t, t < 2 ? pown[2 * st + 1] : xp_pa[(2 * st + 1) * 64 + lane]);
+#pragma unroll
+        for (int j = 0; j < M::kDT; ++j)
+          oacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t & 1][j], pfl, oacc[j], 0, 0, 0);
       }
     }
   };
