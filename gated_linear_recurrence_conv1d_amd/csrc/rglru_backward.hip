@@ -404,19 +404,37 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_emit(
 // wti[g][i][2o + q] = W_q[g][o][i] (q = 0: W_a, 1: W_x) as fp16: the weights transposed and
 // interleaved so that the contraction index k = 2o + q matches the (dpa, dpx) fp16 pair layout of
 // dpre (fp16 holds every bf16 weight of magnitude 2^-14 .. 65504 exactly).
-__global__ void wt_prep(const bf16_t *__restrict__ W_a, const bf16_t *__restrict__ W_x,
-                        uint16_t *__restrict__ wti, int H, int Dh) {
-  const size_t n = static_cast<size_t>(H) * Dh * 2 * Dh;
-  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= n) return;
-  const int k = static_cast<int>(idx % (2 * Dh));
-  const size_t gi = idx / (2 * Dh);
-  const int i = static_cast<int>(gi % Dh);
-  const int g = static_cast<int>(gi / Dh);
-  const int o = k >> 1;
-  const bf16_t *W = (k & 1) ? W_x : W_a;
-  wti[idx] = static_cast<uint16_t>(
-      pack_f16x2(bf16_to_f32(W[(static_cast<size_t>(g) * Dh + o) * Dh + i]), 0.0f));
+// One workgroup per (head, 32 o, 32 i) tile (Dh a multiple of 32): both gates' 32 x 32 blocks
+// read as 16-byte row pieces into LDS (fp16), written out as 16-byte pieces of 32 wti rows.
+__global__ __launch_bounds__(256) void wt_prep(const bf16_t *__restrict__ W_a,
+                                               const bf16_t *__restrict__ W_x,
+                                               uint16_t *__restrict__ wti, int H, int Dh) {
+  __shared__ uint16_t tl[2][32][34];  // [gate][o][i] fp16 (rows padded)
+  const int g = blockIdx.z, o0 = blockIdx.y * 32, i0 = blockIdx.x * 32;
+  const int tid = threadIdx.x;
+  {
+    const int q = tid >> 7, r = (tid >> 2) & 31, c = tid & 3;
+    const bf16_t *W = q ? W_x : W_a;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(
+        W + (static_cast<size_t>(g) * Dh + o0 + r) * Dh + i0 + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t hv = pack_f16x2(bf16lo(v[e]), bf16hi(v[e]));
+      tl[q][r][8 * c + 2 * e] = static_cast<uint16_t>(hv);
+      tl[q][r][8 * c + 2 * e + 1] = static_cast<uint16_t>(hv >> 16);
+    }
+  }
+  __syncthreads();
+  {
+    const int i = tid >> 3, c = tid & 7;  // row i0 + i; k = 2 o0 + 8 c ..: o = 4 c .. 4 c + 3
+    u32x4_t out;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      out[m] = static_cast<uint32_t>(tl[0][4 * c + m][i]) |
+               (static_cast<uint32_t>(tl[1][4 * c + m][i]) << 16);
+    *reinterpret_cast<u32x4_t *>(wti + (static_cast<size_t>(g) * Dh + i0 + i) * 2 * Dh +
+                                 2 * o0 + 8 * c) = out;
+  }
 }
 
 template <int DH>
@@ -1126,8 +1144,7 @@ static hipError_t run_backward(const T *x, const T *conv_w, const T *W_a, const 
   if constexpr (sizeof(T) == 2) {
     if (L.mfma_dxc) {
       uint16_t *wti = reinterpret_cast<uint16_t *>(ws + L.o_wti);
-      const size_t nw = static_cast<size_t>(H) * Dh * 2 * Dh;
-      wt_prep<<<static_cast<unsigned>((nw + 255) / 256), 256, 0, s>>>(W_a, W_x, wti, H, Dh);
+      wt_prep<<<dim3(Dh / 32, Dh / 32, H), 256, 0, s>>>(W_a, W_x, wti, H, Dh);
       const dim3 grid((Tn + kTileRows - 1) / kTileRows, H, B);
       if (resident && resident_dxc_supported(Dh)) {
         // the conv's transpose included: dx and the dconv_w partials come out of this pass
