@@ -63,8 +63,8 @@ template <int DH> struct BwdTile {
 };
 
 // dpre / dxc / part / dh0 as the separate per-element kernel writes them (layouts in
-// rglru_backward.hip: dpre holds (dpa, dpx) as fp16 pairs); agg, incl: [nTT][B][D] words (each tile's map (A, U), and g at its start),
-// all kEmpty; ctrl: [1] give-up count, [2 + g] head g's ticket, all 0.
+// rglru_backward.hip: dpre holds (dpa, dpx) as fp16 pairs); words: [nTT][B][D] (each tile's map
+// (A, U), later g at its start), all kEmpty; ctrl: [1] give-up count, [2 + g] head g's ticket, all 0.
 template <int DH>
 __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ y, const bf16_t *__restrict__ dy,
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     const float *__restrict__ b_x, const float *__restrict__ Lambda, uint32_t *__restrict__ dpre,
     uint16_t *__restrict__ dxc, float *__restrict__ part,
     float *__restrict__ dh0, int B, int T, int D, int H, int nTT, unsigned *ctrl,
-    unsigned long long *agg, unsigned long long *incl) {
+    unsigned long long *words) {
   typedef BwdTile<DH> F;
   __shared__ __attribute__((aligned(16))) bf16_t xr[2][F::kXRows * DH];  // x rows t0-3 ..
   __shared__ __attribute__((aligned(16))) bf16_t dyr[2][kRows * DH];     // dy rows t0 ..
@@ -296,24 +296,25 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
     if (half == 0) {
       const float At = A1 * A0;
       const float Ut = fmaf(A0, U1, U0);
-      // tile tt's words of this channel: agg (its map) and incl (g at its start), word k at
-      // bd + k B D
+      // tile tt's word of this channel (word k at bd + k B D): empty, then its map (A, U), then
+      // g at its start (tagged, in the high half)
       const size_t bd = static_cast<size_t>(b) * D + dc;
       const size_t tstride = static_cast<size_t>(B) * D;
-      if (tt > 0) st_relaxed(agg + bd + static_cast<size_t>(tt) * tstride, pack2(At, Ut));
+      if (tt > 0) st_relaxed(words + bd + static_cast<size_t>(tt) * tstride, pack2(At, Ut));
       // g at the tile's end is the fold g <- A_k g + U_k over the later tiles k, from dh_T at the
       // sequence end. Find the nearest later tile whose g_start is out, passing tiles whose map is
-      // out (a map never waits for anything), then apply the maps in between in the fold's own
-      // order: every incl word is an intermediate value of that one fold, so the result does not
-      // depend on which words happened to be out (bitwise the same from run to run).
+      // out (a map never waits for anything), then fold back over the tiles in between in the
+      // fold's own order, taking a tile's g_start where it is out by then and applying its map
+      // otherwise: every g_start is an intermediate value of that one fold, so the result does
+      // not depend on which words happened to be out (bitwise the same from run to run).
       int k = tt + 1;
       unsigned long long vi = kEmpty;
       unsigned spins = 0;
       bool lost = false;
       while (k < nTT) {
-        vi = ld_relaxed(incl + bd + static_cast<size_t>(k) * tstride);
-        if (vi != kEmpty) break;
-        if (ld_relaxed(agg + bd + static_cast<size_t>(k) * tstride) != kEmpty) {
+        vi = ld_relaxed(words + bd + static_cast<size_t>(k) * tstride);
+        if (is_incl(vi)) break;
+        if (vi != kEmpty) {
           ++k;
           continue;
         }
@@ -327,16 +328,16 @@ __global__ __launch_bounds__(BwdTile<DH>::kThreads, 1) void tile_bwd(
       if (lost) {
         gend = __builtin_nanf("");
       } else {
-        float gg = k < nTT ? lo_f(vi) : (dh_T ? dh_T[bd] : 0.0f);
+        float gg = k < nTT ? hi_f(vi) : (dh_T ? dh_T[bd] : 0.0f);
         for (int jt = k - 1; jt > tt; --jt) {
-          const unsigned long long va = ld_relaxed(agg + bd + static_cast<size_t>(jt) * tstride);
-          gg = fmaf(lo_f(va), gg, hi_f(va));
+          const unsigned long long va = ld_relaxed(words + bd + static_cast<size_t>(jt) * tstride);
+          gg = is_incl(va) ? hi_f(va) : fmaf(lo_f(va), gg, hi_f(va));
         }
         gend = gg;
       }
       const float gstart = fmaf(At, gend, Ut);
       if (tt > 0)
-        st_relaxed(incl + bd + static_cast<size_t>(tt) * tstride, pack2(gstart, 0.0f));
+        st_relaxed(words + bd + static_cast<size_t>(tt) * tstride, pack_incl(gstart));
       else if (dh0)
         dh0[bd] = gstart;
     }
@@ -455,7 +456,7 @@ __global__ void tile_bwd_reset(unsigned long long *slots, size_t n, unsigned *ct
 bool fused_backward_supported(int Dh) { return Dh == 128 || Dh == 256; }
 
 size_t fused_backward_slots(int B, int T, int D) {
-  return 2 * static_cast<size_t>(B) * ((T + kRows - 1) / kRows) * D;  // agg, then incl
+  return static_cast<size_t>(B) * ((T + kRows - 1) / kRows) * D;  // one word per (tile, channel)
 }
 
 hipError_t launch_fused_backward(const void *x, const void *y, const void *dy, const float *h0,
@@ -465,7 +466,6 @@ hipError_t launch_fused_backward(const void *x, const void *y, const void *dy, c
                                  float *part, float *dh0, int B, int T, int D, int H,
                                  unsigned *ctrl, unsigned long long *slots, hipStream_t s) {
   const int nTT = (T + kRows - 1) / kRows;
-  unsigned long long *agg = slots, *incl = slots + fused_backward_slots(B, T, D) / 2;
   {
     const size_t n = fused_backward_slots(B, T, D);
     tile_bwd_reset<<<fill_blocks(n), 256, 0, s>>>(slots, n, ctrl, 2 + H);
@@ -487,12 +487,12 @@ hipError_t launch_fused_backward(const void *x, const void *y, const void *dy, c
     case 128:
       tile_bwd<128><<<H * per, BwdTile<128>::kThreads, 0, s>>>(
           xx, yy, dd, h0, dh_T, cw, wa, b_a, wx, b_x, Lambda, dpre, dxc, part, dh0, B, T, D,
-          H, nTT, ctrl, agg, incl);
+          H, nTT, ctrl, slots);
       break;
     case 256:
       tile_bwd<256><<<H * per, BwdTile<256>::kThreads, 0, s>>>(
           xx, yy, dd, h0, dh_T, cw, wa, b_a, wx, b_x, Lambda, dpre, dxc, part, dh0, B, T, D,
-          H, nTT, ctrl, agg, incl);
+          H, nTT, ctrl, slots);
       break;
     default: return hipErrorInvalidValue;
   }
