@@ -64,17 +64,29 @@ size_t pre_bytes(int B, int T, int D, rglru_dtype dt) {
   return static_cast<size_t>(B) * T * D * rglru::pre_pair_bytes(dt == RGLRU_BF16 ? kBF16 : kF32);
 }
 
-// Scan-stage workspace: chunk summaries [B][nC][D] float2, then carries [B][nC][D] float.
+// Scan-stage workspace: chunk summaries [B][nC][D] float2, then carries [B][nC][D] float, then
+// the tiled scan's control words (2 + H). The tiled scan (64-step chunks chained by look-back,
+// see tiled_scan) puts its look-back words -- one 64-bit word per (tile, channel), B nC D of
+// them -- over the summaries.
 struct ScanCarve {
-  size_t sums, carry, total;
+  size_t sums, carry, ctrl, total;
 };
 
-ScanCarve scan_carve(int B, int D, int nC) {
+ScanCarve scan_carve(int B, int D, int H, int nC) {
   ScanCarve c;
   c.sums = 0;
   c.carry = align_up(static_cast<size_t>(B) * nC * D * sizeof(float2));
-  c.total = c.carry + align_up(static_cast<size_t>(B) * nC * D * sizeof(float));
+  c.ctrl = c.carry + align_up(static_cast<size_t>(B) * nC * D * sizeof(float));
+  c.total = c.ctrl + rglru::fused_ctrl_bytes(H);
   return c;
+}
+
+// The chunked plan with 64-step chunks on the shapes the fused kernel takes (bf16, Dh in {32,
+// 64, 128, 256}) runs as one pass: the fused kernel with the pre-activations read instead of
+// computed, its chunks chained by the decoupled look-back. Other chunk lengths and shapes take
+// the three passes (summaries, carries, final).
+bool tiled_scan(int T, int D, int H, rglru_dtype dt, int L) {
+  return L == 64 && rglru::fused_supported(dt == RGLRU_BF16 ? kBF16 : kF32, T, D, D / H);
 }
 
 enum Kind { kDirect, kChunked, kFused };
@@ -124,7 +136,7 @@ size_t fused_bytes(int B, int T, int D, int H) {
 size_t split_or_fused_bytes(int B, int T, int D, int H, rglru_dtype dt, Kind kind, int L) {
   if (kind == kFused) return align_up(fused_bytes(B, T, D, H));
   return rglru::kCtrlBytes + align_up(pre_bytes(B, T, D, dt)) +
-         (kind == kDirect ? 0 : scan_carve(B, D, (T + L - 1) / L).total);
+         (kind == kDirect ? 0 : scan_carve(B, D, H, (T + L - 1) / L).total);
 }
 
 rglru_status hip_status(hipError_t e) { return e == hipSuccess ? RGLRU_OK : RGLRU_ERR_HIP; }
@@ -146,7 +158,7 @@ const char *rglru_status_string(rglru_status s) {
 
 size_t rglru_scan_workspace_size(int B, int T, int D, int H, rglru_dtype dt) {
   if (check_shape(B, T, D, H, dt) != RGLRU_OK) return 0;
-  return scan_carve(B, D, (T + kMinChunk - 1) / kMinChunk).total;
+  return scan_carve(B, D, H, (T + kMinChunk - 1) / kMinChunk).total;
 }
 
 size_t rglru_forward_workspace_size(int B, int T, int D, int H, rglru_dtype dt) {
@@ -194,11 +206,15 @@ rglru_status rglru_forward_plan_info(int B, int T, int D, int H, rglru_dtype dt,
   return RGLRU_OK;
 }
 
-rglru_status rglru_scan_preacts(const void *x, const void *pre, const void *conv_w,
-                                const float *Lambda, const float *h0, void *y, float *h_T, int B,
-                                int T, int D, int H, rglru_dtype dt, void *workspace,
-                                size_t workspace_bytes, void *stream, rglru_plan plan,
-                                int chunk_len) {
+}  // extern "C"
+
+namespace {
+// rglru_scan_preacts; gave_up (or NULL: a word of the scan's own workspace) counts the look-back
+// waits of the tiled scan that gave up.
+rglru_status scan_preacts(const void *x, const void *pre, const void *conv_w,
+                          const float *Lambda, const float *h0, void *y, float *h_T, int B, int T,
+                          int D, int H, rglru_dtype dt, void *workspace, size_t workspace_bytes,
+                          void *stream, rglru_plan plan, int chunk_len, unsigned *gave_up) {
   rglru_status st = check_shape(B, T, D, H, dt);
   if (st != RGLRU_OK) return st;
   if (!x || !pre || !conv_w || !Lambda || !y) return RGLRU_ERR_INVALID_ARG;
@@ -218,7 +234,7 @@ rglru_status rglru_scan_preacts(const void *x, const void *pre, const void *conv
     return RGLRU_ERR_INVALID_ARG;
   const int nC = direct ? 0 : (T + L - 1) / L;
   if (nC > 65535) return RGLRU_ERR_UNSUPPORTED;  // one grid row per chunk
-  const ScanCarve c = scan_carve(B, D, nC);
+  const ScanCarve c = scan_carve(B, D, H, nC);
   if (!direct) {
     if (!workspace || workspace_bytes < c.total) return RGLRU_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return RGLRU_ERR_INVALID_ARG;
@@ -233,9 +249,27 @@ rglru_status rglru_scan_preacts(const void *x, const void *pre, const void *conv
     return hip_status(
         rglru::launch_scan_direct(x, pre, conv_w, Lambda, h0, y, h_T, B, T, D, io, s));
   char *ws = static_cast<char *>(workspace);
+  if (tiled_scan(T, D, H, dt, L)) {
+    unsigned *ctrl = reinterpret_cast<unsigned *>(ws + c.ctrl);
+    return hip_status(rglru::launch_scan_tiled(
+        x, pre, conv_w, Lambda, h0, y, h_T, B, T, D, H, ctrl, gave_up ? gave_up : ctrl + 1,
+        reinterpret_cast<unsigned long long *>(ws + c.sums), s));
+  }
   return hip_status(rglru::launch_scan_chunked(x, pre, conv_w, Lambda, h0, y, h_T, B, T, D, L,
                                                reinterpret_cast<float2 *>(ws + c.sums),
                                                reinterpret_cast<float *>(ws + c.carry), io, s));
+}
+}  // namespace
+
+extern "C" {
+
+rglru_status rglru_scan_preacts(const void *x, const void *pre, const void *conv_w,
+                                const float *Lambda, const float *h0, void *y, float *h_T, int B,
+                                int T, int D, int H, rglru_dtype dt, void *workspace,
+                                size_t workspace_bytes, void *stream, rglru_plan plan,
+                                int chunk_len) {
+  return scan_preacts(x, pre, conv_w, Lambda, h0, y, h_T, B, T, D, H, dt, workspace,
+                      workspace_bytes, stream, plan, chunk_len, nullptr);
 }
 
 rglru_status rglru_forward_planned(const void *x, const void *conv_w, const void *W_a,
@@ -284,15 +318,15 @@ rglru_status rglru_forward_planned(const void *x, const void *conv_w, const void
   char *ws = static_cast<char *>(workspace);
   char *pre = ws + rglru::kCtrlBytes;
   (void)hipGetLastError();  // start from a clean error state
-  // the split plans never wait: their look-back failure count is zero
+  // the look-back failure count: zero, bumped only by the tiled scan's waits that give up
   hipError_t e = rglru::launch_clear_words(reinterpret_cast<unsigned *>(ws), 2, s);
   if (e == hipSuccess)
     e = rglru::launch_gates(x, conv_w, W_a, b_a, W_x, b_x, pre, B, T, D, H, io, s);
   if (e != hipSuccess) return RGLRU_ERR_HIP;
-  return rglru_scan_preacts(x, pre, conv_w, Lambda, h0, y, h_T, B, T, D, H, dt, ws + pre_area,
-                            workspace_bytes - pre_area, stream, direct ? RGLRU_PLAN_DIRECT
-                                                                       : RGLRU_PLAN_CHUNKED,
-                            L);
+  return scan_preacts(x, pre, conv_w, Lambda, h0, y, h_T, B, T, D, H, dt, ws + pre_area,
+                      workspace_bytes - pre_area, stream,
+                      direct ? RGLRU_PLAN_DIRECT : RGLRU_PLAN_CHUNKED, L,
+                      reinterpret_cast<unsigned *>(ws) + 1);
 }
 
 rglru_status rglru_forward(const void *x, const void *conv_w, const void *W_a, const float *b_a,

@@ -136,7 +136,7 @@ __device__ __forceinline__ void stage_x(const bf16_t *__restrict__ x, bf16_t *xr
 // the thread index on every call so that none of it stays live (and gets spilled) across the
 // rest of the tile. A wave spans whole row groups only when a row group is >= 64 lanes wide
 // (Dh >= 128); then the row index is wave-uniform and stays scalar.
-template <int DH>
+template <int DH, bool WITH_XA = true>
 __device__ __forceinline__ void conv_prologue(const bf16_t *xr, bf16_t *xa, float *xf,
                                               const uint32_t *cws, int tid) {
   typedef Fused<DH> F;
@@ -179,7 +179,7 @@ __device__ __forceinline__ void conv_prologue(const bf16_t *xr, bf16_t *xa, floa
       const float o1 = __builtin_amdgcn_fdot2_f32_bf16(
           ph[r + 2], w23h, __builtin_amdgcn_fdot2_f32_bf16(ph[r], w01h, 0.0f, false), false);
       const int row = pr0 + rb + r;
-      *reinterpret_cast<uint32_t *>(xa + row * F::kLda + pc0) = pack_bf16x2(o0, o1);
+      if (WITH_XA) *reinterpret_cast<uint32_t *>(xa + row * F::kLda + pc0) = pack_bf16x2(o0, o1);
       *reinterpret_cast<float2 *>(xf + row * F::kLdx + pc0) = make_float2(o0, o1);
     }
   }
@@ -226,19 +226,28 @@ __device__ __forceinline__ void gate_b(float e, float px, float xv, float bx2, f
 // Rows past the end of the sequence (only in the last tile) are computed like the others from
 // zero input -- they come after every real row, so they cannot change a real row's state -- and
 // only their stores are masked; h_T is then taken at row T-1 instead of at the end of the tile.
-template <int DH>
+//
+// PRE: the split plan's scan. The gate pre-activations (biases included) come from pre, fp16
+// pairs (pa, px) [B][T][D] written by the gate kernel, instead of the MFMAs: each lane loads its
+// 32 elements straight into the accumulator layout (a half-wave reads one 128-byte line per
+// row), one tile ahead. Without the resident weights the registers hold both tiles. The next
+// tile's ticket is then published before the conv barrier, so that every wave can issue those
+// loads after it. Everything else -- conv for the input term, gates, scan, look-back, fix-up --
+// is the same code.
+template <int DH, bool PRE>
 __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ conv_w,
     const bf16_t *__restrict__ W_a, const float *__restrict__ b_a,
     const bf16_t *__restrict__ W_x, const float *__restrict__ b_x,
+    const uint32_t *__restrict__ pre,
     const float *__restrict__ Lambda, const float *__restrict__ h0, bf16_t *__restrict__ y,
     float *__restrict__ h_T, int B, int T, int D, int H, int nTT, unsigned *ctrl,
-    unsigned long long *slots) {
+    unsigned *gave_up, unsigned long long *slots) {
   typedef Fused<DH> F;
   constexpr int PP = DH / 2;  // channel pairs
   // xa: the conv output in bf16, the MFMA A operand; xf: the same in fp32 for the input term;
   // xr: the staged x rows.
-  __shared__ __attribute__((aligned(16))) bf16_t xa[kFusedRows * F::kLda];
+  __shared__ __attribute__((aligned(16))) bf16_t xa[PRE ? 8 : kFusedRows * F::kLda];
   __shared__ __attribute__((aligned(16))) float xf[kFusedRows * F::kLdx];
   __shared__ __attribute__((aligned(16))) bf16_t xr[F::kXRows * DH];
   __shared__ uint32_t cws[4 * PP];  // conv taps of the head, bf16 pairs
@@ -255,10 +264,10 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
   const int cl = w * 32 + lrow;  // this lane's channel within the head
   const int d = g * DH + cl;
   const float kd = decay_coeff(Lambda[d]);
-  const float ba2 = -kLog2e * b_a[d], bx2 = -kLog2e * b_x[d];
+  const float ba2 = PRE ? 0.0f : -kLog2e * b_a[d], bx2 = PRE ? 0.0f : -kLog2e * b_x[d];
   // B operand of this wave: its 32 channels' W_a / W_x rows, resident for the kernel's life
   bf16x8_t wa[F::kKS], wx[F::kKS];
-  {
+  if (!PRE) {
     const bf16_t *wa_row = W_a + (static_cast<size_t>(g) * DH + cl) * DH + half * 8;
     const bf16_t *wx_row = W_x + (static_cast<size_t>(g) * DH + cl) * DH + half * 8;
 #pragma unroll
@@ -281,11 +290,25 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
   // wave 0 publishes it and stages its rows, so the ticket round trip and the x loads overlap
   // the conv, the MFMA and the gate math. (Claiming further ahead lets a tile wait behind two
   // of its owner's tiles, and its successors in time wait on it.) s_tile is a ring of three.
+  // PRE: this lane's 32 pre-activation pairs of tile j (time row 32 rt + 16 half + jj, channel
+  // cl; rows past T read row T - 1: they only feed rows that are not stored)
+  uint32_t pn[32];
+  auto load_pre = [&](int j) {
+    const int b = j % B, t0 = (j / B) * kFusedRows;
+    const uint32_t *pb = pre + static_cast<size_t>(b) * T * D + d;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj)
+        pn[16 * rt + jj] =
+            pb[static_cast<size_t>(min(t0 + 32 * rt + 16 * half + jj, T - 1)) * D];
+  };
   if (tid == 0) s_tile[0] = static_cast<int>(atomicAdd(ticket, 1u));
   __syncthreads();
   {
     const int j0 = __builtin_amdgcn_readfirstlane(s_tile[0]);
     if (j0 < ntiles) stage_x<DH, F::kNW>(x, xr, j0 % B, (j0 / B) * kFusedRows, g, w, lane, T, D);
+    if (PRE && j0 < ntiles) load_pre(j0);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
   }
 
@@ -301,7 +324,8 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
     tc.tt = tc.j / B;
     tc.b = tc.j % B;
     tc.t0 = tc.tt * kFusedRows;
-    conv_prologue<DH>(xr, xa, xf, cws, tid);
+    conv_prologue<DH, !PRE>(xr, xa, xf, cws, tid);
+    if (PRE && tid == 0) s_tile[slot1] = static_cast<int>(claim);
     __syncthreads();
 
     // ---- gate projections on MFMA: 64 rows x (32 channels x 2 gates) per wave. The A operand's
@@ -313,24 +337,40 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
     const int prow = 16 * ((lrow >> 2) & 1) + 4 * (lrow >> 3) + (lrow & 3);
     const bf16_t *xap = xa + prow * F::kLda + half * 8;
     f32x16_t acc[2][2];  // [row tile][gate]
+    if constexpr (PRE) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      acc[rt][0] = f32x16_t{};
-      acc[rt][1] = f32x16_t{};
-    }
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int ks = 0; ks < F::kKS; ++ks) {
-      const bf16x8_t af = load_bf16x8(xap + ks * 16);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wa[ks], acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wx[ks], acc[0][1], 0, 0, 0);
-    }
+        for (int jj = 0; jj < 16; ++jj) {
+          acc[rt][0][jj] = f16lo(pn[16 * rt + jj]);
+          acc[rt][1][jj] = f16hi(pn[16 * rt + jj]);
+        }
+      // the next tile's pre-activations and x rows, in flight during this tile
+      const int jn = __builtin_amdgcn_readfirstlane(s_tile[slot1]);
+      if (jn < ntiles) {
+        load_pre(jn);
+        if (w == 0) stage_x<DH, 1>(x, xr, jn % B, (jn / B) * kFusedRows, g, 0, lane, T, D);
+      }
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        acc[rt][0] = f32x16_t{};
+        acc[rt][1] = f32x16_t{};
+      }
+#pragma unroll
+      for (int ks = 0; ks < F::kKS; ++ks) {
+        const bf16x8_t af = load_bf16x8(xap + ks * 16);
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wa[ks], acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wx[ks], acc[0][1], 0, 0, 0);
+      }
 
-    // ---- stage the next tile's rows (the prologue that read the buffer finished before the
-    // barrier above); they land during the gate math.
-    if (w == 0) {
-      const int jn = __builtin_amdgcn_readfirstlane(claim);
-      if (lane == 0) s_tile[slot1] = jn;
-      if (jn < ntiles) stage_x<DH, 1>(x, xr, jn % B, (jn / B) * kFusedRows, g, 0, lane, T, D);
+      // ---- stage the next tile's rows (the prologue that read the buffer finished before the
+      // barrier above); they land during the gate math.
+      if (w == 0) {
+        const int jn = __builtin_amdgcn_readfirstlane(claim);
+        if (lane == 0) s_tile[slot1] = jn;
+        if (jn < ntiles) stage_x<DH, 1>(x, xr, jn % B, (jn / B) * kFusedRows, g, 0, lane, T, D);
+      }
     }
 
     // x of this lane's runs, fp32 (time row rt*32 + 16*half + jj, channel cl)
@@ -344,7 +384,7 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
       float xn0 = xfl[0], xn1 = xfl[F::kLdx];
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) {
-        if (ks < F::kKS) {
+        if (!PRE && ks < F::kKS) {
           const bf16x8_t af = load_bf16x8(xap + 32 * F::kLda + ks * 16);
           acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wa[ks], acc[1][0], 0, 0, 0);
           acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wx[ks], acc[1][1], 0, 0, 0);
@@ -440,7 +480,7 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
             }
           } else {
             if (++spins > kMaxSpin) {
-              atomicAdd(ctrl + 1, 1u);
+              atomicAdd(gave_up, 1u);
               h_in = __builtin_nanf("");
               break;
             }
@@ -543,8 +583,9 @@ hipError_t launch_fused(const void *x, const void *conv_w, const void *W_a, cons
 #define RGLRU_FUSED_CASE(DHV)                                                                   \
   case DHV: {                                                                                   \
     const int per = std::max(1, (cus + H - 1) / H);                                             \
-    fused_forward<DHV><<<H * per, Fused<DHV>::kThreads, 0, s>>>(                                \
-        xx, cw, wa, b_a, wx, b_x, Lambda, h0, yy, h_T, B, T, D, H, nTT, ctrl, slots);           \
+    fused_forward<DHV, false><<<H * per, Fused<DHV>::kThreads, 0, s>>>(                         \
+        xx, cw, wa, b_a, wx, b_x, nullptr, Lambda, h0, yy, h_T, B, T, D, H, nTT, ctrl, ctrl + 1, \
+        slots);                                                                                 \
     break;                                                                                      \
   }
   switch (Dh) {
@@ -555,6 +596,46 @@ hipError_t launch_fused(const void *x, const void *conv_w, const void *W_a, cons
     default: return hipErrorInvalidValue;
   }
 #undef RGLRU_FUSED_CASE
+  return hipGetLastError();
+}
+
+// The split plan's scan over 64-step tiles chained by the same look-back (bf16, Dh in
+// {32, 64, 128, 256}): pre holds the gate pre-activations (fp16 pairs, biases included); ctrl:
+// 2 + H words (tickets), words: fused_slots(B, T, H, Dh) look-back words, both reset here;
+// gave_up: the count of lanes whose look-back wait gave up (not reset here).
+hipError_t launch_scan_tiled(const void *x, const void *pre, const void *conv_w,
+                             const float *Lambda, const float *h0, void *y, float *h_T, int B,
+                             int T, int D, int H, unsigned *ctrl, unsigned *gave_up,
+                             unsigned long long *words, hipStream_t s) {
+  const int Dh = D / H;
+  const int nTT = (T + kFusedRows - 1) / kFusedRows;
+  const size_t nslot = fused_slots(B, T, H, Dh);
+  fused_reset<<<fill_blocks(nslot), 256, 0, s>>>(words, nslot, ctrl, 2 + H);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const bf16_t *xx = static_cast<const bf16_t *>(x);
+  const bf16_t *cw = static_cast<const bf16_t *>(conv_w);
+  const uint32_t *pp = static_cast<const uint32_t *>(pre);
+  bf16_t *yy = static_cast<bf16_t *>(y);
+#define RGLRU_TILED_CASE(DHV)                                                                   \
+  case DHV: {                                                                                   \
+    const int per = std::max(1, (cus + H - 1) / H);                                             \
+    fused_forward<DHV, true><<<H * per, Fused<DHV>::kThreads, 0, s>>>(                          \
+        xx, cw, nullptr, nullptr, nullptr, nullptr, pp, Lambda, h0, yy, h_T, B, T, D, H, nTT,    \
+        ctrl, gave_up, words);                                                                  \
+    break;                                                                                      \
+  }
+  switch (Dh) {
+    RGLRU_TILED_CASE(32)
+    RGLRU_TILED_CASE(64)
+    RGLRU_TILED_CASE(128)
+    RGLRU_TILED_CASE(256)
+    default: return hipErrorInvalidValue;
+  }
+#undef RGLRU_TILED_CASE
   return hipGetLastError();
 }
 

@@ -55,13 +55,16 @@ typedef enum { RGLRU_F32 = 0, RGLRU_BF16 = 1 } rglru_dtype;
  * workspace (MFMA gate projection), then scan: DIRECT has one lane per (b, d) walk all T steps;
  * CHUNKED cuts time into chunks, pass 1 reduces each chunk to (sum of log a, local state), pass 2
  * prefixes those summaries across chunks with a wavefront scan, pass 3 re-scans each chunk from
- * its carry-in. FUSED (bf16, Dh in {32, 64, 128, 256}) does everything in one pass over 64-step
+ * its carry-in; with 64-step chunks on the shapes FUSED takes it runs as one pass instead, the
+ * chunks linked by FUSED's decoupled look-back with the pre-activations read rather than
+ * computed. FUSED (bf16, Dh in {32, 64, 128, 256}) does everything in one pass over 64-step
  * tiles -- conv, MFMA gates, nonlinearity, in-tile scan -- and links the tiles of a sequence by a
  * decoupled look-back, so HBM sees x once and y once. All give the same result up to fp32
- * rounding and the rounding of stored pre-activations (the scan is associative). DIRECT and
- * CHUNKED are bitwise deterministic; FUSED combines whichever predecessor tiles have published
- * when it looks back, so its carried state is reproducible to fp32 rounding only. AUTO picks
- * FUSED when supported, else DIRECT or CHUNKED by the number of channels. */
+ * rounding and the rounding of stored pre-activations (the scan is associative). DIRECT and the
+ * three-pass CHUNKED are bitwise deterministic; FUSED and the one-pass CHUNKED combine whichever
+ * predecessor tiles have published when they look back, so their carried state is reproducible
+ * to fp32 rounding only. AUTO picks FUSED when supported, else DIRECT or CHUNKED by the number of
+ * channels. */
 typedef enum {
   RGLRU_PLAN_AUTO = 0,
   RGLRU_PLAN_DIRECT = 1,
@@ -85,8 +88,8 @@ size_t rglru_forward_workspace_size_planned(int B, int T, int D, int H, rglru_dt
 
 /* Every rglru_forward / rglru_forward_planned / rglru_backward workspace begins with a control
  * block; its failure count is the number of look-back waits of the last such call on this
- * workspace that gave up. The FUSED forward and the backward's tile pass link time tiles by
- * bounded waits on words other tiles publish; a wait that exceeds its bound (which only a broken
+ * workspace that gave up. The FUSED forward, the one-pass CHUNKED scan and the backward's tile
+ * pass link time tiles by bounded waits on words other tiles publish; a wait that exceeds its bound (which only a broken
  * ordering invariant can cause) stops, writes NaN for its channel and bumps the count, so a
  * defect shows as NaN and a nonzero count, never as a hang. Plans without waits set the count to
  * zero. This call waits for `stream` (the copy is ordered after the work queued on it), then
@@ -162,8 +165,9 @@ size_t rglru_scan_workspace_size(int B, int T, int D, int H, rglru_dtype dt);
 /* The scan stage alone: conv recomputed from x, gate nonlinearity and RG-LRU scan, reading the
  * pre-activation pairs in the layout rglru_gate_preacts writes. Arguments as for
  * rglru_forward_planned (plan AUTO, DIRECT or CHUNKED; FUSED is rejected as invalid, it has no
- * separate scan stage); `pre` must not overlap y; workspace holds only the chunk summaries
- * (RGLRU_PLAN_DIRECT needs none: workspace may then be NULL). rglru_forward with the DIRECT or
+ * separate scan stage); `pre` must not overlap y; workspace holds only the chunk summaries, or
+ * for the one-pass CHUNKED form the look-back words and tickets (RGLRU_PLAN_DIRECT needs none:
+ * workspace may then be NULL). rglru_forward with the DIRECT or
  * CHUNKED plan is exactly rglru_gate_preacts followed by this call. */
 rglru_status rglru_scan_preacts(const void *x, const void *pre, const void *conv_w,
                                 const float *Lambda, const float *h0, void *y, float *h_T, int B,
