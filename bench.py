@@ -43,6 +43,12 @@ def is_backward_kernel(name: str) -> bool:
     return any(n.startswith(k) for k in BACKWARD_KERNELS)
 
 
+def is_fused_kernel(name: str) -> bool:
+    """The fused forward's kernels (its main kernel and the look-back reset), not the same
+    kernel's instantiation that serves the chunked plan's one-pass scan (template flag true)."""
+    return ("fused_forward" in name and ", true>" not in name) or "fused_reset" in name
+
+
 def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
     for f in sources or KERNEL_SOURCES:
@@ -135,7 +141,8 @@ def traffic_summary(fetch_csv, write_csv, workload, copy_mib=256):
     out = {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = [r for r in _counter_rows(path) if r["Counter_Name"] == name]
-        fused = [float(r["Counter_Value"]) for r in rows if "fused_forward" in r["Kernel_Name"]]
+        fused = [float(r["Counter_Value"]) for r in rows
+                 if is_fused_kernel(r["Kernel_Name"]) and "fused_reset" not in r["Kernel_Name"]]
         copy = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         if not fused or not copy:
             raise SystemExit(f"{path}: no fused_forward or copy dispatches with {name}")
@@ -344,8 +351,7 @@ def trace_summary(stats_csv, workload, bench_line_path=None, key="rg2b"):
             name = r["Name"].split("(")[0].replace("void ", "")
             f.write(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.2f} "
                     f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}  {name}\n")
-        per_call = sum(float(r["AverageNs"]) for r in rows
-                       if "fused_forward" in r["Name"] or "fused_reset" in r["Name"]) / 1e3
+        per_call = sum(float(r["AverageNs"]) for r in rows if is_fused_kernel(r["Name"])) / 1e3
         f.write(f"fused_call_us (fused_forward + fused_reset, one rglru_forward): {per_call:.2f}\n")
         bwd = sum(float(r["AverageNs"]) for r in rows if is_backward_kernel(r["Name"])) / 1e3
         f.write(f"backward_call_us (sum of the averages of the backward's kernels, one "
