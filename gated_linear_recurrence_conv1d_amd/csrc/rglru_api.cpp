@@ -318,8 +318,11 @@ rglru_status rglru_forward_planned(const void *x, const void *conv_w, const void
   char *ws = static_cast<char *>(workspace);
   char *pre = ws + rglru::kCtrlBytes;
   (void)hipGetLastError();  // start from a clean error state
-  // the look-back failure count: zero, bumped only by the tiled scan's waits that give up
-  hipError_t e = rglru::launch_clear_words(reinterpret_cast<unsigned *>(ws), 2, s);
+  // the look-back failure count: zero, bumped only by the tiled scan's waits that give up (its
+  // launcher zeroes it; the other scans never wait)
+  hipError_t e = hipSuccess;
+  if (direct || !tiled_scan(T, D, H, dt, L))
+    e = rglru::launch_clear_words(reinterpret_cast<unsigned *>(ws), 2, s);
   if (e == hipSuccess)
     e = rglru::launch_gates(x, conv_w, W_a, b_a, W_x, b_x, pre, B, T, D, H, io, s);
   if (e != hipSuccess) return RGLRU_ERR_HIP;

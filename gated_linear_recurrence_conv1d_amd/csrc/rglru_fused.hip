@@ -81,8 +81,12 @@ __device__ __forceinline__ bf16x8_t f32x8_to_bf16x8(const float *p) {
 
 // Look-back words to kEmpty and control words to 0: [0] unused, [1] count of lanes that gave up
 // waiting, [2 + g] the tile ticket of head g.
-__global__ void fused_reset(unsigned long long *slots, size_t n, unsigned *ctrl, int nctrl) {
+// (extra: one more word to 0, or NULL -- the failure count of a workspace whose control block
+// lies elsewhere)
+__global__ void fused_reset(unsigned long long *slots, size_t n, unsigned *ctrl, int nctrl,
+                            unsigned *extra) {
   fill_lookback(slots, n, ctrl, nctrl);
+  if (extra && blockIdx.x == 0 && threadIdx.x == 0) *extra = 0u;
 }
 
 __global__ void clear_words(unsigned *p, int n) {
@@ -567,7 +571,7 @@ hipError_t launch_fused(const void *x, const void *conv_w, const void *W_a, cons
   unsigned *ctrl = static_cast<unsigned *>(ctrl_ws);
   unsigned long long *slots =
       reinterpret_cast<unsigned long long *>(static_cast<char *>(ctrl_ws) + fused_ctrl_bytes(H));
-  fused_reset<<<fill_blocks(nslot), 256, 0, s>>>(slots, nslot, ctrl, 2 + H);
+  fused_reset<<<fill_blocks(nslot), 256, 0, s>>>(slots, nslot, ctrl, 2 + H, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int dev = 0, cus = 256;
@@ -602,7 +606,7 @@ hipError_t launch_fused(const void *x, const void *conv_w, const void *W_a, cons
 // The split plan's scan over 64-step tiles chained by the same look-back (bf16, Dh in
 // {32, 64, 128, 256}): pre holds the gate pre-activations (fp16 pairs, biases included); ctrl:
 // 2 + H words (tickets), words: fused_slots(B, T, H, Dh) look-back words, both reset here;
-// gave_up: the count of lanes whose look-back wait gave up (not reset here).
+// gave_up: the count of lanes whose look-back wait gave up (reset here too).
 hipError_t launch_scan_tiled(const void *x, const void *pre, const void *conv_w,
                              const float *Lambda, const float *h0, void *y, float *h_T, int B,
                              int T, int D, int H, unsigned *ctrl, unsigned *gave_up,
@@ -610,7 +614,8 @@ hipError_t launch_scan_tiled(const void *x, const void *pre, const void *conv_w,
   const int Dh = D / H;
   const int nTT = (T + kFusedRows - 1) / kFusedRows;
   const size_t nslot = fused_slots(B, T, H, Dh);
-  fused_reset<<<fill_blocks(nslot), 256, 0, s>>>(words, nslot, ctrl, 2 + H);
+  fused_reset<<<fill_blocks(nslot), 256, 0, s>>>(words, nslot, ctrl, 2 + H,
+                                                 gave_up == ctrl + 1 ? nullptr : gave_up);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int dev = 0, cus = 256;

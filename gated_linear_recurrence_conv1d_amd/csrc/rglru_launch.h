@@ -62,7 +62,7 @@ hipError_t launch_fused(const void *x, const void *conv_w, const void *W_a, cons
 // The split plan's scan with the same kernel, the gate pre-activations read from pre (fp16
 // pairs, biases included) instead of computed (shapes as fused_supported): ctrl 2 + H words and
 // fused_slots() look-back words, reset by the launcher; gave_up counts look-back waits that gave
-// up (not reset).
+// up (reset by the launcher too).
 hipError_t launch_scan_tiled(const void *x, const void *pre, const void *conv_w,
                              const float *Lambda, const float *h0, void *y, float *h_T, int B,
                              int T, int D, int H, unsigned *ctrl, unsigned *gave_up,
