@@ -367,6 +367,27 @@ def trace_summary(stats_csv, workload, bench_line_path=None, key="rg2b"):
     print(open(path).read(), end="")
 
 
+def settle_clocks(torch, dev, seconds):
+    """Keep the GPU busy for `seconds` of wall time with work that is not the measured path (a
+    bf16 matrix product and a 256 MiB device copy, alternating), so that its clocks have left
+    idle before the warm-up steps; the driver's short warm-ups (a handful of ~0.1 ms steps) end
+    while the clocks are still ramping. Returns the seconds spent."""
+    if seconds <= 0:
+        return 0.0
+    a = torch.randn(4096, 4096, device=dev).to(torch.bfloat16)
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            torch.matmul(a, a)
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    del a, src, dst
+    return time.perf_counter() - t0
+
+
 def decode_leg(torch, rg, reps=3):
     """The batched decode step on its workload (1024 rows, D=4096, 16 heads, 256 consecutive
     in-place steps): every step of the workload is timed, after one untimed pass."""
@@ -610,6 +631,9 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     # the warm-up also brings the GPU clocks up to their steady state (a few hundred ms)
     ap.add_argument("--warmup", type=int, default=3000)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="seconds of unrelated GPU work (matmul + copy) before the warm-up steps, "
+                         "so that the clocks have left idle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
@@ -686,6 +710,7 @@ def main():
         rg.rglru_forward(xs[k], g["conv_w"], g["W_a"], g["b_a"], g["W_x"], g["b_x"], g["Lam"],
                          g["h0"], ys[k], hTs[k], ws)
 
+    settled = settle_clocks(torch, dev, args.settle_s)
     for i in range(args.warmup):
         fwd(i)
     torch.cuda.synchronize()
@@ -786,6 +811,7 @@ def main():
         "value": n / (ms * 1e-3),
         "unit": "tokens·channels/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "clock_settle_s": round(settled, 3),
         "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if io == torch.bfloat16 else "f32",
