@@ -77,7 +77,7 @@ ScanCarve scan_carve(int B, int D, int H, int nC) {
   c.sums = 0;
   c.carry = align_up(static_cast<size_t>(B) * nC * D * sizeof(float2));
   c.ctrl = c.carry + align_up(static_cast<size_t>(B) * nC * D * sizeof(float));
-  c.total = c.ctrl + rglru::fused_ctrl_bytes(H);
+  c.total = c.ctrl + rglru::fused_ctrl_bytes(rglru::scan_tiled_groups(D, H));
   return c;
 }
 

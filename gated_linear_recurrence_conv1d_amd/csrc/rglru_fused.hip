@@ -603,18 +603,31 @@ hipError_t launch_fused(const void *x, const void *conv_w, const void *W_a, cons
   return hipGetLastError();
 }
 
+// Channel groups of the split plan's scan. Without the gate contraction nothing ties a
+// workgroup to a whole head: every channel's recurrence is independent once its
+// pre-activations are given. Heads of 256 channels are therefore scanned as groups of 128 (four
+// waves, 52 KB of LDS), several workgroups per CU that share no barrier, so one's look-back or
+// stores overlap another's gate math.
+int scan_tiled_group(int Dh) { return Dh == 256 ? 128 : Dh; }
+int scan_tiled_groups(int D, int H) { return D / scan_tiled_group(D / H); }
+// Workgroups of the scan per CU (grid = this many per CU's worth of groups; they are resident
+// together at Dh 128: 167 VGPRs allow three waves per SIMD, the LDS three workgroups).
+static int scan_tiled_per_cu(int G) { return G == 128 ? 3 : 1; }
+
 // The split plan's scan over 64-step tiles chained by the same look-back (bf16, Dh in
 // {32, 64, 128, 256}): pre holds the gate pre-activations (fp16 pairs, biases included); ctrl:
-// 2 + H words (tickets), words: fused_slots(B, T, H, Dh) look-back words, both reset here;
-// gave_up: the count of lanes whose look-back wait gave up (reset here too).
+// 2 + scan_tiled_groups(D, H) words (tickets), words: fused_slots(B, T, H, Dh) look-back words
+// (the same count under any grouping), both reset here; gave_up: the count of lanes whose
+// look-back wait gave up (reset here too).
 hipError_t launch_scan_tiled(const void *x, const void *pre, const void *conv_w,
                              const float *Lambda, const float *h0, void *y, float *h_T, int B,
                              int T, int D, int H, unsigned *ctrl, unsigned *gave_up,
                              unsigned long long *words, hipStream_t s) {
-  const int Dh = D / H;
+  const int G = scan_tiled_group(D / H);  // channels per workgroup
+  const int Hg = D / G;                   // channel groups, each scanned like a head
   const int nTT = (T + kFusedRows - 1) / kFusedRows;
-  const size_t nslot = fused_slots(B, T, H, Dh);
-  fused_reset<<<fill_blocks(nslot), 256, 0, s>>>(words, nslot, ctrl, 2 + H,
+  const size_t nslot = fused_slots(B, T, Hg, G);
+  fused_reset<<<fill_blocks(nslot), 256, 0, s>>>(words, nslot, ctrl, 2 + Hg,
                                                  gave_up == ctrl + 1 ? nullptr : gave_up);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -627,13 +640,13 @@ hipError_t launch_scan_tiled(const void *x, const void *pre, const void *conv_w,
   bf16_t *yy = static_cast<bf16_t *>(y);
 #define RGLRU_TILED_CASE(DHV)                                                                   \
   case DHV: {                                                                                   \
-    const int per = std::max(1, (cus + H - 1) / H);                                             \
-    fused_forward<DHV, true><<<H * per, Fused<DHV>::kThreads, 0, s>>>(                          \
-        xx, cw, nullptr, nullptr, nullptr, nullptr, pp, Lambda, h0, yy, h_T, B, T, D, H, nTT,    \
+    const int per = std::max(1, (scan_tiled_per_cu(G) * cus + Hg - 1) / Hg);                   \
+    fused_forward<DHV, true><<<Hg * per, Fused<DHV>::kThreads, 0, s>>>(                         \
+        xx, cw, nullptr, nullptr, nullptr, nullptr, pp, Lambda, h0, yy, h_T, B, T, D, Hg, nTT,   \
         ctrl, gave_up, words);                                                                  \
     break;                                                                                      \
   }
-  switch (Dh) {
+  switch (G) {
     RGLRU_TILED_CASE(32)
     RGLRU_TILED_CASE(64)
     RGLRU_TILED_CASE(128)

@@ -60,9 +60,12 @@ hipError_t launch_fused(const void *x, const void *conv_w, const void *W_a, cons
                         void *y, float *h_T, int B, int T, int D, int H, void *ctrl_ws,
                         hipStream_t s);
 // The split plan's scan with the same kernel, the gate pre-activations read from pre (fp16
-// pairs, biases included) instead of computed (shapes as fused_supported): ctrl 2 + H words and
-// fused_slots() look-back words, reset by the launcher; gave_up counts look-back waits that gave
-// up (reset by the launcher too).
+// pairs, biases included) instead of computed (shapes as fused_supported), over groups of
+// scan_tiled_group(Dh) channels: ctrl 2 + scan_tiled_groups(D, H) words and fused_slots()
+// look-back words, reset by the launcher; gave_up counts look-back waits that gave up (reset by
+// the launcher too).
+int scan_tiled_group(int Dh);
+int scan_tiled_groups(int D, int H);
 hipError_t launch_scan_tiled(const void *x, const void *pre, const void *conv_w,
                              const float *Lambda, const float *h0, void *y, float *h_T, int B,
                              int T, int D, int H, unsigned *ctrl, unsigned *gave_up,
