@@ -93,38 +93,38 @@ PROFILE_CMDS = {
              "python3 REPO/bench.py --no-cpu-baseline --no-plan-legs",
     "fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'fused_forward|copyBuffer' -d "
              "OUT/fetch -o fetch --output-format csv -- python3 REPO/bench.py --steps 5 "
-             "--warmup 5 --no-cpu-baseline --no-decode --no-backward --no-mqa --no-plan-legs "
+             "--warmup 5 --no-cpu-baseline --settle-s 0 --no-decode --no-backward --no-mqa --no-plan-legs "
              "--copy-calibration 256",
     "write": "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex 'fused_forward|copyBuffer' -d "
              "OUT/write -o write --output-format csv -- python3 REPO/bench.py --steps 5 "
-             "--warmup 5 --no-cpu-baseline --no-decode --no-backward --no-mqa --no-plan-legs "
+             "--warmup 5 --no-cpu-baseline --settle-s 0 --no-decode --no-backward --no-mqa --no-plan-legs "
              "--copy-calibration 256",
     "bwd_fetch": "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "
                  "'tile_|bwd_|wt_prep|dxc_|conv_bwd|dw_|colsum|copyBuffer' -d OUT/bfetch -o fetch "
                  "--output-format csv -- python3 REPO/bench.py --steps 5 --warmup 5 "
-                 "--no-cpu-baseline --no-decode --no-mqa --no-plan-legs --bwd-warmup 2 "
+                 "--no-cpu-baseline --settle-s 0 --no-decode --no-mqa --no-plan-legs --bwd-warmup 2 "
                  "--bwd-reps 3 --copy-calibration 256",
     "bwd_write": "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex "
                  "'tile_|bwd_|wt_prep|dxc_|conv_bwd|dw_|colsum|copyBuffer' -d OUT/bwrite -o write "
                  "--output-format csv -- python3 REPO/bench.py --steps 5 --warmup 5 "
-                 "--no-cpu-baseline --no-decode --no-mqa --no-plan-legs --bwd-warmup 2 "
+                 "--no-cpu-baseline --settle-s 0 --no-decode --no-mqa --no-plan-legs --bwd-warmup 2 "
                  "--bwd-reps 3 --copy-calibration 256",
     "leg_trace": "rocprofv3 --kernel-trace --stats -d OUT/trace_W -o bench --output-format csv -- "
                  "python3 REPO/bench.py --workload W --steps 20 --warmup 10 --no-cpu-baseline "
                  "--no-backward --no-decode --no-mqa --no-plan-legs",
     "bwd_pmc1": "rocprofv3 --pmc " + " ".join(PMC_PASSES[0]) + " --kernel-include-regex "
                 "'tile_|bwd_|wt_prep|dxc_|conv_bwd|dw_|colsum' -d OUT/bpmc1 -o run --output-format "
-                "csv -- python3 REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-decode "
+                "csv -- python3 REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline --settle-s 0 --no-decode "
                 "--no-mqa --no-plan-legs --bwd-warmup 2 --bwd-reps 3",
     "bwd_pmc2": "rocprofv3 --pmc " + " ".join(PMC_PASSES[1]) + " --kernel-include-regex "
                 "'tile_|bwd_|wt_prep|dxc_|conv_bwd|dw_|colsum' -d OUT/bpmc2 -o run --output-format "
-                "csv -- python3 REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-decode "
+                "csv -- python3 REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline --settle-s 0 --no-decode "
                 "--no-mqa --no-plan-legs --bwd-warmup 2 --bwd-reps 3",
     "pmc1": "rocprofv3 --pmc " + " ".join(PMC_PASSES[0]) + " -d OUT/pmc1 -o run "
-            "--output-format csv -- python3 REPO/bench.py --steps 5 --warmup 2 --no-cpu-baseline "
+            "--output-format csv -- python3 REPO/bench.py --steps 5 --warmup 2 --no-cpu-baseline --settle-s 0 "
             "--no-backward --no-decode --no-mqa --no-plan-legs",
     "pmc2": "rocprofv3 --pmc " + " ".join(PMC_PASSES[1]) + " -d OUT/pmc2 -o run "
-            "--output-format csv -- python3 REPO/bench.py --steps 5 --warmup 2 --no-cpu-baseline "
+            "--output-format csv -- python3 REPO/bench.py --steps 5 --warmup 2 --no-cpu-baseline --settle-s 0 "
             "--no-backward --no-decode --no-mqa --no-plan-legs",
 }
 
