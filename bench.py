@@ -346,8 +346,12 @@ def trace_summary(stats_csv, workload, bench_line_path=None, key="rg2b"):
                     f"OUT/trace_{key}/bench_kernel_stats.csv [OUT/trace_{key}/stdout.txt]\n")
         f.write(f"workload: {workload}\n")
         f.write(f"source_hash: {kernel_source_hash()}\n")
+        f.write("# the library's kernels only (the bench's own torch kernels and its clock-settle\n"
+                "# matrix product and copies are left out)\n")
         f.write(f"{'calls':>7} {'avg_us':>9} {'min_us':>9} {'max_us':>9}  kernel\n")
         for r in rows:
+            if "rglru::" not in r["Name"]:
+                continue
             name = r["Name"].split("(")[0].replace("void ", "")
             f.write(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.2f} "
                     f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f}  {name}\n")
