@@ -86,7 +86,10 @@ ScanCarve scan_carve(int B, int D, int H, int nC) {
 // computed, its chunks chained by the decoupled look-back. Other chunk lengths and shapes take
 // the three passes (summaries, carries, final).
 bool tiled_scan(int T, int D, int H, rglru_dtype dt, int L) {
-  return L == 64 && rglru::fused_supported(dt == RGLRU_BF16 ? kBF16 : kF32, T, D, D / H);
+  // the one-pass scan reads each sequence's pre-activations (4 bytes per element) through 32-bit
+  // buffer offsets
+  return L == 64 && rglru::fused_supported(dt == RGLRU_BF16 ? kBF16 : kF32, T, D, D / H) &&
+         static_cast<long long>(T) * D * 4 < (1LL << 32);
 }
 
 enum Kind { kDirect, kChunked, kFused };

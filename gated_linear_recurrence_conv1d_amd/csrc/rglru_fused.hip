@@ -296,16 +296,23 @@ __global__ __launch_bounds__(Fused<DH>::kThreads, 2) void fused_forward(
   // of its owner's tiles, and its successors in time wait on it.) s_tile is a ring of three.
   // PRE: this lane's 32 pre-activation pairs of tile j (time row 32 rt + 16 half + jj, channel
   // cl; rows past T read row T - 1: they only feed rows that are not stored)
+  // The loads go through a buffer descriptor over sequence b's pre-activations: the row's byte
+  // offset is wave-uniform and the lane's (channel, 16-row half) offset fixed, so each load costs
+  // one 32-bit add (a clamped 64-bit index product was four VALU instructions per load); rows
+  // past T read zeros from the range check (they only feed rows that are not stored).
   uint32_t pn[32];
+  const unsigned pre_lane = (static_cast<unsigned>(d) + 16u * half * static_cast<unsigned>(D)) * 4u;
   auto load_pre = [&](int j) {
     const int b = j % B, t0 = (j / B) * kFusedRows;
-    const uint32_t *pb = pre + static_cast<size_t>(b) * T * D + d;
+    const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t *>(pre + static_cast<size_t>(b) * T * D), static_cast<short>(0),
+        rec_bytes(T, D, 4u), kBufferWord3);
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj)
-        pn[16 * rt + jj] =
-            pb[static_cast<size_t>(min(t0 + 32 * rt + 16 * half + jj, T - 1)) * D];
+        pn[16 * rt + jj] = __builtin_amdgcn_raw_buffer_load_b32(
+            seq, row_bytes(t0 + 32 * rt + jj, D, 4u) + pre_lane, 0, 0);
   };
   if (tid == 0) s_tile[0] = static_cast<int>(atomicAdd(ticket, 1u));
   __syncthreads();
