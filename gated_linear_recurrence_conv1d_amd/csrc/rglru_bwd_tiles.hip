@@ -292,16 +292,28 @@ __global__ __launch_bounds__(DxcTile<DH>::kThreads, 2) void tile_dxc(
     const int jn = j + per;
     if (jn < ntiles) stage(jn, (it + 1) & 1);
     const int b = j % B, t0 = (j / B) * kRows;
-    // the direct part of dxc of rows t0 .. t0 + 66, 16 bytes (8 channels) per lane and piece,
-    // rows past T as zeros
-    const uint16_t *dtile = dxd + (static_cast<size_t>(b) * T + t0) * D + g * DH;
+    // Sequence b of dxd, x and dx through buffer descriptors: a row's byte offset is
+    // wave-uniform, a lane's a fixed 32-bit add, and the range check returns zeros for rows
+    // before t = 0 (negative offsets wrap past the end) or past T - 1 and drops stores there.
+    const __amdgpu_buffer_rsrc_t sd = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(dxd + static_cast<size_t>(b) * T * D), static_cast<short>(0),
+        rec_bytes(T, D, 2u), kWord3);
+    const __amdgpu_buffer_rsrc_t sx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t *>(x + static_cast<size_t>(b) * T * D), static_cast<short>(0),
+        rec_bytes(T, D, 2u), kWord3);
+    const __amdgpu_buffer_rsrc_t so = __builtin_amdgcn_make_buffer_rsrc(
+        dx + static_cast<size_t>(b) * T * D, static_cast<short>(0), rec_bytes(T, D, 2u), kWord3);
+    // the direct part of dxc of rows t0 .. t0 + 66, 16 bytes (8 channels) per lane and piece
+    // (pieces past the 67 rows read nothing: their offset is out of range)
     u32x4_t dv[F::kPer];
 #pragma unroll
     for (int q = 0; q < F::kPer; ++q) {
       const int idx = tid + q * F::kThreads, r = idx / (DH / 8), c8 = idx % (DH / 8);
-      dv[q] = idx < F::kPieces && t0 + r < T
-                  ? *reinterpret_cast<const u32x4_t *>(dtile + static_cast<size_t>(r) * D + 8 * c8)
-                  : u32x4_t{0u, 0u, 0u, 0u};
+      const unsigned off = idx < F::kPieces
+                               ? row_bytes(t0 + r, D, 2u) + static_cast<unsigned>(g * DH + 8 * c8) * 2u
+                               : 0x80000000u;
+      dv[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                              sd, static_cast<int>(off), 0, 0));
     }
     const uint16_t *lt = la + (it & 1) * F::kRowsX * F::kLd;
     f32x16_t acc[F::kGPW][3];  // row tiles: rows 0-31, 32-63, 64-95 (of which 64-66 are kept)
@@ -333,15 +345,11 @@ __global__ __launch_bounds__(DxcTile<DH>::kThreads, 2) void tile_dxc(
     // x rows t0 + 16 rb - 3 .. t0 + 16 rb + 15 of this thread's channel pair (the dconv_w sums),
     // in flight while the products and the direct part are added
     uint32_t xw[F::kRBRows + 3];
-    {
-      const bf16_t *xs = x + (static_cast<size_t>(b) * T) * D + g * DH + 2 * pc;
+    const unsigned pair_off = static_cast<unsigned>(g * DH + 2 * pc) * 2u;
 #pragma unroll
-      for (int k = 0; k < F::kRBRows + 3; ++k) {
-        const int t = t0 + rb * F::kRBRows - 3 + k;
-        xw[k] = t >= 0 && t < T ? *reinterpret_cast<const uint32_t *>(xs + static_cast<size_t>(t) * D)
-                                : 0u;
-      }
-    }
+    for (int k = 0; k < F::kRBRows + 3; ++k)
+      xw[k] = __builtin_amdgcn_raw_buffer_load_b32(
+          sx, static_cast<int>(row_bytes(t0 + rb * F::kRBRows - 3 + k, D, 2u) + pair_off), 0, 0);
     lds_barrier();  // products complete
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile's staging, direct part, x rows
 #pragma unroll
@@ -367,7 +375,6 @@ __global__ __launch_bounds__(DxcTile<DH>::kThreads, 2) void tile_dxc(
     {
       float s[4][2] = {};
       const float *pr = po + 2 * pc;
-      bf16_t *dxs = dx + (static_cast<size_t>(b) * T) * D + g * DH + 2 * pc;
       float2 gw[4];  // dxc rows r .. r + 3
 #pragma unroll
       for (int k = 0; k < 3; ++k)
@@ -383,8 +390,8 @@ __global__ __launch_bounds__(DxcTile<DH>::kThreads, 2) void tile_dxc(
                                                       fmaf(cw[2][0], gw[1].x, cw[3][0] * gw[0].x)));
         const float v1 = fmaf(cw[0][1], gw[3].y, fmaf(cw[1][1], gw[2].y,
                                                       fmaf(cw[2][1], gw[1].y, cw[3][1] * gw[0].y)));
-        if (t0 + r < T)
-          *reinterpret_cast<uint32_t *>(dxs + static_cast<size_t>(t0 + r) * D) = pack_bf16x2(v0, v1);
+        __builtin_amdgcn_raw_buffer_store_b32(
+            pack_bf16x2(v0, v1), so, static_cast<int>(row_bytes(t0 + r, D, 2u) + pair_off), 0, 0);
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {  // x[t - 3 + jt] is xw[u + jt]
           s[jt][0] = fmaf(gw[0].x, bf16lo(xw[u + jt]), s[jt][0]);
