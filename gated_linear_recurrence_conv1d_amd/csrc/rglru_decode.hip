@@ -24,6 +24,8 @@
 
 namespace rglru {
 
+constexpr int kDecodeWord3 = 0x00020000;  // buffer descriptor word 3: raw 32-bit data, no swizzle
+
 // Decode tile: 32 rows of one head, 4 waves. Wave w owns channel groups (32 channels each)
 // w*kGPW .. w*kGPW+kGPW-1 for the 32 rows (waves past the last group only help with the conv).
 // Small tiles give several workgroups per CU, whose load, compute and store phases overlap.
@@ -196,15 +198,31 @@ __global__ __launch_bounds__(2 * DH, 2) void decode_mfma64(
   // tile row of accumulator j in this lane (v_mfma_f32_32x32x16_bf16 layout), half 0
   auto acc_row = [&](int j) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); };
 
+  // Every access goes through a buffer descriptor over its whole tensor (the launcher keeps
+  // N * D * 6 bytes below 2^31): a row's byte offset is wave-uniform and a lane's fixed, so each
+  // access costs one 32-bit add, and the range check reads zeros for rows past N and drops the
+  // stores there (no clamps, no per-row branches; those rows only feed rows that are not stored).
+  const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+      h, static_cast<short>(0), rec_bytes(N, D, 4u), kDecodeWord3);
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      cs, static_cast<short>(0), rec_bytes(N, 3 * D, 2u), kDecodeWord3);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t *>(x_t), static_cast<short>(0), rec_bytes(N, D, 2u), kDecodeWord3);
+  const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+      y_t, static_cast<short>(0), rec_bytes(N, D, 2u), kDecodeWord3);
+  // this lane's element of accumulator row r of tile row block rb: element (n0 + rb + r) of
+  // channel d, r = 8 (j >> 2) + (j & 3) wave-uniform, the half's 4-row shift in the lane offset
+  const unsigned hl = static_cast<unsigned>(4 * (lane >> 5) * D + d);  // elements
+  auto rowj = [&](int rt, int j) { return n0 + rt * 32 + 8 * (j >> 2) + (j & 3); };
+
   // The fp32 states this wave will update are loaded first: they do not depend on the conv.
   float hv[2][16];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int n = min(n0 + rt * 32 + acc_row(j), N - 1);  // clamped; stores masked
-      hv[rt][j] = h[static_cast<size_t>(n) * D + d];
-    }
+    for (int j = 0; j < 16; ++j)
+      hv[rt][j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rh, static_cast<int>(row_bytes(rowj(rt, j), D, 4u) + 4u * hl), 0, 0));
 
   // Conv: thread = (channel pair p, rows r0 .. r0+RPG-1). The shifted conv state is stored only
   // after the MFMAs: vector memory operations complete in issue order, so stores issued here
@@ -226,12 +244,12 @@ __global__ __launch_bounds__(2 * DH, 2) void decode_mfma64(
     uint32_t c0[RPG];
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
-      const int n = min(n0 + r0 + i, N - 1);
-      const uint32_t *c = reinterpret_cast<const uint32_t *>(cs + static_cast<size_t>(n) * 3 * D + d0);
-      c0[i] = c[0];
-      c1[i] = c[D / 2];
-      c2[i] = c[D];
-      xv[i] = *reinterpret_cast<const uint32_t *>(x_t + static_cast<size_t>(n) * D + d0);
+      const unsigned cb = row_bytes(n0 + r0 + i, 3 * D, 2u) + 2u * d0;
+      c0[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<int>(cb), 0, 0);
+      c1[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<int>(cb + 2u * D), 0, 0);
+      c2[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<int>(cb + 4u * D), 0, 0);
+      xv[i] = __builtin_amdgcn_raw_buffer_load_b32(
+          rx, static_cast<int>(row_bytes(n0 + r0 + i, D, 2u) + 2u * d0), 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
@@ -274,31 +292,27 @@ __global__ __launch_bounds__(2 * DH, 2) void decode_mfma64(
     }
   }
 
-  // conv-state shift (rows past N store nothing)
+  // conv-state shift (rows past N are dropped by the range check)
 #pragma unroll
   for (int i = 0; i < RPG; ++i) {
-    const int n = n0 + r0 + i;
-    if (n < N) {
-      uint32_t *c = reinterpret_cast<uint32_t *>(cs + static_cast<size_t>(n) * 3 * D + d0);
-      c[0] = c1[i];
-      c[D / 2] = c2[i];
-      c[D] = xv[i];
-    }
+    const unsigned cb = row_bytes(n0 + r0 + i, 3 * D, 2u) + 2u * d0;
+    __builtin_amdgcn_raw_buffer_store_b32(c1[i], rc, static_cast<int>(cb), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(c2[i], rc, static_cast<int>(cb + 2u * D), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(xv[i], rc, static_cast<int>(cb + 4u * D), 0, 0);
   }
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int row = rt * 32 + acc_row(j);
-      const int n = n0 + row;
-      if (n < N) {
-        float a, u;
-        gate(acc[rt][0][j] + ba, acc[rt][1][j] + bx, lds_xc[row * DH + cl], kd, a, u);
-        const size_t off = static_cast<size_t>(n) * D + d;
-        const float hn = fmaf(a, hv[rt][j], u);
-        h[off] = hn;
-        y_t[off] = f32_to_bf16(hn);
-      }
+      float a, u;
+      gate(acc[rt][0][j] + ba, acc[rt][1][j] + bx, lds_xc[row * DH + cl], kd, a, u);
+      const float hn = fmaf(a, hv[rt][j], u);
+      __builtin_amdgcn_raw_buffer_store_b32(
+          __float_as_uint(hn), rh, static_cast<int>(row_bytes(rowj(rt, j), D, 4u) + 4u * hl), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(
+          __builtin_bit_cast(uint16_t, f32_to_bf16(hn)), ry,
+          static_cast<int>(row_bytes(rowj(rt, j), D, 2u) + 2u * hl), 0, 0);
     }
 }
 
@@ -402,7 +416,10 @@ hipError_t launch_decode(const void *x_t, void *conv_state, float *h, void *y_t,
                          const float *b_x, const float *Lambda, int N, int D, int H, int io,
                          hipStream_t s) {
   const int Dh = D / H;
-  if (io == kBF16 && (Dh == 32 || Dh == 64 || Dh == 128 || Dh == 256)) {
+  // decode_mfma64 addresses its largest tensor (conv_state, 6 bytes per row and channel) with
+  // 32-bit buffer offsets; larger batches take decode_valu
+  const bool mfma64_fits = static_cast<long long>(N) * D * 6 < (1LL << 31);
+  if (io == kBF16 && (Dh == 32 || Dh == 64 || ((Dh == 128 || Dh == 256) && mfma64_fits))) {
     dim3 grid((N + 31) / 32, H);    // DecodeTile<>::kRows rows per workgroup
     dim3 grid64((N + 63) / 64, H);  // decode_mfma64: 64 rows per workgroup
     const bf16_t *xx = static_cast<const bf16_t *>(x_t);
