@@ -172,27 +172,28 @@ __global__ __launch_bounds__(PreTile<DH>::kThreads, 2) void tile_preacts(
           }
         }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // next tile's staging landed
-    // ---- bias, fp16 pairs, store. Row addresses: a wave-uniform row pointer plus this lane's
-    // byte offset (its channel and its half's 4-row shift); Dv is re-read through an empty asm
-    // each tile so that the 32 row offsets are not hoisted out of the loop into registers.
+    // ---- bias, fp16 pairs, store, through a buffer descriptor over sequence b's pre-activations:
+    // a wave-uniform row offset plus this lane's byte offset (its channel and its half's 4-row
+    // shift), one 32-bit add per store; the range check drops rows past T (no per-row branch).
+    // Dv is re-read through an empty asm each tile so that the 32 row offsets are not hoisted
+    // out of the loop into registers.
     const int b = j % B, t0 = (j / B) * kRows;
     unsigned Dv = static_cast<unsigned>(D);
     asm volatile("" : "+s"(Dv));
-    const char *tile = reinterpret_cast<const char *>(pre + (static_cast<size_t>(b) * T + t0) * D +
-                                                      g * DH);
-    const bool full = t0 + kRows <= T;
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        pre + static_cast<size_t>(b) * T * D, static_cast<short>(0), rec_bytes(T, D, 4u), kWord3);
 #pragma unroll
     for (int gi = 0; gi < F::kGPW; ++gi) {
-      const unsigned lane_off = (static_cast<unsigned>(cl0 + 32 * gi) + 4u * half * Dv) * 4u;
+      const unsigned lane_off =
+          (static_cast<unsigned>(g * DH + cl0 + 32 * gi) + 4u * half * Dv) * 4u;
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
           const int r = rt * 32 + 8 * (jj >> 2) + (jj & 3);  // half 0's row; half 1: 4 further
-          if (full || t0 + r + 4 * half < T)
-            *reinterpret_cast<uint32_t *>(const_cast<char *>(tile) + static_cast<size_t>(r) * Dv * 4u +
-                                          lane_off) =
-                pack_f16x2(acc[gi][rt][0][jj] + ba[gi], acc[gi][rt][1][jj] + bx[gi]);
+          __builtin_amdgcn_raw_buffer_store_b32(
+              pack_f16x2(acc[gi][rt][0][jj] + ba[gi], acc[gi][rt][1][jj] + bx[gi]), rp,
+              static_cast<int>(static_cast<unsigned>(t0 + r) * Dv * 4u + lane_off), 0, 0);
         }
     }
   }
